@@ -1,0 +1,144 @@
+"""MI355X (gfx950) quantized rollout linear layer: NVFP4 and blockwise-FP8 weights with a bf16
+LoRA adapter, behind the C ABI of include/qlinear.h.
+
+    y = x . dequant(Wq)^T + s . (x A^T) B^T
+
+``binding`` is the one-to-one ctypes binding of the C entry points (same names).  The
+helpers below only allocate the output and workspace tensors with PyTorch (device memory
+and the current stream are all PyTorch is used for) and call the binding; every step of
+the layer runs in the HIP kernels of libqlinear.so.  Importing the package fails if the
+library has not been built -- there is no fallback.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import binding
+from .binding import (QL_FP8_BLOCK128, QL_NVFP4, QL_OUT_BF16, QL_OUT_F32, QlinearError,  # noqa: F401
+                      make_qweight)
+
+__all__ = ["NVFP4Weight", "FP8Weight", "quantize_nvfp4", "quantize_fp8_block", "quantize_act_fp8",
+           "forward", "forward_fp8_prequant", "RequantTable", "QlinearError", "binding"]
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return t
+
+
+@dataclass
+class NVFP4Weight:
+    codes: torch.Tensor         # uint8 [n, k/2]
+    scales: torch.Tensor        # uint8 [n, k/16] (E4M3)
+    tensor_scale: torch.Tensor  # float32 [1]
+    n: int
+    k: int
+
+    def qweight(self):
+        return make_qweight(QL_NVFP4, self.n, self.k, self.codes, self.scales, self.tensor_scale)
+
+    @staticmethod
+    def empty(n, k, device="cuda"):
+        return NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                           torch.empty((n, k // 16), dtype=torch.uint8, device=device),
+                           torch.empty((1,), dtype=torch.float32, device=device), n, k)
+
+
+@dataclass
+class FP8Weight:
+    codes: torch.Tensor   # uint8 [n, k] (E4M3)
+    scales: torch.Tensor  # float32 [n/128, k/128]
+    n: int
+    k: int
+
+    def qweight(self):
+        return make_qweight(QL_FP8_BLOCK128, self.n, self.k, self.codes, self.scales, None)
+
+    @staticmethod
+    def empty(n, k, device="cuda"):
+        return FP8Weight(torch.empty((n, k), dtype=torch.uint8, device=device),
+                         torch.empty((n // 128, k // 128), dtype=torch.float32, device=device), n, k)
+
+
+def _u16(t):
+    if t.dtype != torch.bfloat16:
+        raise TypeError("bf16 tensors expected")
+    return t
+
+
+def _ws(nbytes, device):
+    return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+
+
+def quantize_nvfp4(w, out=None, status_word=None):
+    _dev(_u16(w))
+    n, k = w.shape
+    q = out if out is not None else NVFP4Weight.empty(n, k, w.device)
+    ws = _ws(binding.qlinear_quantize_workspace(QL_NVFP4, n, k), w.device)
+    binding.qlinear_quantize_nvfp4(w, q.codes, q.scales, q.tensor_scale, ws, status_word)
+    return q
+
+
+def quantize_fp8_block(w, out=None, status_word=None):
+    _dev(_u16(w))
+    n, k = w.shape
+    q = out if out is not None else FP8Weight.empty(n, k, w.device)
+    binding.qlinear_quantize_fp8_block(w, q.codes, q.scales, status_word)
+    return q
+
+
+def quantize_act_fp8(x):
+    _dev(_u16(x))
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
+    binding.qlinear_quantize_act_fp8(x, xq, sx)
+    return xq, sx
+
+
+def _fmt(qw):
+    return QL_NVFP4 if isinstance(qw, NVFP4Weight) else QL_FP8_BLOCK128
+
+
+def forward(qw, x, lora_a=None, lora_b=None, lora_scale=0.0, out_dtype=torch.bfloat16, out=None, ws=None):
+    """y = x . dequant(qw)^T + lora_scale (x A^T) B^T  (bf16 or float32 output)."""
+    _dev(_u16(x))
+    m = x.shape[0]
+    rank = 0 if lora_a is None else lora_a.shape[0]
+    if out is None:
+        out = torch.empty((m, qw.n), dtype=out_dtype, device=x.device)
+    od = QL_OUT_F32 if out.dtype == torch.float32 else QL_OUT_BF16
+    eff_rank = rank if (lora_a is not None and lora_b is not None and lora_scale != 0) else 0
+    if ws is None:
+        ws = _ws(binding.qlinear_forward_workspace(_fmt(qw), m, qw.n, qw.k, eff_rank), x.device)
+    binding.qlinear_forward(qw.qweight(), x, out, od, ws, lora_a, lora_b, rank, lora_scale)
+    return out
+
+
+def forward_fp8_prequant(qw, xq, sx, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
+                         out_dtype=torch.bfloat16, out=None, ws=None):
+    m = xq.shape[0]
+    rank = 0 if lora_a is None else lora_a.shape[0]
+    if out is None:
+        out = torch.empty((m, qw.n), dtype=out_dtype, device=xq.device)
+    od = QL_OUT_F32 if out.dtype == torch.float32 else QL_OUT_BF16
+    eff_rank = rank if (lora_a is not None and lora_b is not None and lora_scale != 0) else 0
+    if ws is None:
+        ws = _ws(binding.qlinear_forward_prequant_workspace(m, qw.n, qw.k, eff_rank), xq.device)
+    binding.qlinear_forward_fp8_prequant(qw.qweight(), xq, sx, out, od, ws, x, lora_a, lora_b, rank, lora_scale)
+    return out
+
+
+class RequantTable:
+    """Device table for requantizing a whole policy (list of (bf16 weight, quantized weight))."""
+
+    def __init__(self, pairs, fmt=QL_NVFP4, device="cuda"):
+        self.pairs = list(pairs)   # keep the tensors alive
+        self.fmt = fmt
+        nbytes = binding.qlinear_requant_table_bytes(len(self.pairs))
+        self.table = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+        self.plan = binding.qlinear_requant_prepare([(w, q.qweight()) for w, q in self.pairs], fmt, self.table)
+
+    def requantize_all(self, status_word=None):
+        binding.qlinear_requantize_all(self.plan, self.table, status_word)

@@ -1,0 +1,193 @@
+"""ctypes binding of libqlinear (include/qlinear.h).
+
+Argument marshalling only: every function here passes tensor data pointers, sizes and
+the current HIP stream to the C entry point of the same name and turns a non-zero
+status into QlinearError.  PyTorch supplies device memory and streams; no step of
+the layer runs in Python.  The library must have been built
+(quantized_linear_layers_block_amd.build); importing this module fails loudly if it
+is missing.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlinear.so")
+
+QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_FORMAT, QL_ERR_WORKSPACE, QL_ERR_HIP, QL_ERR_ARG = range(8)
+QL_NVFP4, QL_FP8_BLOCK128 = 1, 2
+QL_OUT_BF16, QL_OUT_F32 = 1, 2
+
+# every symbol include/qlinear.h declares
+EXPORTS = [
+    "qlinear_status_string",
+    "qlinear_quantize_nvfp4",
+    "qlinear_quantize_fp8_block",
+    "qlinear_quantize_act_fp8",
+    "qlinear_quantize_workspace",
+    "qlinear_forward",
+    "qlinear_forward_fp8_prequant",
+    "qlinear_forward_workspace",
+    "qlinear_forward_prequant_workspace",
+    "qlinear_requant_table_bytes",
+    "qlinear_requant_prepare",
+    "qlinear_requantize_all",
+]
+
+
+class QlinearError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class QWeight(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
+class RequantItem(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("q", QWeight)]
+
+
+class RequantPlan(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("total_units", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_linear_layers_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "qlinear_status_string": ([i32], ctypes.c_char_p),
+        "qlinear_quantize_nvfp4": ([vp, i64, i64, vp, vp, vp, vp, vp, sz, vp], i32),
+        "qlinear_quantize_fp8_block": ([vp, i64, i64, vp, vp, vp, vp], i32),
+        "qlinear_quantize_act_fp8": ([vp, i64, i64, vp, vp, vp], i32),
+        "qlinear_quantize_workspace": ([i32, i64, i64], sz),
+        "qlinear_forward": ([ctypes.POINTER(QWeight), vp, i64, vp, vp, i32, f32, vp, i32, vp, sz, vp], i32),
+        "qlinear_forward_fp8_prequant": ([ctypes.POINTER(QWeight), vp, vp, i64, vp, vp, vp, i32, f32, vp,
+                                          i32, vp, sz, vp], i32),
+        "qlinear_forward_workspace": ([i32, i64, i64, i64, i32], sz),
+        "qlinear_forward_prequant_workspace": ([i64, i64, i64, i32], sz),
+        "qlinear_requant_table_bytes": ([i32], sz),
+        "qlinear_requant_prepare": ([ctypes.POINTER(RequantItem), i32, i32, vp, sz,
+                                     ctypes.POINTER(RequantPlan), vp], i32),
+        "qlinear_requantize_all": ([ctypes.POINTER(RequantPlan), vp, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status):
+    return LIB.qlinear_status_string(status).decode()
+
+
+def _check(status, where):
+    if status != QL_OK:
+        raise QlinearError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------ quantizers
+
+def qlinear_quantize_workspace(fmt, n, k):
+    return LIB.qlinear_quantize_workspace(fmt, n, k)
+
+
+def qlinear_quantize_nvfp4(w, codes, scales, tensor_scale, ws, status_word=None, stream=None):
+    """w bf16 [n,k] -> codes u8 [n,k/2], scales u8 [n,k/16], tensor_scale f32 [1]."""
+    n, k = w.shape
+    _check(LIB.qlinear_quantize_nvfp4(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+                                      _ptr(status_word), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "qlinear_quantize_nvfp4")
+
+
+def qlinear_quantize_fp8_block(w, codes, scales, status_word=None, stream=None):
+    """w bf16 [n,k] -> codes u8 [n,k], scales f32 [n/128, k/128]."""
+    n, k = w.shape
+    _check(LIB.qlinear_quantize_fp8_block(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(status_word),
+                                          _stream(stream)), "qlinear_quantize_fp8_block")
+
+
+def qlinear_quantize_act_fp8(x, xq, sx, stream=None):
+    """x bf16 [m,k] -> xq u8 [m,k], sx f32 [m, k/128]."""
+    m, k = x.shape
+    _check(LIB.qlinear_quantize_act_fp8(_ptr(x), m, k, _ptr(xq), _ptr(sx), _stream(stream)),
+           "qlinear_quantize_act_fp8")
+
+
+# --------------------------------------------------------------------- forward
+
+def make_qweight(fmt, n, k, codes, scales, tensor_scale=None):
+    return QWeight(fmt, 0, n, k, _ptr(codes), _ptr(scales), _ptr(tensor_scale))
+
+
+def qlinear_forward_workspace(fmt, m, n, k, rank):
+    return LIB.qlinear_forward_workspace(fmt, m, n, k, rank)
+
+
+def qlinear_forward_prequant_workspace(m, n, k, rank):
+    return LIB.qlinear_forward_prequant_workspace(m, n, k, rank)
+
+
+def qlinear_forward(qw, x, y, out_dtype, ws=None, lora_a=None, lora_b=None, rank=0, lora_scale=0.0,
+                    stream=None):
+    """y [m,n] = x [m,k] . dequant(qw)^T + lora_scale (x A^T) B^T."""
+    m = x.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(LIB.qlinear_forward(ctypes.byref(qw), _ptr(x), m, _ptr(lora_a), _ptr(lora_b), rank,
+                               float(lora_scale), _ptr(y), out_dtype, _ptr(ws), wsb, _stream(stream)),
+           "qlinear_forward")
+
+
+def qlinear_forward_fp8_prequant(qw, xq, sx, y, out_dtype, ws=None, x=None, lora_a=None, lora_b=None,
+                                 rank=0, lora_scale=0.0, stream=None):
+    m = xq.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(LIB.qlinear_forward_fp8_prequant(ctypes.byref(qw), _ptr(xq), _ptr(sx), m, _ptr(x), _ptr(lora_a),
+                                            _ptr(lora_b), rank, float(lora_scale), _ptr(y), out_dtype,
+                                            _ptr(ws), wsb, _stream(stream)),
+           "qlinear_forward_fp8_prequant")
+
+
+# --------------------------------------------------------------------- requant
+
+def qlinear_requant_table_bytes(count):
+    return LIB.qlinear_requant_table_bytes(count)
+
+
+def qlinear_requant_prepare(items, fmt, table, stream=None):
+    """items: list of (w bf16 tensor, QWeight).  Returns the host RequantPlan."""
+    arr = (RequantItem * len(items))()
+    for i, (w, qw) in enumerate(items):
+        arr[i].w = _ptr(w)
+        arr[i].q = qw
+    plan = RequantPlan()
+    _check(LIB.qlinear_requant_prepare(arr, len(items), fmt, _ptr(table), table.numel() * table.element_size(),
+                                       ctypes.byref(plan), _stream(stream)), "qlinear_requant_prepare")
+    return plan
+
+
+def qlinear_requantize_all(plan, table, status_word=None, stream=None):
+    _check(LIB.qlinear_requantize_all(ctypes.byref(plan), _ptr(table), _ptr(status_word), _stream(stream)),
+           "qlinear_requantize_all")

@@ -1,0 +1,393 @@
+// Weight and activation quantizers for gfx950.
+//
+// NVFP4 (public format definition; QeRL puts the policy's weight path in it,
+// tldrocket.com QeRL page, "Key Features of QeRL"): a tensor-wide |w| maximum gives
+// the FP32 tensor scale S = amax/2688; every 16-element block along K gets the E4M3
+// scale e_b = E4M3(amax_b / (6 S)); elements become E2M1(w / (E4M3(e_b) * S)).
+// Because S is global, NVFP4 takes two passes over the bf16 tensor: a maximum pass
+// that leaves per-workgroup partial maxima, and an encode pass in which every
+// workgroup first reduces those partials (no atomics, no zeroed scratch).
+//
+// FP8 (mexc.co NeMo RL FP8 page, "De technische doorbraak"): E4M3 with one float32
+// scale amax/448 per 128x128 weight tile (one workgroup per tile, one pass) and per
+// 1x128 activation segment (16 lanes per segment).
+//
+// Memory layout and access: bf16 inputs are streamed with 16-byte loads, each wave
+// load instruction covering 1 KB of contiguous memory; a 16-element NVFP4 block is
+// held by a lane pair (8 elements each) and its maximum is exchanged with one DPP
+// move.  Maxima are taken on the integer |bf16| bit patterns, which order like the
+// values and are exact.  Element quotients w/d are formed exactly (see
+// exact_quotient) and converted by the hardware E2M1/E4M3 encoders.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ql {
+
+constexpr int kQThreads = 256;
+constexpr int kQUnroll = 4;                                   // 16-byte loads in flight per lane
+constexpr int64_t kChunkVec = (int64_t)kQThreads * kQUnroll;  // uint4 (8 bf16) per chunk
+
+// --------------------------------------------------------- NVFP4 building blocks
+
+// Max of |bf16| bits over elements [c*kChunkElems, ...) of a tensor of `nvec` uint4.
+__device__ __forceinline__ u16x2 nvfp4_chunk_max(const uint4* __restrict__ w, int64_t nvec,
+                                                 int64_t chunk, u16x2 m) {
+  const int64_t base = chunk * kChunkVec + threadIdx.x;
+  uint4 v[kQUnroll];
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kQThreads;
+    v[j] = i < nvec ? w[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    m = max_u16x2(m, abs_bits2(v[j].x));
+    m = max_u16x2(m, abs_bits2(v[j].y));
+    m = max_u16x2(m, abs_bits2(v[j].z));
+    m = max_u16x2(m, abs_bits2(v[j].w));
+  }
+  return m;
+}
+
+struct Nvfp4TensorScale {
+  float S;
+  float six_S;
+};
+
+__device__ __forceinline__ Nvfp4TensorScale nvfp4_tensor_scale(uint32_t amax_bits) {
+  Nvfp4TensorScale t;
+  const float amax = __uint_as_float(amax_bits << 16);
+  t.S = amax / 2688.0f;
+  t.six_S = 6.0f * t.S;
+  return t;
+}
+
+// Encode one chunk: lanes (2i, 2i+1) hold the two halves of one 16-element block.
+__device__ __forceinline__ void nvfp4_encode_chunk(const uint4* __restrict__ w, int64_t nvec,
+                                                   int64_t chunk, Nvfp4TensorScale ts,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+  const int64_t base = chunk * kChunkVec + threadIdx.x;
+  uint4 v[kQUnroll];
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kQThreads;
+    v[j] = i < nvec ? w[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kQThreads;
+    u16x2 m = abs_bits2(v[j].x);
+    m = max_u16x2(m, abs_bits2(v[j].y));
+    m = max_u16x2(m, abs_bits2(v[j].z));
+    m = max_u16x2(m, abs_bits2(v[j].w));
+    const uint32_t blk_bits = max_pair(hmax_u16x2(m));
+    uint32_t e = 0;
+    if (ts.S != 0.0f) e = e4m3_encode(__uint_as_float(blk_bits << 16) / ts.six_S);
+    const float d = e4m3_value(e) * ts.S;
+    const double r = d > 0.0f ? 1.0 / (double)d : 0.0;
+    float q[8];
+    q[0] = exact_quotient(bf16_lo(v[j].x), r);
+    q[1] = exact_quotient(bf16_hi(v[j].x), r);
+    q[2] = exact_quotient(bf16_lo(v[j].y), r);
+    q[3] = exact_quotient(bf16_hi(v[j].y), r);
+    q[4] = exact_quotient(bf16_lo(v[j].z), r);
+    q[5] = exact_quotient(bf16_hi(v[j].z), r);
+    q[6] = exact_quotient(bf16_lo(v[j].w), r);
+    q[7] = exact_quotient(bf16_hi(v[j].w), r);
+    const uint32_t c = e2m1_pack8(q);
+    if (i < nvec) {
+      codes[i] = c;
+      if ((threadIdx.x & 1) == 0) scales[i >> 1] = (uint8_t)e;
+    }
+  }
+}
+
+// ------------------------------------------------------- NVFP4 single-tensor path
+
+__global__ __launch_bounds__(kQThreads) void nvfp4_amax_kernel(const uint4* __restrict__ w,
+                                                               int64_t nvec, int64_t nchunks,
+                                                               uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  u16x2 m = {0, 0};
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) m = nvfp4_chunk_max(w, nvec, c, m);
+  const uint32_t v = max_block<kQThreads>(hmax_u16x2(m), red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = v;
+}
+
+__global__ __launch_bounds__(kQThreads) void nvfp4_encode_kernel(
+    const uint4* __restrict__ w, int64_t nvec, int64_t nchunks,
+    const uint32_t* __restrict__ partials, int nparts, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int32_t* status) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  uint32_t v = 0;
+  for (int i = threadIdx.x; i < nparts; i += kQThreads) v = umax(v, partials[i]);
+  const uint32_t amax_bits = max_block<kQThreads>(v, red);
+  const Nvfp4TensorScale ts = nvfp4_tensor_scale(amax_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *tensor_scale = ts.S;
+    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+  }
+  // Back to front: the tail of the tensor, read last by the maximum pass, is the part
+  // most likely still held in the memory-side cache.
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x)
+    nvfp4_encode_chunk(w, nvec, nchunks - 1 - c, ts, codes, scales);
+}
+
+static int stream_grid(int64_t nchunks, int cap) {
+  return (int)(nchunks < cap ? (nchunks > 0 ? nchunks : 1) : cap);
+}
+
+hipError_t launch_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                 uint8_t* scales, float* tensor_scale, int32_t* status,
+                                 uint32_t* partials, hipStream_t s) {
+  const int64_t nvec = n * k / 8;
+  const int64_t nchunks = (nvec + kChunkVec - 1) / kChunkVec;
+  const int gp = stream_grid(nchunks, kAmaxParts);
+  nvfp4_amax_kernel<<<gp, kQThreads, 0, s>>>((const uint4*)w, nvec, nchunks, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ge = stream_grid(nchunks, 4096);
+  nvfp4_encode_kernel<<<ge, kQThreads, 0, s>>>((const uint4*)w, nvec, nchunks, partials, gp,
+                                               (uint32_t*)codes, scales, tensor_scale, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- FP8 weights
+
+// One 128x128 tile per workgroup.  Wave v, lane l holds rows 32v + 4j + l/16 (j = 0..7),
+// elements [8 (l%16), 8 (l%16) + 8) of the tile's 128 columns.
+__device__ __forceinline__ void fp8_tile(const uint16_t* __restrict__ w, int64_t k, int64_t tr,
+                                         int64_t tc, uint8_t* __restrict__ codes,
+                                         float* __restrict__ scales, int32_t* status,
+                                         uint32_t* red) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int piece = lane & 15;
+  uint4 v[8];
+  int64_t off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = tr * 128 + wave * 32 + j * 4 + (lane >> 4);
+    off[j] = row * k + tc * 128 + piece * 8;
+    v[j] = *(const uint4*)(w + off[j]);
+  }
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m = max_u16x2(m, abs_bits2(v[j].x));
+    m = max_u16x2(m, abs_bits2(v[j].y));
+    m = max_u16x2(m, abs_bits2(v[j].z));
+    m = max_u16x2(m, abs_bits2(v[j].w));
+  }
+  const uint32_t amax_bits = max_block<kQThreads>(hmax_u16x2(m), red);
+  const float sc = __uint_as_float(amax_bits << 16) / 448.0f;
+  const double r = sc > 0.0f ? 1.0 / (double)sc : 0.0;
+  if (threadIdx.x == 0) {
+    scales[tr * (k / 128) + tc] = sc;
+    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float q[8];
+    q[0] = exact_quotient(bf16_lo(v[j].x), r);
+    q[1] = exact_quotient(bf16_hi(v[j].x), r);
+    q[2] = exact_quotient(bf16_lo(v[j].y), r);
+    q[3] = exact_quotient(bf16_hi(v[j].y), r);
+    q[4] = exact_quotient(bf16_lo(v[j].z), r);
+    q[5] = exact_quotient(bf16_hi(v[j].z), r);
+    q[6] = exact_quotient(bf16_lo(v[j].w), r);
+    q[7] = exact_quotient(bf16_hi(v[j].w), r);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t], -448.0f, 448.0f);
+    uint2 c;
+    c.x = e4m3_pack4(q[0], q[1], q[2], q[3]);
+    c.y = e4m3_pack4(q[4], q[5], q[6], q[7]);
+    *(uint2*)(codes + off[j]) = c;
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void fp8_weight_kernel(const uint16_t* __restrict__ w,
+                                                               int64_t k,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales,
+                                                               int32_t* status) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  fp8_tile(w, k, blockIdx.y, blockIdx.x, codes, scales, status, red);
+}
+
+hipError_t launch_fp8_weight_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                      float* scales, int32_t* status, hipStream_t s) {
+  dim3 grid((unsigned)(k / 128), (unsigned)(n / 128));
+  fp8_weight_kernel<<<grid, kQThreads, 0, s>>>(w, k, codes, scales, status);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ FP8 activations
+
+constexpr int kActSegPerIter = 2;  // segments per 16-lane group per iteration
+
+// Segment = 1x128 of a token row.  16 lanes per segment (8 elements each); a DPP row
+// is exactly one segment, so the segment maximum is four DPP moves.
+__global__ __launch_bounds__(kQThreads) void fp8_act_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t nseg,
+                                                            uint8_t* __restrict__ xq,
+                                                            float* __restrict__ sx) {
+  const int piece = threadIdx.x & 15;
+  const int64_t groups = (nseg + (kQThreads / 16) * kActSegPerIter - 1) /
+                         ((kQThreads / 16) * kActSegPerIter);
+  for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    uint4 v[kActSegPerIter];
+    int64_t seg[kActSegPerIter];
+#pragma unroll
+    for (int j = 0; j < kActSegPerIter; ++j) {
+      seg[j] = (g * kActSegPerIter + j) * (kQThreads / 16) + threadIdx.x / 16;
+      v[j] = seg[j] < nseg ? *(const uint4*)(x + seg[j] * 128 + piece * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kActSegPerIter; ++j) {
+      u16x2 m = abs_bits2(v[j].x);
+      m = max_u16x2(m, abs_bits2(v[j].y));
+      m = max_u16x2(m, abs_bits2(v[j].z));
+      m = max_u16x2(m, abs_bits2(v[j].w));
+      const uint32_t amax_bits = max_row16(hmax_u16x2(m));
+      const float sc = __uint_as_float(amax_bits << 16) / 448.0f;
+      const double r = sc > 0.0f ? 1.0 / (double)sc : 0.0;
+      float q[8];
+      q[0] = exact_quotient(bf16_lo(v[j].x), r);
+      q[1] = exact_quotient(bf16_hi(v[j].x), r);
+      q[2] = exact_quotient(bf16_lo(v[j].y), r);
+      q[3] = exact_quotient(bf16_hi(v[j].y), r);
+      q[4] = exact_quotient(bf16_lo(v[j].z), r);
+      q[5] = exact_quotient(bf16_hi(v[j].z), r);
+      q[6] = exact_quotient(bf16_lo(v[j].w), r);
+      q[7] = exact_quotient(bf16_hi(v[j].w), r);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t], -448.0f, 448.0f);
+      uint2 c;
+      c.x = e4m3_pack4(q[0], q[1], q[2], q[3]);
+      c.y = e4m3_pack4(q[4], q[5], q[6], q[7]);
+      if (seg[j] < nseg) {
+        *(uint2*)(xq + seg[j] * 128 + piece * 8) = c;
+        if (piece == 0) sx[seg[j]] = sc;
+      }
+    }
+  }
+}
+
+hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
+                                   float* sx, hipStream_t s) {
+  const int64_t nseg = m * (k / 128);
+  const int64_t per_block = (kQThreads / 16) * kActSegPerIter;
+  const int64_t groups = (nseg + per_block - 1) / per_block;
+  fp8_act_kernel<<<stream_grid(groups, 4096), kQThreads, 0, s>>>(x, nseg, xq, sx);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ whole-policy requantization
+
+size_t requant_table_bytes(int32_t count) {
+  size_t b = sizeof(RequantHeader) + (size_t)count * sizeof(RequantDesc) + (size_t)count * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+int64_t requant_units(int32_t format, int64_t n, int64_t k) {
+  if (format == 1) return (n * k / 8 + kChunkVec - 1) / kChunkVec;  // NVFP4 chunks
+  return (n / 128) * (k / 128);                                     // FP8 tiles
+}
+
+__device__ __forceinline__ int find_tensor(const RequantDesc* __restrict__ d, int count,
+                                           int64_t unit) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {  // last tensor whose unit_begin <= unit
+    const int mid = (lo + hi + 1) >> 1;
+    if (d[mid].unit_begin <= unit) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kQThreads) void requant_zero_kernel(uint32_t* amax, int count) {
+  for (int i = blockIdx.x * kQThreads + threadIdx.x; i < count; i += gridDim.x * kQThreads)
+    amax[i] = 0;
+}
+
+// Each workgroup takes a contiguous range of units (so that most of its units belong
+// to one tensor) and publishes one integer atomicMax per tensor it touched.
+__global__ __launch_bounds__(kQThreads) void requant_amax_kernel(const RequantHeader* __restrict__ h,
+                                                                 const RequantDesc* __restrict__ d,
+                                                                 uint32_t* __restrict__ amax) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t total = h->total_units;
+  const int count = h->count;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t u0 = (int64_t)blockIdx.x * per;
+  const int64_t u1 = u0 + per < total ? u0 + per : total;
+  int64_t u = u0;
+  while (u < u1) {
+    const int t = find_tensor(d, count, u);
+    const int64_t tend = d[t].unit_begin + d[t].unit_count;
+    const int64_t stop = tend < u1 ? tend : u1;
+    const int64_t nvec = d[t].n * d[t].k / 8;
+    u16x2 m = {0, 0};
+    for (; u < stop; ++u) m = nvfp4_chunk_max((const uint4*)d[t].w, nvec, u - d[t].unit_begin, m);
+    const uint32_t v = max_block<kQThreads>(hmax_u16x2(m), red);
+    if (threadIdx.x == 0) atomicMax(amax + t, v);
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void requant_encode_kernel(const RequantHeader* __restrict__ h,
+                                                                   const RequantDesc* __restrict__ d,
+                                                                   const uint32_t* __restrict__ amax,
+                                                                   int32_t* status) {
+  const int64_t total = h->total_units;
+  const int count = h->count;
+  // Back to front over the whole table: the most recently read tensors go first.
+  for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
+    const int64_t u = total - 1 - i;
+    const int t = find_tensor(d, count, u);
+    const uint32_t amax_bits = amax[t];
+    const Nvfp4TensorScale ts = nvfp4_tensor_scale(amax_bits);
+    const int64_t chunk = u - d[t].unit_begin;
+    if (chunk == 0 && threadIdx.x == 0) {
+      *d[t].tensor_scale = ts.S;
+      if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+    }
+    nvfp4_encode_chunk((const uint4*)d[t].w, d[t].n * d[t].k / 8, chunk, ts,
+                       (uint32_t*)d[t].codes, (uint8_t*)d[t].scales);
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void requant_fp8_kernel(const RequantHeader* __restrict__ h,
+                                                                const RequantDesc* __restrict__ d,
+                                                                int32_t* status) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t total = h->total_units;
+  const int count = h->count;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int t = find_tensor(d, count, u);
+    const int64_t tile = u - d[t].unit_begin;
+    const int64_t tiles_k = d[t].k / 128;
+    fp8_tile(d[t].w, d[t].k, tile / tiles_k, tile % tiles_k, (uint8_t*)d[t].codes,
+             (float*)d[t].scales, status, red);
+  }
+}
+
+hipError_t launch_requant(void* table, const RequantHeader& h, int32_t* status, hipStream_t s) {
+  const RequantHeader* dh = (const RequantHeader*)table;
+  const RequantDesc* dd = (const RequantDesc*)((char*)table + sizeof(RequantHeader));
+  uint32_t* amax = (uint32_t*)((char*)table + sizeof(RequantHeader) + (size_t)h.count * sizeof(RequantDesc));
+  if (h.format == 1) {
+    requant_zero_kernel<<<(h.count + kQThreads - 1) / kQThreads, kQThreads, 0, s>>>(amax, h.count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    requant_amax_kernel<<<stream_grid(h.total_units, 4096), kQThreads, 0, s>>>(dh, dd, amax);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    requant_encode_kernel<<<stream_grid(h.total_units, 4096), kQThreads, 0, s>>>(dh, dd, amax, status);
+    return hipGetLastError();
+  }
+  requant_fp8_kernel<<<stream_grid(h.total_units, 8192), kQThreads, 0, s>>>(dh, dd, status);
+  return hipGetLastError();
+}
+
+}  // namespace ql

@@ -29,10 +29,12 @@ def rng(cfg, shape_idx, role, layer=0, step=0):
 
 
 def to_bf16_bits(x):
-    """float32 array -> bf16 bit patterns (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
-    return r.astype(np.uint16)
+    """finite float32 array -> bf16 bit patterns (uint16), round to nearest even.
+    (For finite inputs the 32-bit sum below cannot wrap.)"""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bits_to_f32(bits):

@@ -1,0 +1,100 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every entry point
+include/qlinear.h declares, and rejects invalid arguments with the documented status
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+b = pytest.importorskip("quantized_linear_layers_block_amd.binding")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qlinear.h")).read()
+    return sorted(set(re.findall(r"\b(qlinear_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared()
+    assert set(declared) == set(b.EXPORTS)
+    for name in declared:
+        assert hasattr(b.LIB, name), name
+
+
+def test_status_strings():
+    for s in range(8):
+        assert b.status_string(s)
+    assert b.status_string(b.QL_ERR_ALIGN) == "pointer not 16-byte aligned"
+
+
+def test_workspace_queries():
+    assert b.qlinear_quantize_workspace(b.QL_NVFP4, 256, 512) == 4096
+    assert b.qlinear_quantize_workspace(b.QL_FP8_BLOCK128, 256, 512) == 0
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 3584, 3584, 32) > 0
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 27648, 5120, 0) == 0
+    # FP8 forward holds the quantized activations (m*k bytes + scales)
+    assert b.qlinear_forward_workspace(b.QL_FP8_BLOCK128, 8192, 4096, 14336, 0) >= 8192 * 14336
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 0, 16, 16, 0) == 0
+    assert b.qlinear_requant_table_bytes(448) > 448 * 56
+    assert b.qlinear_requant_table_bytes(0) == 0
+
+
+FAKE = 0x10000  # an aligned, never-dereferenced address
+
+
+def test_quantize_argument_errors():
+    L = b.LIB
+    assert L.qlinear_quantize_nvfp4(None, 4, 16, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == b.QL_ERR_NULL
+    assert L.qlinear_quantize_nvfp4(FAKE, 4, 24, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == b.QL_ERR_SHAPE
+    assert L.qlinear_quantize_nvfp4(FAKE, 0, 16, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == b.QL_ERR_SHAPE
+    assert L.qlinear_quantize_nvfp4(FAKE + 2, 4, 16, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == b.QL_ERR_ALIGN
+    assert L.qlinear_quantize_nvfp4(FAKE, 4, 16, FAKE, FAKE, FAKE, None, FAKE, 100, None) == b.QL_ERR_WORKSPACE
+    assert L.qlinear_quantize_nvfp4(FAKE, 1 << 21, 1 << 20, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == b.QL_ERR_SHAPE
+    assert L.qlinear_quantize_fp8_block(FAKE, 100, 128, FAKE, FAKE, None, None) == b.QL_ERR_SHAPE
+    assert L.qlinear_quantize_fp8_block(FAKE, 128, 128, None, FAKE, None, None) == b.QL_ERR_NULL
+    assert L.qlinear_quantize_act_fp8(FAKE, 3, 100, FAKE, FAKE, None) == b.QL_ERR_SHAPE
+
+
+def test_forward_argument_errors():
+    L = b.LIB
+    qw = b.QWeight(b.QL_NVFP4, 0, 256, 512, FAKE, FAKE, FAKE)
+    f = lambda qw_, x=FAKE, m=4, la=None, lb=None, r=0, s=0.0, y=FAKE, od=b.QL_OUT_BF16, ws=FAKE, wsb=1 << 30: \
+        L.qlinear_forward(ctypes.byref(qw_), x, m, la, lb, r, s, y, od, ws, wsb, None)
+    assert f(qw, x=None) == b.QL_ERR_NULL
+    assert f(qw, y=None) == b.QL_ERR_NULL
+    assert f(qw, m=0) == b.QL_ERR_SHAPE
+    assert f(qw, od=3) == b.QL_ERR_FORMAT
+    assert f(qw, r=-1) == b.QL_ERR_ARG
+    assert f(qw, r=129) == b.QL_ERR_ARG
+    assert f(qw, la=FAKE, lb=FAKE, r=8, s=2.0, ws=None) == b.QL_ERR_WORKSPACE
+    assert f(qw, la=FAKE, lb=FAKE, r=8, s=2.0, wsb=16) == b.QL_ERR_WORKSPACE
+    assert f(qw, x=FAKE + 8) == b.QL_ERR_ALIGN
+    assert f(b.QWeight(3, 0, 256, 512, FAKE, FAKE, FAKE)) == b.QL_ERR_FORMAT
+    assert f(b.QWeight(b.QL_NVFP4, 0, 256, 500, FAKE, FAKE, FAKE)) == b.QL_ERR_SHAPE
+    assert f(b.QWeight(b.QL_NVFP4, 0, 256, 512, FAKE, FAKE, None)) == b.QL_ERR_NULL
+    assert f(b.QWeight(b.QL_FP8_BLOCK128, 0, 200, 512, FAKE, FAKE, None)) == b.QL_ERR_SHAPE
+    pq = L.qlinear_forward_fp8_prequant(ctypes.byref(qw), FAKE, FAKE, 4, None, None, None, 0, 0.0, FAKE,
+                                        b.QL_OUT_BF16, None, 0, None)
+    assert pq == b.QL_ERR_FORMAT
+
+
+def test_requant_argument_errors():
+    L = b.LIB
+    items = (b.RequantItem * 2)()
+    items[0].w = FAKE
+    items[0].q = b.QWeight(b.QL_NVFP4, 0, 128, 256, FAKE, FAKE, FAKE)
+    items[1].w = FAKE
+    items[1].q = b.QWeight(b.QL_FP8_BLOCK128, 0, 128, 256, FAKE, FAKE, None)
+    plan = b.RequantPlan()
+    nb = b.qlinear_requant_table_bytes(2)
+    assert L.qlinear_requant_prepare(items, 2, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_ARG
+    assert L.qlinear_requant_prepare(items, 0, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_ARG
+    assert L.qlinear_requant_prepare(items, 1, b.QL_NVFP4, FAKE, 8, ctypes.byref(plan), None) == b.QL_ERR_WORKSPACE
+    assert L.qlinear_requant_prepare(items, 1, 9, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_FORMAT
+    items[0].q = b.QWeight(b.QL_NVFP4, 0, 128, 250, FAKE, FAKE, FAKE)
+    assert L.qlinear_requant_prepare(items, 1, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_SHAPE
+    assert L.qlinear_requantize_all(ctypes.byref(plan), FAKE, None, None) == b.QL_ERR_ARG  # empty plan
+    assert L.qlinear_requantize_all(None, FAKE, None, None) == b.QL_ERR_NULL
