@@ -121,49 +121,65 @@ def main():
 
     order = [(si, m) for m in DECODE_M for si in range(len(DECODE_SHAPES))]
     step_bytes = sum(decode_bytes(m, DECODE_SHAPES[si][1], DECODE_SHAPES[si][0], RANK) for si, m in order)
-    counter = [0]
 
-    def step(timer=None):
-        for si, m in order:
-            c = copies[counter[0] % ncopy][si]
-            counter[0] += 1
-            a, b = loras[si]
-            e0 = timer.start() if timer else None
-            ql.forward(c, xs[(si, m)], a, b, LORA_S, out=outs[(si, m)], ws=wss[(si, m)])
-            if timer:
-                timer.stop(e0)
+    def call(c, si, m):
+        a, b = loras[si]
+        ql.forward(c, xs[(si, m)], a, b, LORA_S, out=outs[(si, m)], ws=wss[(si, m)])
 
-    for _ in range(args.warmup):
-        step()
+    def step(j):
+        # call number 12 j + i reads weight copy (12 j + i) mod ncopy: a (copy, shape) pair
+        # comes back only after >= 1 GiB of other weight reads
+        for i, (si, m) in enumerate(order):
+            call(copies[(len(order) * j + i) % ncopy][si], si, m)
+
+    for j in range(args.warmup):
+        step(j)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    # one HIP graph per rotation phase; the timed region replays them
+    graphs = []
+    for j in range(ncopy):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            step(j)
+        graphs.append(gph)
+    torch.cuda.synchronize()
+    for j in range(len(graphs)):
+        graphs[j].replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(timer)
+    for j in range(args.steps):
+        graphs[j % len(graphs)].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
-    launches = len(timer.pairs)
-    kern_ms = timer.total_ms() / launches
-    achieved = step_bytes / len(order) / (kern_ms * 1e-3) / 1e9
 
-    # per-case event times (one extra timed pass per case)
-    cases = []
+    # Per-launch kernel times: queue a cushion of graph replays so that the host runs
+    # ahead, then bracket every layer call with its own pair of events.
+    reps = 10
+    for j in range(40):
+        graphs[j % len(graphs)].replay()
+    timers = {key: Timer(torch) for key in order}
+    for rep in range(reps):
+        for i, (si, m) in enumerate(order):
+            c = copies[(len(order) * (rep + 7) + i) % ncopy][si]
+            e0 = timers[(si, m)].start()
+            call(c, si, m)
+            timers[(si, m)].stop(e0)
+    torch.cuda.synchronize()
+    cases, tot_bytes, tot_ms = [], 0.0, 0.0
     for si, m in order:
         k, n = DECODE_SHAPES[si]
-        tm = Timer(torch)
-        for r in range(20):
-            c = copies[(r * 7 + si) % ncopy][si]
-            a, b = loras[si]
-            e0 = tm.start()
-            ql.forward(c, xs[(si, m)], a, b, LORA_S, out=outs[(si, m)], ws=wss[(si, m)])
-            tm.stop(e0)
-        torch.cuda.synchronize()
-        us = tm.total_ms() * 1e3 / 20
-        gbs = decode_bytes(m, n, k, RANK) / (us * 1e-6) / 1e9
-        cases.append({"K": k, "N": n, "M": m, "us": round(us, 2), "GB/s": round(gbs, 1),
+        ms = timers[(si, m)].total_ms() / reps
+        by = decode_bytes(m, n, k, RANK)
+        tot_bytes += by * reps
+        tot_ms += ms * reps
+        gbs = by / (ms * 1e-3) / 1e9
+        cases.append({"K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                       "frac": round(gbs * 1e9 / HBM_PEAK, 4)})
+    launches = reps * len(order)
+    kern_ms = tot_ms / launches
+    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
 
     result = {
         "metric": "NVFP4/FP8 qlinear TFLOP/s & HBM GB/s (% roofline); requant GB/s",
@@ -184,7 +200,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "qlinear_forward (NVFP4, M<=64)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
-                     "launches": launches, "mean_launch_us": round(kern_ms * 1e3, 3)},
+                     "launches": launches, "mean_launch_us": round(kern_ms * 1e3, 3),
+                     "bytes_per_launch_mean": round(tot_bytes / launches)},
         "decode_cases": cases,
         "setup_s": round(setup_s, 1),
     }

@@ -68,7 +68,8 @@ def _u16(t):
 
 
 def _ws(nbytes, device):
-    return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+    # zero-filled: the library keeps workgroup counters in forward workspaces
+    return torch.zeros((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
 
 
 def quantize_nvfp4(w, out=None, status_word=None):

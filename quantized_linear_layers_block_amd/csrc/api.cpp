@@ -20,7 +20,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Largest token count served by the few-token (streaming) path.
+// Largest token counts served by the few-token (streaming) kernels.
+constexpr int64_t kG16MaxM = 32;
 constexpr int64_t kSkinnyMaxM = 64;
 
 bool elems_ok(int64_t n, int64_t k) {
@@ -48,18 +49,17 @@ int32_t lora_rank(const uint16_t* a, const uint16_t* b, int32_t rank, float scal
   return (rank > 0 && a && b && scale != 0.0f) ? rank : 0;
 }
 
-// Workspace of the LoRA down-projection for the GEMM paths: skinny partials + t (bf16).
+// Workspace of the LoRA down-projection for the GEMM paths (counters, t, partials).
 struct LoraWs {
   SkinnyPlan plan;
-  size_t partials_bytes = 0, t_bytes = 0;
-  size_t total() const { return up(partials_bytes) + up(t_bytes); }
+  size_t bytes = 0;
+  size_t total() const { return up(bytes); }
 };
 LoraWs lora_ws(int64_t m, int64_t k, int32_t rank) {
   LoraWs w;
   if (rank <= 0) return w;
   w.plan = ql::plan_skinny(m, 0, k, rank);
-  w.partials_bytes = ql::skinny_workspace(w.plan, m);
-  w.t_bytes = (size_t)m * (size_t)cdiv(rank, 32) * 32 * sizeof(uint16_t);
+  w.bytes = ql::skinny_workspace(w.plan, m, k);
   return w;
 }
 
@@ -71,13 +71,8 @@ qlinear_status hip_status(hipError_t e) { return e == hipSuccess ? QL_OK : QL_ER
 qlinear_status run_lora_t(const LoraWs& lw, char* ws, const uint16_t* x, int64_t m, int64_t k,
                           const uint16_t* lora_a, int32_t rank, float scale, uint16_t** t_out,
                           hipStream_t s) {
-  float* partials = (float*)ws;
-  uint16_t* t = (uint16_t*)(ws + up(lw.partials_bytes));
-  hipError_t e = ql::launch_skinny(lw.plan, x, m, k, nullptr, nullptr, lora_a, rank, partials, s);
-  if (e != hipSuccess) return QL_ERR_HIP;
-  e = ql::launch_lora_t(lw.plan, m, partials, rank, scale, t, s);
-  if (e != hipSuccess) return QL_ERR_HIP;
-  *t_out = t;
+  if (ql::launch_lora_down(lw.plan, x, m, k, lora_a, rank, scale, ws, s) != hipSuccess) return QL_ERR_HIP;
+  *t_out = ql::lora_t_in_workspace(lw.plan, ws);
   return QL_OK;
 }
 
@@ -145,9 +140,10 @@ qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank) {
   if (m <= 0 || n <= 0 || k <= 0 || rank < 0) return 0;
   if (format == QL_NVFP4) {
+    if (m <= kG16MaxM) return up(ql::g16_workspace(ql::plan_g16(m, n, k, rank), m));
     if (m <= kSkinnyMaxM) {
       const SkinnyPlan p = ql::plan_skinny(m, n, k, rank);
-      return up(ql::skinny_workspace(p, m));
+      return up(ql::skinny_workspace(p, m, k));
     }
     return lora_ws(m, k, rank).total();
   }
@@ -193,13 +189,15 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
   if (w->format == QL_NVFP4) {
     const uint8_t* codes = (const uint8_t*)w->codes;
     const uint8_t* scales = (const uint8_t*)w->scales;
+    if (m <= kG16MaxM) {
+      const ql::G16Plan p = ql::plan_g16(m, w->n, w->k, r);
+      return hip_status(ql::launch_g16(p, x, m, w->n, w->k, codes, scales, w->tensor_scale, lora_a,
+                                       lora_b, r, lora_scale, y, out_f32, wsb, s));
+    }
     if (m <= kSkinnyMaxM) {
       const SkinnyPlan p = ql::plan_skinny(m, w->n, w->k, r);
-      float* partials = (float*)wsb;
-      if (ql::launch_skinny(p, x, m, w->k, codes, scales, lora_a, r, partials, s) != hipSuccess)
-        return QL_ERR_HIP;
-      return hip_status(ql::launch_skinny_reduce(p, m, w->n, partials, w->tensor_scale, lora_b, r,
-                                                 lora_scale, y, out_f32, s));
+      return hip_status(ql::launch_skinny_forward(p, x, m, w->n, w->k, codes, scales, w->tensor_scale,
+                                                  lora_a, lora_b, r, lora_scale, y, out_f32, wsb, s));
     }
     const LoraWs lw = lora_ws(m, w->k, r);
     uint16_t* t = nullptr;

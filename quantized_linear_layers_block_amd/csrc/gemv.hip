@@ -1,159 +1,210 @@
-// Few-token ("decode") NVFP4 layer for gfx950:  y = S . x . (E2M1 * E4M3)^T + s . (x A^T) B^T.
+// Few-token ("decode") NVFP4 layer for gfx950, one launch per call:
 //
-// QeRL's speedup is in rollout decoding, where the policy's weight path is NVFP4
-// (tldrocket.com QeRL page, paragraph after "Key Features of QeRL"); with a handful of
-// tokens the layer streams 0.5625 byte per weight and is bound by HBM, so the kernel
-// is organised around streaming the packed codes once with 16-byte loads.
+//   y = S . x . (E2M1 * E4M3)^T  +  bf16(s . x A^T) . B^T
 //
-// Kernel 1 (skinny_kernel): every wave owns R tiles of 16 weight rows and a set of
-// 512-wide K chunks.  Lane l reads row (l % 16) of each tile and the 128 consecutive
-// K of lane group g = l / 16 (64 bytes of codes, 8 block scales), dequantizes them in
-// registers -- E2M1 -> float by the hardware converter, times the E4M3 block scale in
-// float32 (the product is exact and has at most 6 significant bits, so it is an exact
-// bf16) -- and feeds 16x16x32 bf16 MFMAs with the activations as the other operand.
-// The K order inside an MFMA is a permutation shared by both operands, which lets each
-// lane keep 128 contiguous K.  The four waves of a workgroup split the K chunks of one
-// split and add their partial tiles through LDS.  The LoRA down-projection x A^T runs
-// in the same launch: extra workgroups treat the bf16 rows of A as weight rows.
-// Output: float32 partial sums [split][m][row].
+// QeRL's rollout speedup comes from decoding with the policy's weight path in NVFP4
+// (tldrocket.com QeRL page, paragraph after "Key Features of QeRL").  With a handful of
+// tokens the layer streams 0.5625 byte per weight and is bound by HBM, so everything is
+// organised around reading the packed codes once, as early as possible.
 //
-// Kernel 2 (skinny_reduce_kernel): sums the K splits in a fixed order, multiplies by
-// S, rounds s.t to bf16 and adds the LoRA up-projection with one 16x16x32 bf16 MFMA per
-// 32 ranks, then writes bf16 (round to nearest even) or float32.
+// Work items (one workgroup of four waves each, 1-D grid):
+//   * LoRA items come first in dispatch order: 64 R bf16 rows of A (16 R per wave)
+//     against the activations over ONE 256-wide K chunk; float32 partials of x A^T.
+//   * weight items: 64 R NVFP4 rows (16 R per wave) over one K split of several chunks.
+// Within a chunk, lane l reads row (l % 16) of each of its wave's row tiles and the 64
+// consecutive K of lane group g = l / 16 (32 bytes of codes, 4 block scales).  Chunks
+// are processed in batches of CB: the codes of the next batch are loaded into registers
+// and its activations x[m][k] staged into LDS (double buffer) while the current batch is
+// multiplied.  Codes are dequantized in registers -- E2M1 -> float by the hardware
+// converter, times the E4M3 block scale in float32 (exact, at most 6 significant bits,
+// hence an exact bf16) -- and fed to 16x16x32 bf16 MFMAs whose B operand (activations)
+// comes from LDS.  The K order inside an MFMA is a permutation shared by both operands.
+//
+// Completion without a second launch: when K is split over several items, each stores its
+// partial tile with device-scope (write-through) stores and increments an integer counter;
+// the last arrival reads the partials back with device-scope loads and adds them in split
+// order.  The last LoRA item of an m group
+// writes t = bf16(s . sum) and raises a flag; a weight row group's last arrival waits for
+// that flag (LoRA items are dispatched before every weight item, so they are running or
+// done; the wait is bounded), adds t B^T with one MFMA per 32 ranks, applies S and stores
+// y.  Every counter and flag is returned to zero by the call that used it, so the
+// workspace only has to be zero before its first use.
 #include "common.hpp"
+#include "gemv_common.hpp"
 #include "launch.hpp"
 
 namespace ql {
 
-constexpr int kSkThreads = 256;
-constexpr int kChunk = 512;  // K per wave iteration: 4 lane groups x 128
+constexpr int kGvThreads = 256;
+constexpr int kGvChunk = 256;  // K per chunk: 4 lane groups x 64
 
-struct SkinnyArgs {
+struct GvArgs {
   const uint16_t* x;
   int64_t m, k;
   const uint8_t* codes;
   const uint8_t* scales;
+  const float* tensor_scale;
   const uint16_t* lora_a;
+  const uint16_t* lora_b;
   int32_t rank;
-  int64_t rows_w;        // NVFP4 rows (n)
-  int64_t rows_w_pad;    // first LoRA row in the partials (n padded to whole row tiles)
-  int64_t rows_total;
-  int64_t wg_w;          // workgroups along rows for the NVFP4 rows
+  float lora_scale;
+  int64_t n;
+  void* y;
+  int out_f32;
+  int produce_y;          // 0: LoRA-only launch that just leaves t in the workspace
+  // plan
+  int splits;
+  int64_t cps;            // chunks per split
   int64_t kchunks;
-  int64_t cps;           // chunks per split
-  float* partials;
+  int64_t groups_w;       // weight row groups (64 R rows each)
+  int64_t groups_l;       // LoRA row groups
+  int m_groups;           // m groups (16 MT rows each); weight items only use m group 0
+  int64_t rows_w_pad;     // row length of the weight partials
+  int64_t rows_l_pad;     // row length of the LoRA partials
+  int rank_pad;           // row length of t (multiple of 32)
+  int xstride;            // LDS row stride of staged activations (elements)
+  int xbuf;               // elements per LDS activation buffer (two buffers)
+  // workspace
+  uint32_t* cnt_w;        // [groups_w]
+  uint32_t* cnt_l;        // [m_groups]
+  uint32_t* t_ready;      // [m_groups]
+  uint32_t* fin;          // [1]
+  uint16_t* t;            // [m][rank_pad] bf16
+  float* part_w;          // [splits][m][rows_w_pad]
+  float* part_l;          // [kchunks][m][rows_l_pad]
 };
 
-// 8 E2M1 codes (one dword) times one block scale -> 8 exact bf16 values.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t c, float sc) {
-  f32x2 p0 = e2m1_unpack2<0>(c), p1 = e2m1_unpack2<1>(c), p2 = e2m1_unpack2<2>(c),
-        p3 = e2m1_unpack2<3>(c);
-  uint32_t o0 = pack_exact_bf16(p0.x * sc, p0.y * sc);
-  uint32_t o1 = pack_exact_bf16(p1.x * sc, p1.y * sc);
-  uint32_t o2 = pack_exact_bf16(p2.x * sc, p2.y * sc);
-  uint32_t o3 = pack_exact_bf16(p3.x * sc, p3.y * sc);
-  i32x4 o = {(int)o0, (int)o1, (int)o2, (int)o3};
-  return __builtin_bit_cast(bf16x8, o);
-}
+// Register image of one chunk for one row tile: 32 bytes of codes and 4 scale bytes.
+struct ChunkRegs {
+  uint4 c0, c1;
+  uint32_t s;
+};
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  i32x4 z = {0, 0, 0, 0};
-  return __builtin_bit_cast(bf16x8, z);
-}
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  uint4 v = *(const uint4*)p;
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-template <int MT, int R, bool LORA, bool FULL>
-__device__ __forceinline__ void skinny_chunk(const SkinnyArgs& a, int64_t row0, int64_t row_lim,
-                                             int64_t mbase, int64_t kk, f32x4 (&acc)[R][MT]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int64_t kl = kk + 128 * g;                              // first K of this lane
-  const int valid = FULL ? 128 : (int)max((int64_t)0, min((int64_t)128, a.k - kl));
-
-  // A operand source for each row tile: NVFP4 codes + scales, or bf16 rows of LoRA A.
-  uint4 cw[R][4];
-  uint2 sw[R];
-  if constexpr (!LORA) {
+template <bool ALIGNED>
+__device__ __forceinline__ ChunkRegs load_chunk(const GvArgs& a, int64_t row, bool rv, int64_t kl) {
+  ChunkRegs cr;
+  const uint8_t* cp = a.codes + row * (a.k / 2) + kl / 2;
+  const uint8_t* sp = a.scales + row * (a.k / 16) + kl / 16;
+  if (ALIGNED) {  // K % 256 == 0: whole chunks, naturally aligned 16- and 4-byte loads
+    cr.c0 = rv ? *(const uint4*)cp : make_uint4(0, 0, 0, 0);
+    cr.c1 = rv ? *(const uint4*)(cp + 16) : make_uint4(0, 0, 0, 0);
+    cr.s = rv ? *(const uint32_t*)sp : 0u;
+  } else {        // K % 16 == 0: 16-element blocks, 8-byte code loads, byte scale loads
+    uint32_t cw[8], sb[4];
 #pragma unroll
-    for (int p = 0; p < R; ++p) {
-      const int64_t row = row0 + 16 * p + r;
-      const bool rv = row < row_lim;
-      const uint8_t* cp = a.codes + row * (a.k / 2) + kl / 2;
-      const uint8_t* sp = a.scales + row * (a.k / 16) + kl / 16;
-      if (FULL) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cw[p][j] = rv ? *(const uint4*)(cp + 16 * j) : make_uint4(0, 0, 0, 0);
-        sw[p] = rv ? *(const uint2*)sp : make_uint2(0, 0);
-      } else {
-        uint32_t cd[16];
-        uint32_t sb[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {  // 16-element blocks: 8 code bytes, 1 scale byte
-          const bool bv = rv && 16 * b < valid;
-          uint2 v = bv ? *(const uint2*)(cp + 8 * b) : make_uint2(0, 0);
-          cd[2 * b] = v.x;
-          cd[2 * b + 1] = v.y;
-          sb[b] = bv ? sp[b] : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cw[p][j] = make_uint4(cd[4 * j], cd[4 * j + 1], cd[4 * j + 2], cd[4 * j + 3]);
-        sw[p].x = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-        sw[p].y = sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24);
-      }
+    for (int b = 0; b < 4; ++b) {
+      const bool ok = rv && kl + 16 * b < a.k;
+      const uint2 v = ok ? *(const uint2*)(cp + 8 * b) : make_uint2(0, 0);
+      cw[2 * b] = v.x;
+      cw[2 * b + 1] = v.y;
+      sb[b] = ok ? sp[b] : 0u;
     }
+    cr.c0 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    cr.c1 = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+    cr.s = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
   }
+  return cr;
+}
 
+// Stage x[mbase .. mbase+mrows) x [c_begin*256, c_end*256) into one LDS buffer (zero past K).
+__device__ __forceinline__ void stage_x(const GvArgs& a, uint16_t* xs, int64_t mbase, int mrows,
+                                        int64_t cbeg, int64_t cend) {
+  const int per_row = (int)(cend - cbeg) * (kGvChunk / 8);  // 16-byte units per row
+  const int units = mrows * per_row;
+  for (int u = threadIdx.x; u < units; u += kGvThreads) {
+    const int i = u / per_row;
+    const int col = (u - i * per_row) * 8;
+    const int64_t k = cbeg * kGvChunk + col;
+    // K % 16 == 0 and k % 8 == 0: a unit is entirely inside or entirely past K
+    const uint4 v = k < a.k ? *(const uint4*)(a.x + (mbase + i) * a.k + k) : make_uint4(0, 0, 0, 0);
+    *(uint4*)(xs + i * a.xstride + col) = v;
+  }
+}
+
+// B fragment of m tile q, chunk slot ci, k-step t (8 bf16 of row 16q + r).
+template <int MT>
+__device__ __forceinline__ bf16x8 x_frag(const GvArgs& a, const uint16_t* xs, int mrows, int q,
+                                         int ci, int t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, g = lane >> 4;
+  const int mi = 16 * q + r;
+  if (mi >= mrows) return gv_zero8();
+  return __builtin_bit_cast(bf16x8, *(const uint4*)(xs + mi * a.xstride + ci * kGvChunk + 64 * g + 8 * t));
+}
+
+// Multiply a batch of weight chunks held in registers against staged activations.
+template <int MT, int R, int CB>
+__device__ __forceinline__ void mul_batch(const GvArgs& a, const uint16_t* xs, int mrows, int nch,
+                                          const ChunkRegs (&cr)[CB][R], f32x4 (&acc)[R][MT]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {  // 32 K per step of j, 4 MFMA k-steps of 8 per lane
-    bf16x8 bx[4][MT];
+  for (int ci = 0; ci < CB; ++ci) {
+    if (ci >= nch) break;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int e0 = 32 * j + 8 * t;                              // element offset in lane range
+    for (int t = 0; t < 8; ++t) {
+      bf16x8 bx[MT];
 #pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mrow = mbase + 16 * q + r;
-        const bool ok = mrow < a.m && (FULL || e0 < valid);
-        bx[t][q] = ok ? load_bf16x8(a.x + mrow * a.k + kl + e0) : zero_bf16x8();
-      }
-    }
+      for (int q = 0; q < MT; ++q) bx[q] = x_frag<MT>(a, xs, mrows, q, ci, t);
 #pragma unroll
-    for (int p = 0; p < R; ++p) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x8 av;
-        if constexpr (LORA) {
-          const int64_t row = row0 + 16 * p + r;
-          const int e0 = 32 * j + 8 * t;
-          const bool ok = row < row_lim && (FULL || e0 < valid);
-          av = ok ? load_bf16x8(a.lora_a + row * a.k + kl + e0) : zero_bf16x8();
-        } else {
-          const uint32_t c = t == 0 ? cw[p][j].x : t == 1 ? cw[p][j].y : t == 2 ? cw[p][j].z : cw[p][j].w;
-          const int blk = (32 * j + 8 * t) / 16;                  // block within the lane's 8
-          const uint32_t sbyte = ((blk < 4 ? sw[p].x : sw[p].y) >> (8 * (blk & 3))) & 0xFFu;
-          av = dequant8(c, e4m3_value(sbyte));
-        }
+      for (int p = 0; p < R; ++p) {
+        const uint32_t c = t == 0 ? cr[ci][p].c0.x : t == 1 ? cr[ci][p].c0.y : t == 2 ? cr[ci][p].c0.z :
+                           t == 3 ? cr[ci][p].c0.w : t == 4 ? cr[ci][p].c1.x : t == 5 ? cr[ci][p].c1.y :
+                           t == 6 ? cr[ci][p].c1.z : cr[ci][p].c1.w;
+        const bf16x8 av = gv_dequant8(c, e4m3_value((cr[ci][p].s >> (8 * (t >> 1))) & 0xFFu));
 #pragma unroll
         for (int q = 0; q < MT; ++q)
-          acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[t][q], acc[p][q], 0, 0, 0);
+          acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[q], acc[p][q], 0, 0, 0);
       }
     }
   }
 }
 
-template <int MT, int R, bool LORA>
-__device__ __forceinline__ void skinny_body(const SkinnyArgs& a, int64_t row0, int64_t row_lim,
-                                            int64_t row_out0, f32x4* red) {
+template <int R, int CB, bool ALIGNED>
+__device__ __forceinline__ void load_batch(const GvArgs& a, int64_t wrow0, int64_t cbeg, int64_t cend,
+                                           ChunkRegs (&cr)[CB][R]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ci = 0; ci < CB; ++ci) {
+    const int64_t c = cbeg + ci;
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+      const int64_t row = wrow0 + 16 * p + r;
+      cr[ci][p] = load_chunk<ALIGNED>(a, row, row < a.n && c < cend, c * kGvChunk + 64 * g);
+    }
+  }
+}
+
+// Counter arrival; true in every thread of the last-arriving workgroup.
+__device__ __forceinline__ bool arrive(uint32_t* cnt, uint32_t total, int* flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == total - 1;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Bounded wait for a flag raised by another workgroup (device-scope polls).
+__device__ __forceinline__ void wait_flag(const uint32_t* f) {
+  if (threadIdx.x == 0) {
+    int it = 0;
+    while (ld_dev_u32(f) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+}
+
+template <int MT, int R, int CB, bool ALIGNED>
+__global__ __launch_bounds__(kGvThreads) void gv_kernel(GvArgs a) {
+  extern __shared__ __align__(16) uint16_t gv_smem[];
+  __shared__ int flag;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int64_t split = blockIdx.y;
-  const int64_t mbase = (int64_t)blockIdx.z * 16 * MT;
-  const int64_t c0 = split * a.cps;
-  const int64_t c1 = min(c0 + a.cps, a.kchunks);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t items_l = a.groups_l * a.kchunks * a.m_groups;
+  const int xbuf = a.xbuf;
+  int64_t id = blockIdx.x;
 
   f32x4 acc[R][MT];
 #pragma unroll
@@ -161,47 +212,206 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& a, int64_t row0, i
 #pragma unroll
     for (int q = 0; q < MT; ++q) acc[p][q] = f32x4{0, 0, 0, 0};
 
-  for (int64_t c = c0 + wave; c < c1; c += 4) {
-    const int64_t kk = c * kChunk;
-    // The unguarded path needs whole 512-chunks and 8-byte aligned scale rows (k % 128 == 0).
-    if (kk + kChunk <= a.k && (a.k & 127) == 0) skinny_chunk<MT, R, LORA, true>(a, row0, row_lim, mbase, kk, acc);
-    else skinny_chunk<MT, R, LORA, false>(a, row0, row_lim, mbase, kk, acc);
-  }
-
-  // Add the four waves' tiles (fixed order) and store wave 0's result.
+  if (id < items_l) {
+    // ------------------------------------------------- LoRA item: one chunk of A rows
+    const int64_t grp = id % a.groups_l;
+    const int64_t c = (id / a.groups_l) % a.kchunks;
+    const int mg = (int)(id / (a.groups_l * a.kchunks));
+    const int64_t mbase = (int64_t)mg * 16 * MT;
+    const int mrows = (int)min((int64_t)16 * MT, a.m - mbase);
+    const int64_t wrow0 = grp * 64 * R + wave * 16 * R;
+    uint4 av[R][8];
 #pragma unroll
-  for (int p = 0; p < R; ++p) {
+    for (int p = 0; p < R; ++p) {
+      const int64_t row = wrow0 + 16 * p + r;
 #pragma unroll
-    for (int q = 0; q < MT; ++q) red[(wave * MT + q) * kWave + lane] = acc[p][q];
+      for (int t = 0; t < 8; ++t) {
+        const int64_t k = c * kGvChunk + 64 * g + 8 * t;
+        av[p][t] = (row < a.rank && k < a.k) ? *(const uint4*)(a.lora_a + row * a.k + k) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    stage_x(a, gv_smem, mbase, mrows, c, c + 1);
     __syncthreads();
-    if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bf16x8 bx[MT];
+#pragma unroll
+      for (int q = 0; q < MT; ++q) bx[q] = x_frag<MT>(a, gv_smem, mrows, q, 0, t);
+#pragma unroll
+      for (int p = 0; p < R; ++p)
+#pragma unroll
+        for (int q = 0; q < MT; ++q)
+          acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[p][t]), bx[q], acc[p][q], 0, 0, 0);
+    }
+    // partials [chunk][m][rows_l_pad]; lane holds m = mbase + 16 q + r, rows wrow0 + 16 p + 4 g + i
+#pragma unroll
+    for (int p = 0; p < R; ++p)
 #pragma unroll
       for (int q = 0; q < MT; ++q) {
-        f32x4 s = red[(0 * MT + q) * kWave + lane];
-        s += red[(1 * MT + q) * kWave + lane];
-        s += red[(2 * MT + q) * kWave + lane];
-        s += red[(3 * MT + q) * kWave + lane];
-        const int64_t mrow = mbase + 16 * q + (lane & 15);
+        const int64_t mrow = mbase + 16 * q + r;
+        if (mrow < a.m) st_dev4(a.part_l + (c * a.m + mrow) * a.rows_l_pad + wrow0 + 16 * p + 4 * g, acc[p][q]);
+      }
+    if (!arrive(a.cnt_l + mg, (uint32_t)(a.groups_l * a.kchunks), &flag)) return;
+    // last LoRA item of this m group: t = bf16(s . sum over chunks), then raise the flag
+    for (int64_t i = threadIdx.x; i < (int64_t)mrows * a.rank_pad; i += kGvThreads) {
+      const int64_t mm = mbase + i / a.rank_pad;
+      const int j = (int)(i % a.rank_pad);
+      float v = 0.0f;
+      if (j < a.rank)
+        for (int64_t cc = 0; cc < a.kchunks; ++cc) v += ld_dev(a.part_l + (cc * a.m + mm) * a.rows_l_pad + j);
+      a.t[mm * a.rank_pad + j] = (uint16_t)f32_to_bf16_rne(a.lora_scale * v);
+    }
+    // t is read by weight items of this launch (device-scope, see below) or by the next
+    // launch on the stream; make it visible before the flag goes up.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      st_dev_u32(a.cnt_l + mg, 0u);
+      if (a.produce_y) st_dev_u32(a.t_ready + mg, 1u);
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ weight item
+  id -= items_l;
+  const int64_t grp = id % a.groups_w;
+  const int64_t split = id / a.groups_w;
+  const int64_t wrow0 = grp * 64 * R + wave * 16 * R;   // this wave's first row
+  const int64_t c0 = split * a.cps, c1 = min(c0 + a.cps, a.kchunks);
+  const int mrows = (int)min((int64_t)16 * MT, a.m);
+
+  ChunkRegs ca[CB][R], cb_[CB][R];
+  int64_t cb = c0;
+  load_batch<R, CB, ALIGNED>(a, wrow0, cb, c1, ca);
+  stage_x(a, gv_smem, 0, mrows, cb, min(cb + CB, c1));
+  __syncthreads();
+  int buf = 0;
+  while (true) {
+    // batch in ca / LDS buffer `buf`; prefetch the next into cb_ / buf ^ 1
+    int64_t nb = cb + CB;
+    if (nb < c1) {
+      load_batch<R, CB, ALIGNED>(a, wrow0, nb, c1, cb_);
+      stage_x(a, gv_smem + (buf ^ 1) * xbuf, 0, mrows, nb, min(nb + CB, c1));
+    }
+    mul_batch<MT, R, CB>(a, gv_smem + buf * xbuf, mrows, (int)(min(cb + CB, c1) - cb), ca, acc);
+    __syncthreads();
+    if (nb >= c1) break;
+    buf ^= 1;
+    cb = nb;
+    nb = cb + CB;
+    if (nb < c1) {
+      load_batch<R, CB, ALIGNED>(a, wrow0, nb, c1, ca);
+      stage_x(a, gv_smem + (buf ^ 1) * xbuf, 0, mrows, nb, min(nb + CB, c1));
+    }
+    mul_batch<MT, R, CB>(a, gv_smem + buf * xbuf, mrows, (int)(min(cb + CB, c1) - cb), cb_, acc);
+    __syncthreads();
+    if (nb >= c1) break;
+    buf ^= 1;
+    cb = nb;
+  }
+
+  if (a.splits > 1) {
+#pragma unroll
+    for (int p = 0; p < R; ++p)
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mrow = 16 * q + r;
+        if (mrow < a.m) st_dev4(a.part_w + (split * a.m + mrow) * a.rows_w_pad + wrow0 + 16 * p + 4 * g, acc[p][q]);
+      }
+    if (!arrive(a.cnt_w + grp, (uint32_t)a.splits, &flag)) return;
+#pragma unroll
+    for (int p = 0; p < R; ++p)
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mrow = 16 * q + r;
+        f32x4 s = {0, 0, 0, 0};
+        if (mrow < a.m)
+          for (int sp = 0; sp < a.splits; ++sp)
+            s += ld_dev4(a.part_w + ((int64_t)sp * a.m + mrow) * a.rows_w_pad + wrow0 + 16 * p + 4 * g);
+        acc[p][q] = s;
+      }
+    if (threadIdx.x == 0) st_dev_u32(a.cnt_w + grp, 0u);
+  }
+  // The last arrival finishes the row group: lane holds C[n][m], m = 16 q + r, n = wrow0 + 16 p + 4 g + i
+  const float S = *a.tensor_scale;
+#pragma unroll
+  for (int p = 0; p < R; ++p)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[p][q] *= S;
+  if (a.rank > 0) {  // wait (bounded) for t from the LoRA items
+    wait_flag(a.t_ready);
+    for (int j0 = 0; j0 < a.rank_pad; j0 += 32) {
+      bf16x8 tb[MT];
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mrow = 16 * q + r;
         if (mrow < a.m) {
-          const int64_t row = row_out0 + 16 * p + 4 * (lane >> 4);
-          *(f32x4*)(a.partials + (split * a.m + mrow) * a.rows_total + row) = s;
+          const uint32_t* tp = (const uint32_t*)(a.t + mrow * a.rank_pad + j0 + 8 * g);
+          i32x4 tv = {(int)ld_dev_u32(tp), (int)ld_dev_u32(tp + 1), (int)ld_dev_u32(tp + 2), (int)ld_dev_u32(tp + 3)};
+          tb[q] = __builtin_bit_cast(bf16x8, tv);
+        } else {
+          tb[q] = gv_zero8();
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < R; ++p) {
+        const int64_t nrow = wrow0 + 16 * p + r;
+        uint32_t bw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int j = j0 + 8 * g + e;
+          const uint32_t b0 = (nrow < a.n && j < a.rank) ? a.lora_b[nrow * a.rank + j] : 0u;
+          const uint32_t b1 = (nrow < a.n && j + 1 < a.rank) ? a.lora_b[nrow * a.rank + j + 1] : 0u;
+          bw[e / 2] = b0 | (b1 << 16);
+        }
+        i32x4 bi = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bi);
+#pragma unroll
+        for (int q = 0; q < MT; ++q)
+          acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, tb[q], acc[p][q], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < R; ++p)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+      const int64_t mrow = 16 * q + r;
+      const int64_t nb = wrow0 + 16 * p + 4 * g;
+      if (mrow >= a.m || nb >= a.n) continue;
+      const f32x4 v = acc[p][q];
+      if (a.out_f32) {
+        float* y = (float*)a.y + mrow * a.n;
+        if (nb + 4 <= a.n && (a.n & 3) == 0) {
+          *(f32x4*)(y + nb) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nb + i < a.n) y[nb + i] = v[i];
+        }
+      } else {
+        uint16_t* y = (uint16_t*)a.y + mrow * a.n;
+        const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+        const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+        if (nb + 4 <= a.n && (a.n & 3) == 0) {
+          *(uint2*)(y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        } else {
+          if (nb + 0 < a.n) y[nb + 0] = (uint16_t)b0;
+          if (nb + 1 < a.n) y[nb + 1] = (uint16_t)b1;
+          if (nb + 2 < a.n) y[nb + 2] = (uint16_t)b2;
+          if (nb + 3 < a.n) y[nb + 3] = (uint16_t)b3;
         }
       }
     }
-    __syncthreads();
-  }
-}
-
-template <int MT, int R>
-__global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
-  __shared__ f32x4 red[4 * MT * kWave];
-  const int64_t bx = blockIdx.x;
-  if (bx < a.wg_w) {
-    const int64_t row0 = bx * 16 * R;
-    skinny_body<MT, R, false>(a, row0, a.rows_w, row0, red);
-  } else {
-    const int64_t row0 = (bx - a.wg_w) * 16 * R;
-    skinny_body<MT, R, true>(a, row0, a.rank, a.rows_w_pad + row0, red);
+  if (a.rank > 0) {
+    __syncthreads();  // every wave has read t
+    if (threadIdx.x == 0) {  // t was read (values in registers) before this point
+      const uint32_t done = __hip_atomic_fetch_add(a.fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (uint32_t)a.groups_w - 1) {  // every row group has read t: lower the flag
+        st_dev_u32(a.t_ready, 0u);
+        st_dev_u32(a.fin, 0u);
+      }
+    }
   }
 }
 
@@ -209,191 +419,147 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkinnyArgs a) {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-static int skinny_r(int mt) { return mt >= 3 ? 4 : (mt == 2 ? 2 : 1); }
+static int batch_chunks(int mt) { return mt == 1 ? 4 : (mt == 2 ? 2 : 1); }
 
+// m <= 64 with weight rows (n > 0), or any m for a LoRA-only launch (n == 0, m groups of 64).
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int32_t rank) {
   SkinnyPlan p;
-  p.mt = (int)min((int64_t)4, cdiv(m, 16));
+  const int64_t mt_rows = n > 0 ? m : 64;
+  p.mt = mt_rows <= 16 ? 1 : (mt_rows <= 32 ? 2 : 4);
+  p.r = p.mt;
   p.m_groups = (int)cdiv(m, 16 * p.mt);
-  const int R = skinny_r(p.mt);
   p.rows_w = n;
-  p.rows_w_pad = round_up(n, 16 * R);
+  p.rows_w_pad = round_up(n, 64 * p.r);
   p.rows_l = rank > 0 ? round_up(rank, 16) : 0;
-  p.rows_total = p.rows_w_pad + round_up(p.rows_l, 16 * R);
-  const int64_t kchunks = cdiv(k, kChunk);
-  const int64_t row_wgs = cdiv(n, 16 * R) + cdiv(p.rows_l, 16 * R);
-  // Aim for >= ~1024 workgroups (4 per CU) while keeping >= 4 chunks (one per wave) per split.
+  p.rows_total = round_up(p.rows_l, 64 * p.r);  // LoRA partial row length
+  p.groups_w = n > 0 ? cdiv(n, 64 * p.r) : 0;
+  p.groups_l = p.rows_l > 0 ? cdiv(p.rows_l, 64 * p.r) : 0;
+  p.rank_pad = (int)round_up(p.rows_l, 32);
+  const int64_t kchunks = cdiv(k, kGvChunk);
+  const int cb = batch_chunks(p.mt);
+  // At least ~4 workgroups per CU (2 for the wider tiles), splits of >= CB chunks while
+  // there are already more workgroups than CUs.
+  const int64_t target = p.mt == 1 ? 1024 : 512;
   int64_t splits = 1;
-  while (row_wgs * p.m_groups * splits < 1024 && cdiv(kchunks, splits * 2) >= 4) splits *= 2;
+  if (p.groups_w > 0) {
+    while (p.groups_w * splits < target && splits < kchunks) {
+      const int64_t next = splits * 2;
+      if (cdiv(kchunks, next) < cb && p.groups_w * splits >= 256) break;
+      splits = next;
+    }
+  }
   p.kchunks_per_split = cdiv(kchunks, splits);
   p.splits = (int)cdiv(kchunks, p.kchunks_per_split);
   return p;
 }
 
-size_t skinny_workspace(const SkinnyPlan& p, int64_t m) {
-  return (size_t)p.splits * (size_t)m * (size_t)p.rows_total * sizeof(float);
+// Workspace: counters (zero before first use, zero after every call) | t | partials.
+static size_t counter_words(const SkinnyPlan& p) { return (size_t)(p.groups_w + 2 * p.m_groups + 1); }
+
+static size_t part_w_bytes(const SkinnyPlan& p, int64_t m) {
+  return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)p.rows_w_pad * 4 : 0;
+}
+static size_t part_l_bytes(const SkinnyPlan& p, int64_t m, int64_t k) {
+  return p.rows_l > 0 ? (size_t)cdiv(k, kGvChunk) * (size_t)m * (size_t)p.rows_total * 4 : 0;
 }
 
-template <int MT, int R>
-static hipError_t launch_skinny_t(const SkinnyPlan& p, const SkinnyArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.wg_w + cdiv(p.rows_l, 16 * R)), (unsigned)p.splits, (unsigned)p.m_groups);
-  skinny_kernel<MT, R><<<grid, kSkThreads, 0, s>>>(a);
+size_t skinny_workspace(const SkinnyPlan& p, int64_t m, int64_t k) {
+  return align256(counter_words(p) * 4) + align256((size_t)m * (size_t)p.rank_pad * 2) +
+         align256(part_w_bytes(p, m)) + align256(part_l_bytes(p, m, k));
+}
+
+template <int MT, int R, int CB>
+static hipError_t launch_gv(const GvArgs& a, int64_t items, int mrows_lds, hipStream_t s) {
+  const size_t lds = 2 * (size_t)mrows_lds * (size_t)a.xstride * 2;
+  if (a.k % kGvChunk == 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)gv_kernel<MT, R, CB, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    gv_kernel<MT, R, CB, true><<<(unsigned)items, kGvThreads, lds, s>>>(a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)gv_kernel<MT, R, CB, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    gv_kernel<MT, R, CB, false><<<(unsigned)items, kGvThreads, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_skinny(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
-                         const uint8_t* codes, const uint8_t* scales, const uint16_t* lora_a,
-                         int32_t rank, float* partials, hipStream_t s) {
-  SkinnyArgs a;
+static hipError_t launch_gv_plan(const SkinnyPlan& p, GvArgs& a, char* ws, int64_t m, hipStream_t s) {
+  const int cb = batch_chunks(p.mt);
+  a.splits = p.splits;
+  a.cps = p.kchunks_per_split;
+  a.kchunks = cdiv(a.k, kGvChunk);
+  a.groups_w = p.groups_w;
+  a.groups_l = p.groups_l;
+  a.m_groups = p.m_groups;
+  a.rows_w_pad = p.rows_w_pad;
+  a.rows_l_pad = p.rows_total;
+  a.rank_pad = p.rank_pad;
+  a.xstride = cb * kGvChunk + 8;
+  uint32_t* cnt = (uint32_t*)ws;
+  a.cnt_w = cnt;
+  a.cnt_l = cnt + p.groups_w;
+  a.t_ready = a.cnt_l + p.m_groups;
+  a.fin = a.t_ready + p.m_groups;
+  size_t off = align256(counter_words(p) * 4);
+  a.t = (uint16_t*)(ws + off);
+  off += align256((size_t)m * (size_t)p.rank_pad * 2);
+  a.part_w = (float*)(ws + off);
+  off += align256(part_w_bytes(p, m));
+  a.part_l = (float*)(ws + off);
+  const int64_t items = a.groups_l * a.kchunks * a.m_groups + (a.produce_y ? a.groups_w * a.splits : 0);
+  if (items <= 0) return hipSuccess;
+  // LDS rows: the weight items stage min(m, 16 MT) rows; LoRA items 16 MT rows at most
+  const int mrows_lds = (int)min((int64_t)16 * p.mt, m);
+  a.xbuf = mrows_lds * a.xstride;
+  if (p.mt == 1) return launch_gv<1, 1, 4>(a, items, mrows_lds, s);
+  if (p.mt == 2) return launch_gv<2, 2, 2>(a, items, mrows_lds, s);
+  return launch_gv<4, 4, 1>(a, items, mrows_lds, s);
+}
+
+hipError_t launch_skinny_forward(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t n,
+                                 int64_t k, const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scale, const uint16_t* lora_a,
+                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
+                                 int out_f32, void* ws, hipStream_t s) {
+  GvArgs a = {};
   a.x = x;
   a.m = m;
   a.k = k;
   a.codes = codes;
   a.scales = scales;
-  a.lora_a = lora_a;
-  a.rank = p.rows_l > 0 ? rank : 0;
-  a.rows_w = p.rows_w;
-  a.rows_w_pad = p.rows_w_pad;
-  a.rows_total = p.rows_total;
-  const int R = skinny_r(p.mt);
-  a.wg_w = cdiv(p.rows_w, 16 * R);
-  a.kchunks = cdiv(k, kChunk);
-  a.cps = p.kchunks_per_split;
-  a.partials = partials;
-  switch (p.mt) {
-    case 1: return launch_skinny_t<1, 1>(p, a, s);
-    case 2: return launch_skinny_t<2, 2>(p, a, s);
-    case 3: return launch_skinny_t<3, 4>(p, a, s);
-    default: return launch_skinny_t<4, 4>(p, a, s);
-  }
-}
-
-// ------------------------------------------------------------------- reduce
-
-struct ReduceArgs {
-  int64_t m, n;
-  int splits;
-  int64_t rows_total, rows_w_pad;
-  const float* partials;
-  const float* tensor_scale;
-  const uint16_t* lora_b;
-  int32_t rank;
-  float lora_scale;
-  void* y;
-  int out_f32;
-};
-
-// bf16(lora_scale * t[m][j]) from the partials, 0 outside [0, rank) or for m >= M.
-__device__ __forceinline__ uint32_t lora_t_bf16(const ReduceArgs& a, int64_t m, int j) {
-  if (m >= a.m || j >= a.rank) return 0;
-  float t = 0.0f;
-  for (int s = 0; s < a.splits; ++s)
-    t += a.partials[((int64_t)s * a.m + m) * a.rows_total + a.rows_w_pad + j];
-  return f32_to_bf16_rne(a.lora_scale * t);
-}
-
-// One wave per 16 (n) x 16 (m) output tile; a workgroup holds four tiles along m.
-__global__ __launch_bounds__(kSkThreads) void skinny_reduce_kernel(ReduceArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t m0 = ((int64_t)blockIdx.y * 4 + wave) * 16;
-  if (m0 >= a.m) return;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  f32x4 lo = {0, 0, 0, 0};
-  if (a.rank > 0) {
-    for (int j0 = 0; j0 < a.rank; j0 += 32) {
-      // A operand: B_lora rows n0 + r, ranks j0 + 8g .. +8 (bf16); B operand: s.t for m0 + r.
-      uint32_t bw[4] = {0, 0, 0, 0}, tw[4] = {0, 0, 0, 0};
-      const int64_t nrow = n0 + r;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int j = j0 + 8 * g + e;
-        uint32_t b0 = (nrow < a.n && j < a.rank) ? a.lora_b[nrow * a.rank + j] : 0u;
-        uint32_t b1 = (nrow < a.n && j + 1 < a.rank) ? a.lora_b[nrow * a.rank + j + 1] : 0u;
-        bw[e / 2] = b0 | (b1 << 16);
-        tw[e / 2] = lora_t_bf16(a, m0 + r, j) | (lora_t_bf16(a, m0 + r, j + 1) << 16);
-      }
-      i32x4 bi = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
-      i32x4 ti = {(int)tw[0], (int)tw[1], (int)tw[2], (int)tw[3]};
-      lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bi),
-                                                   __builtin_bit_cast(bf16x8, ti), lo, 0, 0, 0);
-    }
-  }
-  // lane holds m = m0 + r, n = n0 + 4g + i
-  const int64_t m = m0 + r;
-  if (m >= a.m) return;
-  const float S = *a.tensor_scale;
-  const int64_t nb = n0 + 4 * g;
-  f32x4 acc = {0, 0, 0, 0};
-  for (int s = 0; s < a.splits; ++s)
-    acc += *(const f32x4*)(a.partials + ((int64_t)s * a.m + m) * a.rows_total + nb);
-  float out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = S * acc[i] + lo[i];
-  if (a.out_f32) {
-    float* y = (float*)a.y + m * a.n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (nb + i < a.n) y[nb + i] = out[i];
-  } else {
-    uint16_t* y = (uint16_t*)a.y + m * a.n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (nb + i < a.n) y[nb + i] = (uint16_t)f32_to_bf16_rne(out[i]);
-  }
-}
-
-hipError_t launch_skinny_reduce(const SkinnyPlan& p, int64_t m, int64_t n, const float* partials,
-                                const float* tensor_scale, const uint16_t* lora_b, int32_t rank,
-                                float lora_scale, void* y, int out_f32, hipStream_t s) {
-  ReduceArgs a;
-  a.m = m;
-  a.n = n;
-  a.splits = p.splits;
-  a.rows_total = p.rows_total;
-  a.rows_w_pad = p.rows_w_pad;
-  a.partials = partials;
   a.tensor_scale = tensor_scale;
+  a.lora_a = lora_a;
   a.lora_b = lora_b;
   a.rank = p.rows_l > 0 ? rank : 0;
   a.lora_scale = lora_scale;
+  a.n = n;
   a.y = y;
   a.out_f32 = out_f32;
-  dim3 grid((unsigned)cdiv(n, 16), (unsigned)cdiv(m, 64));
-  skinny_reduce_kernel<<<grid, kSkThreads, 0, s>>>(a);
-  return hipGetLastError();
+  a.produce_y = 1;
+  return launch_gv_plan(p, a, (char*)ws, m, s);
 }
 
-// ------------------------------------------- LoRA intermediate for the GEMM paths
-
-__global__ __launch_bounds__(kSkThreads) void lora_t_kernel(const float* __restrict__ partials,
-                                                            int64_t m, int splits,
-                                                            int64_t rows_total, int64_t row0,
-                                                            int32_t rank, int32_t rank_pad,
-                                                            float lora_scale, uint16_t* __restrict__ t) {
-  const int64_t total = m * rank_pad;
-  for (int64_t i = (int64_t)blockIdx.x * kSkThreads + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * kSkThreads) {
-    const int64_t mm = i / rank_pad;
-    const int j = (int)(i % rank_pad);
-    float v = 0.0f;
-    if (j < rank)
-      for (int s = 0; s < splits; ++s) v += partials[((int64_t)s * m + mm) * rows_total + row0 + j];
-    t[i] = (uint16_t)f32_to_bf16_rne(lora_scale * v);
-  }
+hipError_t launch_lora_down(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
+                            const uint16_t* lora_a, int32_t rank, float lora_scale, void* ws,
+                            hipStream_t s) {
+  GvArgs a = {};
+  a.x = x;
+  a.m = m;
+  a.k = k;
+  a.lora_a = lora_a;
+  a.rank = rank;
+  a.lora_scale = lora_scale;
+  a.n = 0;
+  a.produce_y = 0;
+  return launch_gv_plan(p, a, (char*)ws, m, s);
 }
 
-hipError_t launch_lora_t(const SkinnyPlan& p, int64_t m, const float* partials, int32_t rank,
-                         float lora_scale, uint16_t* t, hipStream_t s) {
-  const int32_t rank_pad = (int32_t)round_up(rank, 32);
-  const int64_t total = m * rank_pad;
-  const int grid = (int)min((int64_t)4096, cdiv(total, kSkThreads));
-  lora_t_kernel<<<grid, kSkThreads, 0, s>>>(partials, m, p.splits, p.rows_total,
-                                            p.rows_w_pad, rank, rank_pad, lora_scale, t);
-  return hipGetLastError();
+uint16_t* lora_t_in_workspace(const SkinnyPlan& p, void* ws) {
+  return (uint16_t*)((char*)ws + align256(counter_words(p) * 4));
 }
 
 }  // namespace ql

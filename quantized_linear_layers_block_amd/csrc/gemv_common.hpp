@@ -1,0 +1,62 @@
+// Device helpers shared by the few-token NVFP4 kernels: exact dequantization of E2M1
+// codes to bf16 MFMA operands, and device-scope publication of data that another
+// workgroup of the same launch will read.
+#pragma once
+
+#include "common.hpp"
+
+namespace ql {
+
+constexpr int kGvSpinLimit = 1 << 22;  // bounded wait for another workgroup's flag
+
+// 8 E2M1 codes (one dword) times one block scale -> 8 exact bf16 values.
+__device__ __forceinline__ bf16x8 gv_dequant8(uint32_t c, float sc) {
+  const f32x2 p0 = e2m1_unpack2<0>(c), p1 = e2m1_unpack2<1>(c), p2 = e2m1_unpack2<2>(c),
+              p3 = e2m1_unpack2<3>(c);
+  i32x4 o = {(int)pack_exact_bf16(p0.x * sc, p0.y * sc), (int)pack_exact_bf16(p1.x * sc, p1.y * sc),
+             (int)pack_exact_bf16(p2.x * sc, p2.y * sc), (int)pack_exact_bf16(p3.x * sc, p3.y * sc)};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+__device__ __forceinline__ bf16x8 gv_zero8() {
+  i32x4 z = {0, 0, 0, 0};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Cross-workgroup publication.  Data another workgroup will read is stored with
+// device-scope (write-through, "sc1") stores and read with device-scope loads, so no
+// L2-wide write-back or invalidate is needed; s_waitcnt 0 makes sure those stores have
+// completed before the counter or flag that announces them is touched.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* p, f32x4 v) {
+  st_dev(p, v[0]);
+  st_dev(p + 1, v[1]);
+  st_dev(p + 2, v[2]);
+  st_dev(p + 3, v[3]);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_dev4(const float* p) {
+  return f32x4{ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3)};
+}
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Bounded wait for a flag raised by another workgroup, for the calling wave only (lane 0
+// polls with device-scope loads while the other lanes are masked off).
+__device__ __forceinline__ void wave_wait_flag(const uint32_t* f) {
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    int it = 0;
+    while (ld_dev_u32(f) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+}  // namespace ql

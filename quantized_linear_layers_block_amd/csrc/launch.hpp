@@ -39,29 +39,56 @@ size_t requant_table_bytes(int32_t count);
 hipError_t launch_requant(void* table, const RequantHeader& h, int32_t* status, hipStream_t s);
 int64_t requant_units(int32_t format, int64_t n, int64_t k);
 
-// ---- NVFP4 / bf16 skinny GEMM for few tokens (gemv.hip)
-// partials[split][m][rows_total] float32 with rows_total = n + rank_pad
+// ---- NVFP4 few-token layer and LoRA down-projection (gemv.hip)
 struct SkinnyPlan {
-  int mt;          // m tiles of 16 per workgroup (1..4)
-  int splits;      // k splits
-  int64_t kchunks_per_split;  // 512-wide k chunks per split
-  int m_groups;    // workgroups along m
-  int64_t rows_w;      // NVFP4 rows (n)
-  int64_t rows_w_pad;  // n rounded up to a whole number of workgroup row tiles
-  int64_t rows_l;      // bf16 LoRA rows (rank padded to 16), 0 if none
-  int64_t rows_total;
+  int mt;                     // m tiles of 16 per workgroup (1, 2, 4)
+  int r;                      // row tiles of 16 per wave
+  int splits;                 // K splits
+  int64_t kchunks_per_split;  // 256-wide K chunks per split
+  int m_groups;               // groups of 16 mt tokens
+  int64_t rows_w;             // NVFP4 rows (n)
+  int64_t rows_w_pad;         // n rounded up to whole row groups
+  int64_t rows_l;             // LoRA rows (rank rounded up to 16), 0 if none
+  int64_t rows_total;         // row length of the LoRA partials
+  int64_t groups_w, groups_l; // row groups of 16 r rows
+  int rank_pad;               // row length of t (rank rounded up to 32)
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int32_t rank);
-size_t skinny_workspace(const SkinnyPlan& p, int64_t m);
-hipError_t launch_skinny(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
-                         const uint8_t* codes, const uint8_t* scales, const uint16_t* lora_a,
-                         int32_t rank, float* partials, hipStream_t s);
-hipError_t launch_skinny_reduce(const SkinnyPlan& p, int64_t m, int64_t n, const float* partials,
-                                const float* tensor_scale, const uint16_t* lora_b, int32_t rank,
-                                float lora_scale, void* y, int out_f32, hipStream_t s);
-// t[m][j] = bf16(lora_scale * sum over splits of partials[s][m][rows_w + j]) for the GEMM paths
-hipError_t launch_lora_t(const SkinnyPlan& p, int64_t m, const float* partials, int32_t rank,
-                         float lora_scale, uint16_t* t, hipStream_t s);
+size_t skinny_workspace(const SkinnyPlan& p, int64_t m, int64_t k);
+// y = S x Wq^T + bf16(s x A^T) B^T in one launch (m <= 64).  ws must be zero before its
+// first use; the call leaves its counters zero.
+hipError_t launch_skinny_forward(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t n,
+                                 int64_t k, const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scale, const uint16_t* lora_a,
+                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
+                                 int out_f32, void* ws, hipStream_t s);
+// t = bf16(s x A^T) [m][rank_pad] into the workspace (plan from plan_skinny(m, 0, k, rank)).
+hipError_t launch_lora_down(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
+                            const uint16_t* lora_a, int32_t rank, float lora_scale, void* ws,
+                            hipStream_t s);
+uint16_t* lora_t_in_workspace(const SkinnyPlan& p, void* ws);
+
+// ---- NVFP4 layer for up to 32 tokens (gemv16.hip); workspace zero before first use
+struct G16Plan {
+  int mt;             // m tiles of 16 (1 or 2)
+  int64_t tiles_w;    // weight row tiles of 16
+  int64_t kchunks;    // 256-wide K chunks
+  int64_t tiles_l;    // LoRA row tiles of 16
+  int64_t lgroups;    // LoRA chunk groups
+  int lc;             // chunks per LoRA item
+  int rank_pad;
+  int64_t cps;        // chunks per K split
+  int splits;
+  int64_t n_pad;
+  int xstride;        // LDS row stride of the staged activations
+  size_t lds_bytes;
+};
+G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank);
+size_t g16_workspace(const G16Plan& p, int64_t m);
+hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                      const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                      const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
+                      float lora_scale, void* y, int out_f32, void* ws, hipStream_t s);
 
 // ---- large-M GEMMs (gemm_nvfp4.hip, gemm_fp8.hip)
 hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
