@@ -3,30 +3,31 @@
 //   y = S . x . (E2M1 * E4M3)^T  +  bf16(s . x A^T) . B^T
 //
 // This is the decoding case of QeRL's NVFP4 weight path (tldrocket.com QeRL page,
-// paragraph after "Key Features of QeRL"): 0.5625 byte per weight streamed once, so the
-// design minimises the latency chain of every workgroup.
+// paragraph after "Key Features of QeRL"): 0.5625 byte per weight is streamed once, so the
+// design is about keeping HBM busy from the first cycle and hiding every other latency
+// behind that stream.
 //
-// * A workgroup owns 16 weight rows; its four waves take interleaved 256-wide K chunks,
-//   each lane reading row (l % 16) and the 64 consecutive K of lane group g = l / 16
-//   (32 bytes of codes, 4 block scales) -- four chunks per wave are loaded before any
-//   is used, and the next four while these are multiplied.
-// * The activations of the workgroup's whole K range (at most 32 KB) are copied into LDS
-//   once, while the first codes are in flight; they are the B operand of 16x16x32 bf16
-//   MFMAs whose A operand is the codes dequantized in registers (E2M1 -> float by the
-//   hardware converter, times the E4M3 block scale in float32: exact, at most 6
-//   significant bits, hence an exact bf16).  The K order inside an MFMA is a permutation
-//   shared by both operands.
-// * The four waves' tiles are added in LDS.  K is split over several workgroups only when
-//   there are too few row tiles to fill the chip; the partial tiles then go to the
-//   workspace with device-scope stores, and the last arrival on the row tile's counter
-//   loads all of them at once and adds them in split order.
-// * LoRA: items that multiply 16 rows of A by up to eight K chunks are dispatched before
-//   all weight items; each stores its partial of x A^T (device scope) and bumps a counter.
-//   A row tile's finishing workgroup (its B rows were fetched at the start) waits for the
-//   counter (bounded; the LoRA items were dispatched first, so they are running or done),
-//   loads every partial at once, forms t = bf16(s . x A^T) in LDS in a fixed order, adds
-//   t B^T with one MFMA per 32 ranks, applies S and stores y.  Counters are returned to
-//   zero by the call that used them.
+// * A workgroup owns RT tiles of 16 weight rows (RT = 1 or 2) and a range of 256-wide K
+//   chunks; its four waves take the chunks in turn.  For each chunk a lane reads row
+//   (l % 16) of every row tile, K columns 64 (l / 16) .. +64 (32 bytes of codes and 4 block
+//   scales).  A wave issues up to four such (chunk, row tile) loads before using any.
+// * The activations of the workgroup's K range (at most 30 KB) are fetched into registers
+//   first, then the LoRA B rows, then the codes; the activations are written to LDS and the
+//   workgroup synchronises while the codes are still in flight, so each chunk is multiplied
+//   as soon as it arrives.  They are the B operand of 16x16x32 bf16 MFMAs whose A operand is
+//   the codes dequantized in registers (E2M1 -> float by the hardware converter, times the
+//   E4M3 block scale in float32: exact, at most 6 significant bits, hence an exact bf16).
+//   The K order inside an MFMA is a permutation shared by both operands.
+// * The four waves' tiles are added in LDS in a fixed order.  When the K range is split
+//   over several workgroups, the partial tiles go to the workspace with device-scope stores
+//   and the last arrival on the row tile's counter adds all of them in split order.
+// * LoRA: items that multiply 16 rows of A by up to four K chunks are dispatched before all
+//   weight items; each stores its partial of x A^T (device scope) and counts itself on a
+//   counter.  The last one adds the partials in a fixed order, publishes t = bf16(s . x A^T)
+//   once and raises a flag.  A row tile's finishing waves (their B rows were fetched at the
+//   start) wait for the flag (bounded; LoRA items are dispatched first, so they are running
+//   or done), add t B^T with one MFMA per 32 ranks, apply S and store y.  Counters and the
+//   flag are returned to zero by the call that used them.
 #include "../../include/qlinear.h"
 #include "common.hpp"
 #include "gemv_common.hpp"
@@ -35,10 +36,15 @@
 namespace ql {
 
 constexpr int kG16Threads = 256;
+constexpr int kG16Waves = kG16Threads / kWave;
 constexpr int kG16Chunk = 256;
-constexpr int kG16Batch = 4;          // chunks per wave loaded ahead
-constexpr int kG16MaxSplits = 16;
-constexpr int kG16XBytes = 32768;     // LDS for staged activations (5 workgroups per CU)
+constexpr int kG16Pairs = 4;           // (chunk, row tile) code loads in flight per wave
+constexpr int kG16XBytes = 30720;      // LDS for staged activations (5 workgroups per CU)
+constexpr int kG16XUnits = 8;          // 16-byte activation units per thread (8 * 256 * 16 >= 30720)
+constexpr int kG16XUnits1 = 2;         // the same for one token: 16 chunks of 32 units
+constexpr int kG16EarlyRank = 64;      // B rows of ranks up to 64 are fetched at the start
+constexpr int kG16MaxLoraChunks = 4;   // one chunk per wave
+constexpr int kG16CUs = 256;           // workgroups that run at once: 5 per CU for one token tile, 4 for two
 
 struct G16Args {
   const uint16_t* x;
@@ -56,18 +62,15 @@ struct G16Args {
   int splits;
   int64_t cps;        // chunks per split
   int64_t kchunks;
-  int64_t tiles_w;    // weight row tiles (16 rows)
+  int64_t tiles_w;    // weight tiles of 16 * RT rows
   int64_t tiles_l;    // LoRA row tiles (16 rows of A)
   int64_t lgroups;    // LoRA chunk groups
-  int lc;             // chunks per LoRA item (at most 8: two per wave)
+  int lc;             // chunks per LoRA item (at most four: one per wave)
   int rank_pad;       // t row length (multiple of 32)
   int64_t n_pad;      // row length of the weight partials
   int xstride;        // LDS row stride of the activations (elements)
-  uint32_t* cnt_w;    // [tiles_w]
-  uint32_t* cnt_l;    // [1]
-  uint32_t* t_ready;  // [1]
-  uint32_t* fin;      // [1]
-  uint16_t* t;        // [m][rank_pad]
+  uint32_t* ctr;      // counters and flags, one per 128-byte line (g16_line_*)
+  uint32_t* t;        // [m][rank_pad / 2] bf16 pairs
   float* part_w;      // [splits][m][n_pad]
   float* part_l;      // [lgroups][m][tiles_l * 16]
 };
@@ -77,24 +80,75 @@ struct G16Chunk {
   uint32_t s;
 };
 
+// Counters and flags, each on a 128-byte line of its own (atomics on one line serialise and
+// delay every other access to it): [0, tiles_w) split arrivals per row tile, the LoRA
+// counter, the t flag, 32 finishing groups, the finishing top counter.
+constexpr int kG16LineWords = 32;
+constexpr int kG16FinGroups = 32;
+__device__ __forceinline__ uint32_t* g16_ctr(const G16Args& a, int64_t line) { return a.ctr + line * kG16LineWords; }
+__device__ __forceinline__ int64_t g16_line_l(const G16Args& a) { return a.tiles_w; }
+__device__ __forceinline__ int64_t g16_line_t(const G16Args& a) { return a.tiles_w + 1; }
+__device__ __forceinline__ int64_t g16_line_fg(const G16Args& a, int j) { return a.tiles_w + 2 + j; }
+__device__ __forceinline__ int64_t g16_line_ft(const G16Args& a) { return a.tiles_w + 2 + kG16FinGroups; }
+
+// One finishing row tile on a two-level counter (tile i counts in group i % 32); true for the
+// last one overall.  Every last arrival returns its counter to zero.
+__device__ __forceinline__ bool g16_fin(const G16Args& a, int64_t tile) {
+  const int j = (int)(tile % kG16FinGroups);
+  const int64_t gsize = (a.tiles_w - j + kG16FinGroups - 1) / kG16FinGroups;
+  const int ngroups = a.tiles_w < kG16FinGroups ? (int)a.tiles_w : kG16FinGroups;
+  uint32_t* cg = g16_ctr(a, g16_line_fg(a, j));
+  if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)gsize - 1) return false;
+  st_dev_u32(cg, 0u);
+  uint32_t* ct = g16_ctr(a, g16_line_ft(a));
+  if (__hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)ngroups - 1) return false;
+  st_dev_u32(ct, 0u);
+  return true;
+}
+
+// Memory operations complete in order, and the compiler can only count the ones still in
+// flight (and wait for exactly the ones a value needs) across straight-line code.  So every
+// load below is issued unconditionally, from a clamped in-bounds address when the lane has
+// nothing to load, and its value is then masked to zero.  The mask goes through an empty asm
+// statement: otherwise the compiler turns "ok ? load : 0" back into a branch around the load.
+__device__ __forceinline__ uint32_t opaque_mask(bool ok) {
+  uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+__device__ __forceinline__ uint4 mask4(uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+__device__ __forceinline__ uint4 ld16_or0(const void* p, bool ok, const void* dummy) {
+  const uint4 v = *(const uint4*)(ok ? p : dummy);
+  return mask4(v, opaque_mask(ok));
+}
+
 template <bool ALIGNED>
 __device__ __forceinline__ G16Chunk g16_load(const G16Args& a, int64_t row, bool ok, int64_t kl) {
   G16Chunk cr;
+  if (!ok) row = 0, kl = 0;
   const uint8_t* cp = a.codes + row * (a.k / 2) + kl / 2;
   const uint8_t* sp = a.scales + row * (a.k / 16) + kl / 16;
   if (ALIGNED) {  // K % 256 == 0: whole chunks, naturally aligned 16- and 4-byte loads
-    cr.c0 = ok ? *(const uint4*)cp : make_uint4(0, 0, 0, 0);
-    cr.c1 = ok ? *(const uint4*)(cp + 16) : make_uint4(0, 0, 0, 0);
-    cr.s = ok ? *(const uint32_t*)sp : 0u;
+    const uint4 c0 = *(const uint4*)cp, c1 = *(const uint4*)(cp + 16);
+    const uint32_t sc = *(const uint32_t*)sp;
+    const uint32_t m = opaque_mask(ok);
+    cr.c0 = mask4(c0, m);
+    cr.c1 = mask4(c1, m);
+    cr.s = sc & m;
   } else {        // K % 16 == 0: whole 16-element blocks, 8-byte code loads, byte scales
     uint32_t cw[8], sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const bool bok = ok && kl + 16 * b < a.k;
-      const uint2 v = bok ? *(const uint2*)(cp + 8 * b) : make_uint2(0, 0);
-      cw[2 * b] = v.x;
-      cw[2 * b + 1] = v.y;
-      sb[b] = bok ? sp[b] : 0u;
+      const int64_t off = bok ? 16 * b : 0;
+      const uint2 v = *(const uint2*)(cp + off / 2);
+      const uint32_t sv = sp[off / 16];
+      const uint32_t m = opaque_mask(bok);
+      cw[2 * b] = v.x & m;
+      cw[2 * b + 1] = v.y & m;
+      sb[b] = sv & m;
     }
     cr.c0 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     cr.c1 = make_uint4(cw[4], cw[5], cw[6], cw[7]);
@@ -103,19 +157,40 @@ __device__ __forceinline__ G16Chunk g16_load(const G16Args& a, int64_t row, bool
   return cr;
 }
 
-// Copy x[0 .. mrows) x [c0*256, c1*256) into LDS (row stride xstride), zero past K.
-__device__ __forceinline__ void g16_stage_x(const G16Args& a, uint16_t* xs, int mrows, int64_t c0,
-                                            int64_t c1) {
-  const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);  // 16-byte units per row
+// Activations x[0 .. mrows) x [c0*256, c1*256) in 16-byte units: thread i takes units
+// i + 256 j (j < XU).  They are issued into registers first, so that the code loads issued
+// after them do not delay the copy to LDS (memory operations complete in order).  Row i of
+// the copy starts at element i * xstride; xo is a unit's byte offset in LDS, or -1 for a unit
+// past the range.  With TAIL (K not
+// a multiple of 256) units past K are zeroed; K % 16 == 0 and units are 8-element aligned,
+// so a unit lies entirely inside or entirely past K.
+template <int XU, bool TAIL>
+__device__ __forceinline__ void g16_x_issue(const G16Args& a, int mrows, int64_t c0, int64_t c1,
+                                            i32x4 (&xv)[XU], int (&xo)[XU]) {
+  const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);
   const int units = mrows * per_row;
-  for (int u = threadIdx.x; u < units; u += kG16Threads) {
+#pragma unroll
+  for (int j = 0; j < XU; ++j) {
+    const int u = threadIdx.x + kG16Threads * j;
     const int i = u / per_row;
-    const int col = (u - i * per_row) * 8;
-    const int64_t k = c0 * kG16Chunk + col;
-    // K % 16 == 0 and k % 8 == 0: a unit lies entirely inside or entirely past K
-    const uint4 v = k < a.k ? *(const uint4*)(a.x + (int64_t)i * a.k + k) : make_uint4(0, 0, 0, 0);
-    *(uint4*)(xs + i * a.xstride + col) = v;
+    const int64_t kk = c0 * kG16Chunk + (int64_t)(u - i * per_row) * 8;
+    const bool ok = TAIL ? (u < units && kk < a.k) : u < units;
+    const i32x4 v = *(const i32x4*)(ok ? a.x + (int64_t)i * a.k + kk : a.x);
+    if (TAIL) {
+      const int m = (int)opaque_mask(ok);
+      xv[j] = i32x4{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+    } else {
+      xv[j] = v;
+    }
+    xo[j] = u < units ? (i * a.xstride + (u - i * per_row) * 8) * 2 : -1;
   }
+}
+
+template <int XU>
+__device__ __forceinline__ void g16_x_store(uint16_t* xs, const i32x4 (&xv)[XU], const int (&xo)[XU]) {
+#pragma unroll
+  for (int j = 0; j < XU; ++j)
+    if (xo[j] >= 0) *(i32x4*)((char*)xs + xo[j]) = xv[j];
 }
 
 // B operand: 8 activations of token 16 q + r at LDS column `col`.
@@ -127,42 +202,52 @@ __device__ __forceinline__ bf16x8 g16_xfrag(const G16Args& a, const uint16_t* xs
   return __builtin_bit_cast(bf16x8, *(const uint4*)(xs + mi * a.xstride + col));
 }
 
-template <int MT>
+// One 256-wide chunk of RT row tiles: 8 K steps of 32, each MFMA'd against MT token tiles.
+template <int MT, int RT>
 __device__ __forceinline__ void g16_mul_chunk(const G16Args& a, const uint16_t* xs, int mrows,
-                                              int col0, const G16Chunk& cr, f32x4 (&acc)[MT]) {
+                                              int col0, const G16Chunk (&cr)[RT], f32x4 (&acc)[RT][MT]) {
   const int g = (threadIdx.x & (kWave - 1)) >> 4;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const uint32_t c = t == 0 ? cr.c0.x : t == 1 ? cr.c0.y : t == 2 ? cr.c0.z : t == 3 ? cr.c0.w :
-                       t == 4 ? cr.c1.x : t == 5 ? cr.c1.y : t == 6 ? cr.c1.z : cr.c1.w;
-    const bf16x8 av = gv_dequant8(c, e4m3_value((cr.s >> (8 * (t >> 1))) & 0xFFu));
+    bf16x8 xf[MT];
 #pragma unroll
-    for (int q = 0; q < MT; ++q)
-      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, g16_xfrag(a, xs, mrows, q, col0 + 64 * g + 8 * t),
-                                                       acc[q], 0, 0, 0);
-  }
-}
-
-// Sum the four waves' tiles (fixed order) into wave 0.
-template <int MT>
-__device__ __forceinline__ void g16_reduce(f32x4 (&acc)[MT], f32x4* red) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  if (wave > 0) {
+    for (int q = 0; q < MT; ++q) xf[q] = g16_xfrag(a, xs, mrows, q, col0 + 64 * g + 8 * t);
 #pragma unroll
-    for (int q = 0; q < MT; ++q) red[((wave - 1) * MT + q) * kWave + lane] = acc[q];
-  }
-  __syncthreads();
-  if (wave == 0) {
+    for (int rt = 0; rt < RT; ++rt) {
+      const G16Chunk& c = cr[rt];
+      const uint32_t w = t == 0 ? c.c0.x : t == 1 ? c.c0.y : t == 2 ? c.c0.z : t == 3 ? c.c0.w :
+                         t == 4 ? c.c1.x : t == 5 ? c.c1.y : t == 6 ? c.c1.z : c.c1.w;
+      const bf16x8 av = gv_dequant8(w, e4m3_value((c.s >> (8 * (t >> 1))) & 0xFFu));
 #pragma unroll
-    for (int q = 0; q < MT; ++q) {
-      acc[q] += red[(0 * MT + q) * kWave + lane];
-      acc[q] += red[(1 * MT + q) * kWave + lane];
-      acc[q] += red[(2 * MT + q) * kWave + lane];
+      for (int q = 0; q < MT; ++q)
+        acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xf[q], acc[rt][q], 0, 0, 0);
     }
   }
 }
 
+// Sum the four waves' tiles in a fixed order; wave w < RT*MT receives tile (w / MT, w % MT).
+// The LDS of the staged activations is reused, so every wave must be done reading it.
+template <int RT, int MT>
+__device__ __forceinline__ f32x4 g16_reduce(const f32x4 (&acc)[RT][MT], uint16_t* xs) {
+  f32x4* red = (f32x4*)xs;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) red[(wave * RT * MT + rt * MT + q) * kWave + lane] = acc[rt][q];
+  __syncthreads();
+  f32x4 v = {0, 0, 0, 0};
+  if (wave < RT * MT) {
+#pragma unroll
+    for (int w = 0; w < kG16Waves; ++w) v += red[(w * RT * MT + wave) * kWave + lane];
+  }
+  return v;
+}
+
+// All threads: count this workgroup on `cnt` once its device-scope stores have completed;
+// true in every thread of the workgroup that arrived last.
 __device__ __forceinline__ bool g16_arrive(uint32_t* cnt, uint32_t total, int* flag) {
   wait_stores();
   __syncthreads();
@@ -174,10 +259,111 @@ __device__ __forceinline__ bool g16_arrive(uint32_t* cnt, uint32_t total, int* f
   return *flag != 0;
 }
 
-template <int MT, bool ALIGNED, bool MULTI>
-__global__ __launch_bounds__(kG16Threads) void g16_kernel(G16Args a) {
+// LoRA up-projection A operand: row `row` of B, ranks 32 c + 8 g .. +8 (zero past the rank).
+// Ranks that are a multiple of 8: one 16-byte load (straight-line).
+__device__ __forceinline__ i32x4 g16_b_frag_vec(const G16Args& a, int64_t row, bool ok, int c) {
+  const int g = (threadIdx.x & (kWave - 1)) >> 4;
+  const int j0 = 32 * c + 8 * g;
+  ok = ok && j0 < a.rank;
+  return __builtin_bit_cast(i32x4, ld16_or0(a.lora_b + row * a.rank + j0, ok, a.x));
+}
+// Any rank: element loads.
+__device__ __forceinline__ i32x4 g16_b_frag_any(const G16Args& a, int64_t row, bool ok, int c) {
+  const int g = (threadIdx.x & (kWave - 1)) >> 4;
+  uint32_t w4[4] = {0, 0, 0, 0};
+  const int j0 = 32 * c + 8 * g;
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t b0 = j0 + e < a.rank ? a.lora_b[row * a.rank + j0 + e] : 0u;
+      const uint32_t b1 = j0 + e + 1 < a.rank ? a.lora_b[row * a.rank + j0 + e + 1] : 0u;
+      w4[e / 2] = b0 | (b1 << 16);
+    }
+  }
+  return i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+}
+
+// ------------------------------------------------------------------ LoRA item
+// 16 rows of A times chunks [c0, c1) of x (one chunk per wave).  The last item to finish
+// publishes t.
+template <int MT, int XU, bool TAIL>
+__device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, int* flag, int64_t id) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int mrows = (int)min((int64_t)16 * MT, a.m);
+  const int64_t tile = id % a.tiles_l;
+  const int64_t cg = id / a.tiles_l;
+  const int64_t c0 = cg * a.lc, c1 = min(c0 + a.lc, a.kchunks);
+  const int64_t c = c0 + wave;
+  const int64_t row = tile * 16 + r;
+
+  i32x4 xv[XU];
+  int xo[XU];
+  g16_x_issue<XU, TAIL>(a, mrows, c0, c1, xv, xo);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 av[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t kk = c * kG16Chunk + 64 * g + 8 * t;
+    av[t] = ld16_or0(a.lora_a + row * a.k + kk, c < c1 && row < a.rank && kk < a.k, a.x);
+  }
+  g16_x_store<XU>(xs, xv, xo);
+  __syncthreads();
+  f32x4 acc[1][MT];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) acc[0][q] = f32x4{0, 0, 0, 0};
+  if (c < c1) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int q = 0; q < MT; ++q)
+        acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, av[t]),
+            g16_xfrag(a, xs, mrows, q, (int)(c - c0) * kG16Chunk + 64 * g + 8 * t), acc[0][q], 0, 0, 0);
+  }
+  const f32x4 v = g16_reduce<1, MT>(acc, xs);
+  const int64_t lrow = a.tiles_l * 16;
+  if (wave < MT) {
+    const int64_t mi = 16 * wave + r;
+    if (mi < a.m) st_dev4(a.part_l + (cg * a.m + mi) * lrow + tile * 16 + 4 * g, v);
+  }
+  if (!g16_arrive(g16_ctr(a, g16_line_l(a)), (uint32_t)(a.tiles_l * a.lgroups), flag)) return;
+
+  // last LoRA item: t = bf16(s . (partials added in group order)), published once
+  const int rp2 = a.rank_pad / 2;
+  const int64_t stride = a.m * lrow;
+  for (int e = threadIdx.x; e < (int)a.m * rp2; e += kG16Threads) {
+    const int mi = e / rp2;
+    const int j = 2 * (e - mi * rp2);
+    const float* pp = a.part_l + (int64_t)mi * lrow + j;
+    float v0 = 0.0f, v1 = 0.0f;
+    for (int64_t g0 = 0; g0 < a.lgroups; g0 += 8) {  // 8 groups in flight, added in order
+      float p0[8], p1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = g0 + u < a.lgroups;
+        p0[u] = in && j < a.rank ? ld_dev(pp + (g0 + u) * stride) : 0.0f;
+        p1[u] = in && j + 1 < a.rank ? ld_dev(pp + (g0 + u) * stride + 1) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v0 += p0[u];
+        v1 += p1[u];
+      }
+    }
+    st_dev_u32(a.t + e, f32_to_bf16_rne(a.lora_scale * v0) | (f32_to_bf16_rne(a.lora_scale * v1) << 16));
+  }
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, g16_line_t(a)), 1u);
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int MT, int RT, bool ALIGNED, int XU>
+__global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALIGNED ? (MT == 1 ? 5 : 4) : 1))) void g16_kernel(G16Args a) {
   extern __shared__ __align__(16) uint16_t xs[];
-  __shared__ f32x4 red[3 * MT * kWave];
   __shared__ int flag;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -185,55 +371,8 @@ __global__ __launch_bounds__(kG16Threads) void g16_kernel(G16Args a) {
   const int mrows = (int)min((int64_t)16 * MT, a.m);
   const int64_t items_l = a.tiles_l * a.lgroups;
   int64_t id = blockIdx.x;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int q = 0; q < MT; ++q) acc[q] = f32x4{0, 0, 0, 0};
-
   if (id < items_l) {
-    // ------------------------------------- LoRA item: 16 rows of A, lc chunks (2 per wave)
-    const int64_t tile = id % a.tiles_l;
-    const int64_t cg = id / a.tiles_l;
-    const int64_t c0 = cg * a.lc, c1 = min(c0 + a.lc, a.kchunks);
-    const int64_t row = tile * 16 + r;
-    uint4 av[2][8];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t c = c0 + wave + 4 * i;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int64_t k = c * kG16Chunk + 64 * g + 8 * t;
-        av[i][t] = (row < a.rank && c < c1 && k < a.k) ? *(const uint4*)(a.lora_a + row * a.k + k)
-                                                      : make_uint4(0, 0, 0, 0);
-      }
-    }
-    g16_stage_x(a, xs, mrows, c0, c1);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t c = c0 + wave + 4 * i;
-      if (c < c1) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int q = 0; q < MT; ++q)
-            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, av[i][t]),
-                g16_xfrag(a, xs, mrows, q, (int)(c - c0) * kG16Chunk + 64 * g + 8 * t), acc[q], 0, 0, 0);
-      }
-    }
-    g16_reduce<MT>(acc, red);
-    const int64_t lrow = a.tiles_l * 16;
-    if (wave == 0) {
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        if (mi < a.m) st_dev4(a.part_l + (cg * a.m + mi) * lrow + tile * 16 + 4 * g, acc[q]);
-      }
-    }
-    // announce the partial; the weight tiles add all partials themselves
-    wait_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.cnt_l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g16_lora_item<MT, XU, !ALIGNED>(a, xs, &flag, id);
     return;
   }
 
@@ -242,200 +381,136 @@ __global__ __launch_bounds__(kG16Threads) void g16_kernel(G16Args a) {
   const int64_t tile = id % a.tiles_w;
   const int64_t split = id / a.tiles_w;
   const int64_t c0 = split * a.cps, c1 = min(c0 + a.cps, a.kchunks);
-  const int64_t row = tile * 16 + r;
-  const bool rv = row < a.n;
+  const int64_t row0 = tile * 16 * RT;
+  constexpr int kCB = kG16Pairs / RT;  // chunks per wave batch
 
-  // B rows of the LoRA up-projection do not depend on anything: fetch them first
-  // (lane: row tile*16 + r, ranks 32 c + 8 g .. +8, the A-operand layout of the MFMA)
-  constexpr int kMaxRankChunks = QLINEAR_MAX_RANK / 32;
-  i32x4 bw[kMaxRankChunks];
-  if (a.rank > 0) {
-    const int rc = a.rank_pad / 32;
-    const bool vec = (a.rank & 7) == 0;
+  i32x4 xv[XU];
+  int xo[XU];
+  g16_x_issue<XU, !ALIGNED>(a, mrows, c0, c1, xv, xo);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // waves w < RT*MT finish output tile (w / MT, w % MT); their B rows do not depend on
+  // anything, so small ranks fetch them now
+  const bool tile_wave = wave < RT * MT;
+  const int rt_e = tile_wave ? wave / MT : 0, q_e = tile_wave ? wave % MT : 0;
+  const int64_t brow = row0 + 16 * rt_e + r;
+  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
+  const i32x4 bw0 = g16_b_frag_vec(a, brow, early_b && tile_wave && brow < a.n, 0);
+  const i32x4 bw1 = g16_b_frag_vec(a, brow, early_b && tile_wave && brow < a.n, 1);
+  const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // code loads: some before the activations are copied to LDS (that copy waits for the
+  // activations only), the rest after, which keeps fewer registers live at once
+  constexpr int kEarly = XU > 4 ? 1 : kG16Pairs / 2;
+  G16Chunk ca[kCB][RT];
 #pragma unroll
-    for (int c = 0; c < kMaxRankChunks; ++c) {
-      uint32_t w4[4] = {0, 0, 0, 0};
-      const int j0 = 32 * c + 8 * g;
-      if (c < rc && rv) {
-        if (vec) {
-          if (j0 < a.rank) {
-            const uint4 v = *(const uint4*)(a.lora_b + row * a.rank + j0);
-            w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
-          }
-        } else {
+  for (int p = 0; p < kEarly; ++p) {
+    const int i = p / RT, rt = p % RT;
+    const int64_t c = c0 + wave + kG16Waves * i;
+    const int64_t row = row0 + 16 * rt + r;
+    ca[i][rt] = g16_load<ALIGNED>(a, row, row < a.n && c < c1, c * kG16Chunk + 64 * g);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  g16_x_store<XU>(xs, xv, xo);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t b0 = j0 + e < a.rank ? a.lora_b[row * a.rank + j0 + e] : 0u;
-            const uint32_t b1 = j0 + e + 1 < a.rank ? a.lora_b[row * a.rank + j0 + e + 1] : 0u;
-            w4[e / 2] = b0 | (b1 << 16);
-          }
+  for (int p = kEarly; p < kG16Pairs; ++p) {
+    const int i = p / RT, rt = p % RT;
+    const int64_t c = c0 + wave + kG16Waves * i;
+    const int64_t row = row0 + 16 * rt + r;
+    ca[i][rt] = g16_load<ALIGNED>(a, row, row < a.n && c < c1, c * kG16Chunk + 64 * g);
+  }
+  __syncthreads();
+
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[rt][q] = f32x4{0, 0, 0, 0};
+  // the plan gives every wave at most kCB chunks
+#pragma unroll
+  for (int i = 0; i < kCB; ++i) {
+    const int64_t c = c0 + wave + kG16Waves * i;
+    if (c < c1) g16_mul_chunk<MT, RT>(a, xs, mrows, (int)(c - c0) * kG16Chunk, ca[i], acc);
+  }
+  f32x4 v = g16_reduce<RT, MT>(acc, xs);
+
+  // v is C[n][m] of tile (rt_e, q_e): m = 16 q_e + r, n = nb + i
+  const int64_t mi = 16 * q_e + r;
+  const int64_t nb = row0 + 16 * rt_e + 4 * g;
+  if (a.splits > 1) {
+    if (tile_wave && mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + nb, v);
+    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, &flag)) return;
+    if (tile_wave) {
+      f32x4 s = {0, 0, 0, 0};
+      for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {  // 8 partials in flight, added in order
+        f32x4 part[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sp = sp0 + u;
+          part[u] = (sp < a.splits && mi < a.m)
+                        ? (sp == split ? v : ld_dev4(a.part_w + ((int64_t)sp * a.m + mi) * a.n_pad + nb))
+                        : f32x4{0, 0, 0, 0};
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += part[u];
       }
-      bw[c] = i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+      v = s;
+    }
+    if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, tile), 0u);
+  }
+
+  v *= ts;
+  if (a.rank > 0) {  // every wave passes the two barriers
+    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
+      int it = 0;
+      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
+    }
+    __syncthreads();
+    if (tile_wave) {
+      const int rc = a.rank_pad / 32;
+#pragma unroll
+      for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
+        if (c >= rc) break;
+        const i32x4 b = early_b ? (c == 0 ? bw0 : bw1) : g16_b_frag_any(a, brow, brow < a.n, c);
+        i32x4 tv = {0, 0, 0, 0};
+        if (mi < a.m) {
+          const uint32_t* tp = a.t + (mi * a.rank_pad + 32 * c + 8 * g) / 2;
+          tv = i32x4{(int)ld_dev_u32(tp), (int)ld_dev_u32(tp + 1), (int)ld_dev_u32(tp + 2), (int)ld_dev_u32(tp + 3)};
+        }
+        v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, tv),
+                                                    v, 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every tile wave of this workgroup has read t
+    if (threadIdx.x == 0 && g16_fin(a, tile)) {  // the last finishing tile returns the flags to zero
+      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
+      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
     }
   }
-
-  G16Chunk ca[kG16Batch];
+  if (!tile_wave) return;
+  if (mi >= a.m || nb >= a.n) return;
+  if (a.out_f32) {
+    float* y = (float*)a.y + mi * a.n;
+    if (nb + 4 <= a.n && (a.n & 3) == 0) {
+      *(f32x4*)(y + nb) = v;
+    } else {
 #pragma unroll
-  for (int i = 0; i < kG16Batch; ++i) {
-    const int64_t c = c0 + wave + 4 * i;
-    ca[i] = g16_load<ALIGNED>(a, row, rv && c < c1, c * kG16Chunk + 64 * g);
-  }
-  g16_stage_x(a, xs, mrows, c0, c1);
-  __syncthreads();
-  if constexpr (!MULTI) {  // every wave has at most kG16Batch chunks
-#pragma unroll
-    for (int i = 0; i < kG16Batch; ++i) {
-      const int64_t c = c0 + wave + 4 * i;
-      if (c < c1) g16_mul_chunk<MT>(a, xs, mrows, (int)(c - c0) * kG16Chunk, ca[i], acc);
+      for (int i = 0; i < 4; ++i)
+        if (nb + i < a.n) y[nb + i] = v[i];
     }
   } else {
-    G16Chunk cb[kG16Batch];
-    for (int64_t b0 = c0 + wave;;) {
-      // current batch in ca (chunks b0 + 4 i); prefetch the next into cb
-      const int64_t b1 = b0 + 4 * kG16Batch;
-      if (b1 < c1) {
-#pragma unroll
-        for (int i = 0; i < kG16Batch; ++i) {
-          const int64_t c = b1 + 4 * i;
-          cb[i] = g16_load<ALIGNED>(a, row, rv && c < c1, c * kG16Chunk + 64 * g);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kG16Batch; ++i) {
-        const int64_t c = b0 + 4 * i;
-        if (c < c1) g16_mul_chunk<MT>(a, xs, mrows, (int)(c - c0) * kG16Chunk, ca[i], acc);
-      }
-      if (b1 >= c1) break;
-      const int64_t b2 = b1 + 4 * kG16Batch;
-      if (b2 < c1) {
-#pragma unroll
-        for (int i = 0; i < kG16Batch; ++i) {
-          const int64_t c = b2 + 4 * i;
-          ca[i] = g16_load<ALIGNED>(a, row, rv && c < c1, c * kG16Chunk + 64 * g);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kG16Batch; ++i) {
-        const int64_t c = b1 + 4 * i;
-        if (c < c1) g16_mul_chunk<MT>(a, xs, mrows, (int)(c - c0) * kG16Chunk, cb[i], acc);
-      }
-      if (b2 >= c1) break;
-      b0 = b2;
-    }
-  }
-  g16_reduce<MT>(acc, red);
-
-  if (a.splits > 1) {
-    if (wave == 0) {
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        if (mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + tile * 16 + 4 * g, acc[q]);
-      }
-    }
-    if (!g16_arrive(a.cnt_w + tile, (uint32_t)a.splits, &flag)) return;
-    if (wave == 0) {
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        f32x4 part[kG16MaxSplits];
-#pragma unroll
-        for (int sp = 0; sp < kG16MaxSplits; ++sp)
-          part[sp] = (sp < a.splits && mi < a.m)
-                         ? ld_dev4(a.part_w + ((int64_t)sp * a.m + mi) * a.n_pad + tile * 16 + 4 * g)
-                         : f32x4{0, 0, 0, 0};
-        f32x4 s = part[0];
-#pragma unroll
-        for (int sp = 1; sp < kG16MaxSplits; ++sp) s += part[sp];
-        acc[q] = s;
-      }
-      if (lane == 0) st_dev_u32(a.cnt_w + tile, 0u);
-    }
-  }
-  // t = bf16(s . x A^T) from the LoRA partials, computed by the whole workgroup into LDS
-  uint16_t* tl = xs;  // the staged activations are no longer needed
-  if (a.rank > 0) {
-    if (threadIdx.x == 0) {  // bounded wait until every LoRA item has announced its partial
-      int it = 0;
-      while (ld_dev_u32(a.cnt_l) < (uint32_t)items_l && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(2);
-    }
-    __syncthreads();
-    const int64_t lrow = a.tiles_l * 16;
-    const int E = mrows * a.rank_pad;
-    for (int e = threadIdx.x; e < E; e += kG16Threads) {
-      const int mi = e / a.rank_pad;
-      const int j = e - mi * a.rank_pad;
-      float v = 0.0f;
-      if (j < a.rank) {
-        const float* pp = a.part_l + (int64_t)mi * lrow + j;
-        const int64_t stride = a.m * lrow;
-        for (int64_t g0 = 0; g0 < a.lgroups; g0 += 16) {  // 16 loads in flight, summed in order
-          float part[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) part[u] = g0 + u < a.lgroups ? ld_dev(pp + (g0 + u) * stride) : 0.0f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u) v += part[u];
-        }
-      }
-      tl[e] = (uint16_t)f32_to_bf16_rne(a.lora_scale * v);
-    }
-    __syncthreads();
-  }
-  if (wave != 0) return;
-
-  // wave 0 finishes the tile: acc[q] is C[n][m] with m = 16 q + r, n = tile*16 + 4 g + i
-  const float S = *a.tensor_scale;
-#pragma unroll
-  for (int q = 0; q < MT; ++q) acc[q] *= S;
-  if (a.rank > 0) {
-    const int rc = a.rank_pad / 32;
-#pragma unroll
-    for (int c = 0; c < kMaxRankChunks; ++c) {
-      if (c >= rc) break;
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int mi = 16 * q + r;
-        const bf16x8 tv = mi < mrows ? __builtin_bit_cast(bf16x8, *(const uint4*)(tl + mi * a.rank_pad + 32 * c + 8 * g))
-                                     : gv_zero8();
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bw[c]), tv, acc[q], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    const int64_t mi = 16 * q + r;
-    const int64_t nb = tile * 16 + 4 * g;
-    if (mi >= a.m || nb >= a.n) continue;
-    const f32x4 v = acc[q];
-    if (a.out_f32) {
-      float* y = (float*)a.y + mi * a.n;
-      if (nb + 4 <= a.n && (a.n & 3) == 0) {
-        *(f32x4*)(y + nb) = v;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (nb + i < a.n) y[nb + i] = v[i];
-      }
+    uint16_t* y = (uint16_t*)a.y + mi * a.n;
+    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    if (nb + 4 <= a.n && (a.n & 3) == 0) {
+      *(uint2*)(y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
     } else {
-      uint16_t* y = (uint16_t*)a.y + mi * a.n;
-      const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-      const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-      if (nb + 4 <= a.n && (a.n & 3) == 0) {
-        *(uint2*)(y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      } else {
-        if (nb + 0 < a.n) y[nb + 0] = (uint16_t)b0;
-        if (nb + 1 < a.n) y[nb + 1] = (uint16_t)b1;
-        if (nb + 2 < a.n) y[nb + 2] = (uint16_t)b2;
-        if (nb + 3 < a.n) y[nb + 3] = (uint16_t)b3;
-      }
-    }
-  }
-  if (a.rank > 0 && lane == 0) {  // this tile is done with the LoRA partials
-    const uint32_t done = __hip_atomic_fetch_add(a.fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (uint32_t)a.tiles_w - 1) {  // every tile has read the LoRA partials
-      st_dev_u32(a.cnt_l, 0u);
-      st_dev_u32(a.fin, 0u);
+      if (nb + 0 < a.n) y[nb + 0] = (uint16_t)b0;
+      if (nb + 1 < a.n) y[nb + 1] = (uint16_t)b1;
+      if (nb + 2 < a.n) y[nb + 2] = (uint16_t)b2;
+      if (nb + 3 < a.n) y[nb + 3] = (uint16_t)b3;
     }
   }
 }
@@ -448,34 +523,44 @@ static size_t g16_align(size_t b) { return (b + 255) & ~(size_t)255; }
 G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   G16Plan p;
   p.mt = m <= 16 ? 1 : 2;
-  p.tiles_w = g16_cdiv(n, 16);
   p.kchunks = g16_cdiv(k, kG16Chunk);
+  // K chunks whose activations fit the LDS budget (at least one for m <= 32)
+  int64_t cps_lds = ((int64_t)kG16XBytes / 2 / m - 8) / kG16Chunk;
+  if (cps_lds < 1) cps_lds = 1;
   p.tiles_l = rank > 0 ? g16_cdiv(rank, 16) : 0;
-  int64_t lc = ((int64_t)kG16XBytes / 2 / m - 8) / kG16Chunk;
-  lc = lc < 1 ? 1 : (lc > 8 ? 8 : lc);
-  p.lc = (int)lc;
-  p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, lc) : 0;
+  p.lc = (int)(cps_lds < kG16MaxLoraChunks ? cps_lds : kG16MaxLoraChunks);
+  p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   p.rank_pad = rank > 0 ? (int)(g16_cdiv(rank, 32) * 32) : 0;
-  const int64_t mrows = m;
-  // largest K range whose activations fit the LDS budget
-  int64_t cps_max = ((int64_t)kG16XBytes / 2 / mrows - 8) / kG16Chunk;
-  if (cps_max < 1) cps_max = 1;
-  int64_t splits = g16_cdiv(p.kchunks, cps_max);
-  // fill the chip: with few row tiles, split K (at most 16 ways)
-  while (p.tiles_w * splits < 512 && splits < kG16MaxSplits && splits < p.kchunks) ++splits;
-  p.cps = g16_cdiv(p.kchunks, splits);
-  p.splits = (int)g16_cdiv(p.kchunks, p.cps);
-  p.n_pad = g16_cdiv(n, 16) * 16;
+  const int64_t items_l = p.tiles_l * p.lgroups;
+  // Smallest K split with one batch of loads per wave; one row tile per workgroup if the
+  // grid then runs in one round, else two (halves the workgroups of a split).
+  for (int rt = 1; rt <= 2; ++rt) {
+    const int64_t batch_chunks = (int64_t)kG16Waves * (kG16Pairs / rt);
+    int64_t cps = cps_lds < batch_chunks ? cps_lds : batch_chunks;
+    int64_t splits = g16_cdiv(p.kchunks, cps);
+    cps = g16_cdiv(p.kchunks, splits);
+    splits = g16_cdiv(p.kchunks, cps);
+    p.rt = rt;
+    p.tiles_w = g16_cdiv(n, 16 * rt);
+    p.cps = cps;
+    p.splits = (int)splits;
+    if (items_l + p.tiles_w * splits <= (int64_t)kG16CUs * (p.mt == 1 ? 5 : 4)) break;
+  }
+  p.n_pad = p.tiles_w * 16 * p.rt;
   const int64_t xcols = (p.cps > p.lc ? p.cps : p.lc) * kG16Chunk;
   p.xstride = (int)(xcols + 8);
-  p.lds_bytes = (size_t)mrows * (size_t)p.xstride * 2;
-  const size_t t_bytes = (size_t)m * (size_t)p.rank_pad * 2;   // t is formed in the same LDS
-  if (p.lds_bytes < t_bytes) p.lds_bytes = t_bytes;
+  p.lds_bytes = (size_t)m * (size_t)p.xstride * 2;
+  const size_t red_bytes = (size_t)kG16Waves * p.rt * p.mt * kWave * 16;  // the wave reduction reuses it
+  if (p.lds_bytes < red_bytes) p.lds_bytes = red_bytes;
   return p;
 }
 
+static size_t g16_counter_bytes(const G16Plan& p) {
+  return g16_align((size_t)(p.tiles_w + 3 + kG16FinGroups) * kG16LineWords * 4);
+}
+
 size_t g16_workspace(const G16Plan& p, int64_t m) {
-  const size_t counters = g16_align((size_t)(p.tiles_w + 3) * 4);
+  const size_t counters = g16_counter_bytes(p);
   const size_t t = g16_align((size_t)m * (size_t)p.rank_pad * 2);
   const size_t pw = p.splits > 1 ? g16_align((size_t)p.splits * (size_t)m * (size_t)p.n_pad * 4) : 0;
   const size_t pl = g16_align((size_t)p.lgroups * (size_t)m * (size_t)(p.tiles_l * 16) * 4);
@@ -511,33 +596,36 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.n_pad = p.n_pad;
   a.xstride = p.xstride;
   char* w = (char*)ws;
-  uint32_t* cnt = (uint32_t*)w;
-  a.cnt_w = cnt;
-  a.cnt_l = cnt + p.tiles_w;
-  a.t_ready = a.cnt_l + 1;
-  a.fin = a.t_ready + 1;
-  size_t off = g16_align((size_t)(p.tiles_w + 3) * 4);
-  a.t = (uint16_t*)(w + off);
+  a.ctr = (uint32_t*)w;
+  size_t off = g16_counter_bytes(p);
+  a.t = (uint32_t*)(w + off);
   off += g16_align((size_t)m * (size_t)p.rank_pad * 2);
   a.part_w = (float*)(w + off);
   off += p.splits > 1 ? g16_align((size_t)p.splits * (size_t)m * (size_t)p.n_pad * 4) : 0;
   a.part_l = (float*)(w + off);
   const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.tiles_w * p.splits);
   const bool aligned = (k % kG16Chunk) == 0;
+  if (p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return hipErrorInvalidValue;  // plan invariant
   hipError_t e;
-  const bool multi = p.cps > 4 * kG16Batch;
-#define QL_G16_LAUNCH(MT, AL, MU)                                                              \
-  e = hipFuncSetAttribute((const void*)g16_kernel<MT, AL, MU>,                                 \
+#define QL_G16_LAUNCH(MT, RT, AL, XU)                                                          \
+  e = hipFuncSetAttribute((const void*)g16_kernel<MT, RT, AL, XU>,                             \
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);       \
   if (e != hipSuccess) return e;                                                               \
-  g16_kernel<MT, AL, MU><<<items, kG16Threads, p.lds_bytes, s>>>(a);
-#define QL_G16_LAUNCH_M(MT, AL) if (multi) { QL_G16_LAUNCH(MT, AL, true) } else { QL_G16_LAUNCH(MT, AL, false) }
+  g16_kernel<MT, RT, AL, XU><<<items, kG16Threads, p.lds_bytes, s>>>(a);
+#define QL_G16_LAUNCH_X(MT, RT, AL) \
+  if (m == 1) { QL_G16_LAUNCH(MT, RT, AL, kG16XUnits1) } else { QL_G16_LAUNCH(MT, RT, AL, kG16XUnits) }
+#define QL_G16_LAUNCH_A(MT, RT) if (aligned) { QL_G16_LAUNCH_X(MT, RT, true) } else { QL_G16_LAUNCH_X(MT, RT, false) }
   if (p.mt == 1) {
-    if (aligned) { QL_G16_LAUNCH_M(1, true) } else { QL_G16_LAUNCH_M(1, false) }
+    if (p.rt == 1) { QL_G16_LAUNCH_A(1, 1) } else { QL_G16_LAUNCH_A(1, 2) }
   } else {
-    if (aligned) { QL_G16_LAUNCH_M(2, true) } else { QL_G16_LAUNCH_M(2, false) }
+    if (p.rt == 1) {
+      if (aligned) { QL_G16_LAUNCH(2, 1, true, kG16XUnits) } else { QL_G16_LAUNCH(2, 1, false, kG16XUnits) }
+    } else {
+      if (aligned) { QL_G16_LAUNCH(2, 2, true, kG16XUnits) } else { QL_G16_LAUNCH(2, 2, false, kG16XUnits) }
+    }
   }
-#undef QL_G16_LAUNCH_M
+#undef QL_G16_LAUNCH_A
+#undef QL_G16_LAUNCH_X
 #undef QL_G16_LAUNCH
   return hipGetLastError();
 }

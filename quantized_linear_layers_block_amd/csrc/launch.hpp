@@ -71,7 +71,8 @@ uint16_t* lora_t_in_workspace(const SkinnyPlan& p, void* ws);
 // ---- NVFP4 layer for up to 32 tokens (gemv16.hip); workspace zero before first use
 struct G16Plan {
   int mt;             // m tiles of 16 (1 or 2)
-  int64_t tiles_w;    // weight row tiles of 16
+  int rt;             // row tiles of 16 per workgroup (1 or 2)
+  int64_t tiles_w;    // weight tiles of 16 * rt rows
   int64_t kchunks;    // 256-wide K chunks
   int64_t tiles_l;    // LoRA row tiles of 16
   int64_t lgroups;    // LoRA chunk groups
