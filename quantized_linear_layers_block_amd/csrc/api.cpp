@@ -21,7 +21,7 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest token counts served by the few-token (streaming) kernels.
-constexpr int64_t kG16MaxM = 32;
+constexpr int64_t kG16MaxM = 64;
 constexpr int64_t kSkinnyMaxM = 64;
 
 bool elems_ok(int64_t n, int64_t k) {

@@ -283,6 +283,32 @@ __device__ __forceinline__ i32x4 g16_b_frag_any(const G16Args& a, int64_t row, b
   return i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
 }
 
+// y[mi][nb .. nb+4) = v (bf16, round to nearest even, or float32), within N.
+__device__ __forceinline__ void g16_store(const G16Args& a, int64_t mi, int64_t nb, const f32x4& v) {
+  if (a.out_f32) {
+    float* y = (float*)a.y + mi * a.n;
+    if (nb + 4 <= a.n && (a.n & 3) == 0) {
+      *(f32x4*)(y + nb) = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nb + i < a.n) y[nb + i] = v[i];
+    }
+  } else {
+    uint16_t* y = (uint16_t*)a.y + mi * a.n;
+    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    if (nb + 4 <= a.n && (a.n & 3) == 0) {
+      *(uint2*)(y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    } else {
+      if (nb + 0 < a.n) y[nb + 0] = (uint16_t)b0;
+      if (nb + 1 < a.n) y[nb + 1] = (uint16_t)b1;
+      if (nb + 2 < a.n) y[nb + 2] = (uint16_t)b2;
+      if (nb + 3 < a.n) y[nb + 3] = (uint16_t)b3;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ LoRA item
 // 16 rows of A times chunks [c0, c1) of x (one chunk per wave).  The last item to finish
 // publishes t.
@@ -359,10 +385,207 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
   if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, g16_line_t(a)), 1u);
 }
 
+
+// ------------------------------------------------------------------ many-token weight item
+// 33 to 64 tokens: the activations of a whole K range no longer fit in LDS, so the
+// workgroup (64 RT rows: wave w owns rows 16 RT w .. +16 RT, all four 16-token tiles) runs
+// over its K chunks with the activations of two chunks in LDS (the one being multiplied and
+// the next) and those of the chunk after in registers, and the codes of each wave two
+// chunks ahead.  Every load is issued unconditionally (clamped past the range) so the
+// compiler waits for exactly the data each step needs.
+template <int RT, bool ALIGNED>
+__device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, int* flag, int64_t id) {
+  constexpr int MT = 4;
+  constexpr int XU = kG16Chunk / 8 * 16 * MT / kG16Threads;  // 8 activation units per thread
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t tile = id % a.tiles_w;
+  const int64_t split = id / a.tiles_w;
+  const int64_t c0 = split * a.cps, c1 = min(c0 + a.cps, a.kchunks);
+  const int64_t row0 = tile * 64 * RT + 16 * RT * wave;  // this wave's first row
+  const int xbuf = 16 * MT * a.xstride;                   // elements per LDS buffer
+
+  // x chunk c -> registers (units u = tid + 256 j: token u / 32, 8 columns at (u % 32) * 8)
+  auto x_issue = [&](int64_t c, i32x4 (&xr)[XU]) {
+    const int64_t cc = c < c1 ? c : c0;
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+      const int u = threadIdx.x + kG16Threads * j;
+      const int i = u >> 5;
+      const int64_t kk = cc * kG16Chunk + (u & 31) * 8;
+      const bool ok = i < a.m && kk < a.k;
+      const i32x4 v = *(const i32x4*)(ok ? a.x + (int64_t)i * a.k + kk : a.x);
+      if (!ALIGNED || 16 * MT > a.m) {  // zero tokens past m and columns past K
+        const int mk = (int)opaque_mask(ok);
+        xr[j] = i32x4{v[0] & mk, v[1] & mk, v[2] & mk, v[3] & mk};
+      } else {
+        xr[j] = v;
+      }
+    }
+  };
+  auto x_store = [&](int buf, const i32x4 (&xr)[XU]) {
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+      const int u = threadIdx.x + kG16Threads * j;
+      *(i32x4*)(xs + buf * xbuf + (u >> 5) * a.xstride + (u & 31) * 8) = xr[j];
+    }
+  };
+  auto c_issue = [&](int64_t c, G16Chunk (&cr)[RT]) {
+    const int64_t cc = c < c1 ? c : c0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t row = row0 + 16 * rt + r;
+      cr[rt] = g16_load<ALIGNED>(a, row, row < a.n, cc * kG16Chunk + 64 * g);
+    }
+  };
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[rt][q] = f32x4{0, 0, 0, 0};
+  auto compute = [&](int buf, const G16Chunk (&cr)[RT]) {
+    const uint16_t* xb = xs + buf * xbuf + r * a.xstride + 64 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bf16x8 xf[MT];
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        xf[q] = gv_zero8();
+        if (16 * q + r < a.m) xf[q] = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + 16 * q * a.xstride + 8 * t));
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const G16Chunk& c = cr[rt];
+        const uint32_t w = t == 0 ? c.c0.x : t == 1 ? c.c0.y : t == 2 ? c.c0.z : t == 3 ? c.c0.w :
+                           t == 4 ? c.c1.x : t == 5 ? c.c1.y : t == 6 ? c.c1.z : c.c1.w;
+        const bf16x8 av = gv_dequant8(w, e4m3_value((c.s >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+        for (int q = 0; q < MT; ++q)
+          acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xf[q], acc[rt][q], 0, 0, 0);
+      }
+    }
+  };
+
+  // LoRA B rows and S first, then the pipeline prologue
+  constexpr int kMaxB = 2;
+  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
+  i32x4 bw[RT][kMaxB];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t brow = row0 + 16 * rt + r;
+#pragma unroll
+    for (int c = 0; c < kMaxB; ++c) bw[rt][c] = g16_b_frag_vec(a, brow, early_b && brow < a.n, c);
+  }
+  const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  i32x4 xr0[XU], xr1[XU];
+  G16Chunk cs0[RT], cs1[RT];
+  x_issue(c0, xr0);
+  x_issue(c0 + 1, xr1);
+  c_issue(c0, cs0);
+  c_issue(c0 + 1, cs1);
+  x_store(0, xr0);
+  __syncthreads();
+  for (int64_t c = c0; c < c1; c += 2) {
+    // chunk c: LDS buffer 0, codes cs0; x(c+1) in flight in xr1
+    x_issue(c + 2, xr0);
+    compute(0, cs0);
+    c_issue(c + 2, cs0);
+    if (c + 1 < c1) x_store(1, xr1);
+    __syncthreads();
+    if (c + 1 >= c1) break;
+    // chunk c+1: LDS buffer 1, codes cs1; x(c+2) in flight in xr0
+    x_issue(c + 3, xr1);
+    compute(1, cs1);
+    c_issue(c + 3, cs1);
+    if (c + 2 < c1) x_store(0, xr0);
+    __syncthreads();
+  }
+
+  // tiles (rt, q): acc[rt][q] is C[n][m] with m = 16 q + r, n = row0 + 16 rt + 4 g + i
+  if (a.splits > 1) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mi = 16 * q + r;
+        if (mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g, acc[rt][q]);
+      }
+    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mi = 16 * q + r;
+        f32x4 sum = {0, 0, 0, 0};
+        for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {  // 8 partials in flight, added in split order
+          f32x4 part[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int sp = sp0 + u;
+            part[u] = (sp < a.splits && mi < a.m)
+                          ? (sp == split ? acc[rt][q]
+                                         : ld_dev4(a.part_w + ((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g))
+                          : f32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sum += part[u];
+        }
+        acc[rt][q] = sum;
+      }
+    if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, tile), 0u);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[rt][q] *= ts;
+  if (a.rank > 0) {
+    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
+      int it = 0;
+      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
+    }
+    __syncthreads();
+    const int rc = a.rank_pad / 32;
+#pragma unroll
+    for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
+      if (c >= rc) break;
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mi = 16 * q + r;
+        i32x4 tv = {0, 0, 0, 0};
+        if (mi < a.m) {
+          const uint32_t* tp = a.t + (mi * a.rank_pad + 32 * c + 8 * g) / 2;
+          tv = i32x4{(int)ld_dev_u32(tp), (int)ld_dev_u32(tp + 1), (int)ld_dev_u32(tp + 2), (int)ld_dev_u32(tp + 3)};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int64_t brow = row0 + 16 * rt + r;
+          const i32x4 b = early_b ? (c == 0 ? bw[rt][0] : bw[rt][1]) : g16_b_frag_any(a, brow, brow < a.n, c);
+          acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                               __builtin_bit_cast(bf16x8, tv), acc[rt][q], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave of this workgroup has read t
+    if (threadIdx.x == 0 && g16_fin(a, tile)) {
+      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
+      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+      const int64_t mi = 16 * q + r;
+      const int64_t nb = row0 + 16 * rt + 4 * g;
+      if (mi < a.m && nb < a.n) g16_store(a, mi, nb, acc[rt][q]);
+    }
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <int MT, int RT, bool ALIGNED, int XU>
-__global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALIGNED ? (MT == 1 ? 5 : 4) : 1))) void g16_kernel(G16Args a) {
+__global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALIGNED ? (MT == 1 ? 5 : MT == 2 ? 4 : 2) : 1))) void g16_kernel(G16Args a) {
   extern __shared__ __align__(16) uint16_t xs[];
   __shared__ int flag;
   const int lane = threadIdx.x & (kWave - 1);
@@ -377,6 +600,9 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   }
 
   // -------------------------------------------------------------------- weight item
+  if constexpr (MT == 4) {
+    g16_stream_item<RT, ALIGNED>(a, xs, &flag, id - items_l);
+  } else {
   id -= items_l;
   const int64_t tile = id % a.tiles_w;
   const int64_t split = id / a.tiles_w;
@@ -491,27 +717,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   }
   if (!tile_wave) return;
   if (mi >= a.m || nb >= a.n) return;
-  if (a.out_f32) {
-    float* y = (float*)a.y + mi * a.n;
-    if (nb + 4 <= a.n && (a.n & 3) == 0) {
-      *(f32x4*)(y + nb) = v;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (nb + i < a.n) y[nb + i] = v[i];
-    }
-  } else {
-    uint16_t* y = (uint16_t*)a.y + mi * a.n;
-    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-    if (nb + 4 <= a.n && (a.n & 3) == 0) {
-      *(uint2*)(y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    } else {
-      if (nb + 0 < a.n) y[nb + 0] = (uint16_t)b0;
-      if (nb + 1 < a.n) y[nb + 1] = (uint16_t)b1;
-      if (nb + 2 < a.n) y[nb + 2] = (uint16_t)b2;
-      if (nb + 3 < a.n) y[nb + 3] = (uint16_t)b3;
-    }
+  g16_store(a, mi, nb, v);
   }
 }
 
@@ -522,15 +728,33 @@ static size_t g16_align(size_t b) { return (b + 255) & ~(size_t)255; }
 
 G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   G16Plan p;
-  p.mt = m <= 16 ? 1 : 2;
   p.kchunks = g16_cdiv(k, kG16Chunk);
+  p.tiles_l = rank > 0 ? g16_cdiv(rank, 16) : 0;
+  p.rank_pad = rank > 0 ? (int)(g16_cdiv(rank, 32) * 32) : 0;
+  if (m > 32) {
+    // 33..64 tokens: 64-row workgroups running over their K chunks; split K only when there
+    // are too few row tiles to fill the chip
+    p.mt = 4;
+    p.rt = 1;
+    p.tiles_w = g16_cdiv(n, 64);
+    int64_t splits = g16_cdiv(224, p.tiles_w);
+    if (splits > p.kchunks) splits = p.kchunks;
+    if (splits < 1) splits = 1;
+    p.cps = g16_cdiv(p.kchunks, splits);
+    p.splits = (int)g16_cdiv(p.kchunks, p.cps);
+    p.lc = 1;
+    p.lgroups = rank > 0 ? p.kchunks : 0;
+    p.n_pad = p.tiles_w * 64;
+    p.xstride = kG16Chunk + 8;
+    p.lds_bytes = (size_t)2 * 64 * (size_t)p.xstride * 2;  // two chunks of 64 tokens
+    return p;
+  }
+  p.mt = m <= 16 ? 1 : 2;
   // K chunks whose activations fit the LDS budget (at least one for m <= 32)
   int64_t cps_lds = ((int64_t)kG16XBytes / 2 / m - 8) / kG16Chunk;
   if (cps_lds < 1) cps_lds = 1;
-  p.tiles_l = rank > 0 ? g16_cdiv(rank, 16) : 0;
   p.lc = (int)(cps_lds < kG16MaxLoraChunks ? cps_lds : kG16MaxLoraChunks);
   p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
-  p.rank_pad = rank > 0 ? (int)(g16_cdiv(rank, 32) * 32) : 0;
   const int64_t items_l = p.tiles_l * p.lgroups;
   // Smallest K split with one batch of loads per wave; one row tile per workgroup if the
   // grid then runs in one round, else two (halves the workgroups of a split).
@@ -605,7 +829,7 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.part_l = (float*)(w + off);
   const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.tiles_w * p.splits);
   const bool aligned = (k % kG16Chunk) == 0;
-  if (p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return hipErrorInvalidValue;  // plan invariant
+  if (p.mt < 4 && p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return hipErrorInvalidValue;  // plan invariant
   hipError_t e;
 #define QL_G16_LAUNCH(MT, RT, AL, XU)                                                          \
   e = hipFuncSetAttribute((const void*)g16_kernel<MT, RT, AL, XU>,                             \
@@ -617,12 +841,14 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
 #define QL_G16_LAUNCH_A(MT, RT) if (aligned) { QL_G16_LAUNCH_X(MT, RT, true) } else { QL_G16_LAUNCH_X(MT, RT, false) }
   if (p.mt == 1) {
     if (p.rt == 1) { QL_G16_LAUNCH_A(1, 1) } else { QL_G16_LAUNCH_A(1, 2) }
-  } else {
+  } else if (p.mt == 2) {
     if (p.rt == 1) {
       if (aligned) { QL_G16_LAUNCH(2, 1, true, kG16XUnits) } else { QL_G16_LAUNCH(2, 1, false, kG16XUnits) }
     } else {
       if (aligned) { QL_G16_LAUNCH(2, 2, true, kG16XUnits) } else { QL_G16_LAUNCH(2, 2, false, kG16XUnits) }
     }
+  } else {
+    if (aligned) { QL_G16_LAUNCH(4, 1, true, kG16XUnits) } else { QL_G16_LAUNCH(4, 1, false, kG16XUnits) }
   }
 #undef QL_G16_LAUNCH_A
 #undef QL_G16_LAUNCH_X
