@@ -10,8 +10,8 @@
 // operand (columns m): a lane's four accumulators then share one m and one 128-row
 // weight block, i.e. one scale per lane per K block.
 //
-// Tiling: 256 (n) x 256 (m) per workgroup of four waves (2 x 2), 128 x 128 per wave
-// (8 x 8 MFMA tiles), K step 128.  Operand tiles (32 KB each) are double-buffered in
+// Tiling: 256 (n) x 256 (m) per workgroup of eight waves (2 along n x 4 along m), 128 x 64
+// per wave (8 x 4 MFMA tiles, 128 float32 accumulators per lane), K step 128.  Operand tiles (32 KB each) are double-buffered in
 // LDS (128 KB) with a 16-byte XOR swizzle so that the 16 lanes reading one column of
 // 16 rows hit distinct banks; the next K block is fetched into registers while the
 // current one is multiplied.  Workgroup ids are remapped so that the tiles an XCD
@@ -21,7 +21,7 @@
 
 namespace ql {
 
-constexpr int kGThreads = 256;
+constexpr int kGThreads = 512;
 constexpr int kTile = 256;     // rows of n and of m per workgroup
 constexpr int kRowBytes = 128; // one K block of fp8 per LDS row
 
@@ -55,7 +55,11 @@ __device__ __forceinline__ void gemm_tile_coords(int64_t tiles_m, int64_t tiles_
   tn = in / gsize;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// 16-byte slot of logical chunk `chunk` in LDS row `row`.  A fragment read has 16 lanes
+// reading one chunk column of 16 consecutive rows; with 128-byte rows, rows r and r + 8
+// would share banks under a 64-bank LDS, so bit 3 of the row flips the slot as well.
+// Conflict-free for 8-lane / 32-bank and 16-lane / 64-bank service alike.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
 // Store a float4 of outputs for one m and four consecutive n.
 __device__ __forceinline__ void store4(void* y, int out_f32, int64_t n_total, int64_t m,
@@ -107,101 +111,165 @@ __device__ __forceinline__ f32x4 lora_tile(const uint16_t* __restrict__ lora_b,
   return c;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)p;
+}
+
+// 16 bytes per lane from global memory (uniform base + per-lane byte offset) straight
+// into LDS at m0 + 16 * lane (m0 uniform).  An LDS-DMA load needs one wait state after
+// the write of m0.
+__device__ __forceinline__ void lds_copy16(const uint8_t* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x8 frag_fp8(const uint8_t* tile, int row, int g) {
+  const uint8_t* p = tile + row * kRowBytes;
+  const i32x4 lo = *(const i32x4*)(p + swz(row, 2 * g) * 16);
+  const i32x4 hi = *(const i32x4*)(p + swz(row, 2 * g + 1) * 16);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 template <int OUT_F32>
-__global__ __launch_bounds__(kGThreads, 1) void gemm_fp8_kernel(Fp8GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* As = smem;                                  // [2][256][128] weights (rows n)
-  uint8_t* Bs = smem + 2 * kTile * kRowBytes;          // [2][256][128] activations (rows m)
-  float* Ss = (float*)(smem + 4 * kTile * kRowBytes);  // [2][256] sx of the tile's m rows
+__global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
+  constexpr int kStage = 2 * kTile * kRowBytes;
 
   int64_t tm, tn;
   gemm_tile_coords(a.tiles_m, a.tiles_n, tm, tn);
   const int64_t n0 = tn * kTile, m0 = tm * kTile;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wn = wave & 1, wm = wave >> 1;  // wave tile: n 128 wn .. +128, m 64 wm .. +64
   const int r = lane & 15, g = lane >> 4;
   const int64_t kblocks = a.k / 128;
 
-  // global -> register staging: 8 x 16 B per operand per thread (rows tid/8 + 32 i, chunk tid%8)
-  uint4 ga[8], gb[8];
-  float gs;
-  auto fetch = [&](int64_t kb) {
+  // Direct global -> LDS copies: one instruction of a wave fills 8 LDS rows (1 KB) with
+  // lane l writing row 8 (wave + 8 i) + l / 8, 16-byte slot l % 8.  The slot holds the
+  // row's logical chunk swz(row, l % 8) (the swizzle is an XOR, its own inverse), which the
+  // fragment reads undo.  Rows past the matrix edge copy the last row; their outputs are never stored.
+  // Offsets are relative to the tile's first row, so they fit 32 bits for k < 2^24.
+  uint32_t oa[4], ob[4];
+  const int64_t n_last = a.n - 1 - n0, m_last = a.m - 1 - m0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = tid / 8 + 32 * i;
-      const int ch = tid & 7;
-      const int64_t nr = n0 + row, mr = m0 + row;
-      ga[i] = nr < a.n ? *(const uint4*)(a.wq + nr * a.k + kb * 128 + ch * 16) : make_uint4(0, 0, 0, 0);
-      gb[i] = mr < a.m ? *(const uint4*)(a.xq + mr * a.k + kb * 128 + ch * 16) : make_uint4(0, 0, 0, 0);
-    }
-    const int64_t mr = m0 + tid;
-    gs = mr < a.m ? a.sx[mr * kblocks + kb] : 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * wave + 64 * i + (lane >> 3);
+    const uint32_t lc = (uint32_t)swz(row, lane & 7);
+    oa[i] = (uint32_t)(row < n_last ? row : n_last) * (uint32_t)a.k + lc * 16;
+    ob[i] = (uint32_t)(row < m_last ? row : m_last) * (uint32_t)a.k + lc * 16;
+  }
+  const uint8_t* wbase = a.wq + n0 * a.k;
+  const uint8_t* xbase = a.xq + m0 * a.k;
+  // Issued as inline assembly: the compiler would otherwise assume these LDS writes may
+  // alias the fragment reads of the other buffer and wait for them before every read.
+  // Completion is awaited explicitly (vmcnt 0) before the barrier that ends a K block.
+  // Copy q (0..7) of a K block: q < 4 weight rows 64 q.., q >= 4 activation rows.
+  auto dma = [&](int64_t kb, int buf, int q) {
+    const uint32_t lb = lds_addr(smem + buf * kStage) + 8 * wave * kRowBytes;
+    if (q < 4)
+      lds_copy16(wbase + kb * 128, oa[q], lb + 64 * q * kRowBytes);
+    else
+      lds_copy16(xbase + kb * 128, ob[q - 4], lb + (kTile + 64 * (q - 4)) * kRowBytes);
   };
-  auto stash = [&](int buf) {
+  // Activation scales of the lane's four m rows and the wave's weight-block scale, one K
+  // block ahead.
+  uint32_t osx[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = tid / 8 + 32 * i;
-      const int ch = swz(row, tid & 7);
-      *(uint4*)(As + (buf * kTile + row) * kRowBytes + ch * 16) = ga[i];
-      *(uint4*)(Bs + (buf * kTile + row) * kRowBytes + ch * 16) = gb[i];
-    }
-    Ss[buf * kTile + tid] = gs;
-  };
+  for (int j = 0; j < 4; ++j) {
+    const int64_t row = 64 * wm + 16 * j + r;
+    osx[j] = (uint32_t)((row < m_last ? row : m_last) * kblocks);
+  }
+  const float* sxbase = a.sx + m0 * kblocks;
+  const int64_t nblk = (n0 + 128 * wn) / 128;  // the wave's 128-row weight block
+  const bool nblk_ok = nblk * 128 < a.n;
+  const float* swp = a.sw + (nblk_ok ? nblk : 0) * kblocks;
+  const float swmask = nblk_ok ? 1.0f : 0.0f;
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  fetch(0);
-  stash(0);
+  float sxn[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma(0, 0, q);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j]];
+  float swn = swp[0];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  // Software pipeline.  The MFMAs of a K block run fragment by fragment (8 A fragments x
+  // 4 B fragments); each MFMA is issued right after the four FMAs that fold the product
+  // the same registers held one fragment earlier into its accumulators.  One MFMA and
+  // four FMAs per step lets the vector ALU work of one wave proceed while the other
+  // wave's MFMA runs (back-to-back MFMAs would hold the issue port instead).  Step 0 of
+  // fragment i reads fragment i + 1 from LDS; the next block's copies go out during
+  // fragments 0-3.  The block barrier sits before fragment 7, whose steps also load the
+  // next block's B fragments, so the next block starts without an LDS wait.  Products of
+  // fragment 7 are folded by fragment 0 of the next block with that block's scales
+  // (zero products before the first block).
   const f32x4 zero = {0, 0, 0, 0};
-  const int64_t nblk = (n0 + 128 * wn) / 128;  // this wave's 128-row weight block
+  f32x4 p[4] = {zero, zero, zero, zero};
+  float sc[4] = {0, 0, 0, 0}, sc_prev[4];
+  i32x8 bf[4], af, afn;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bf[j] = frag_fp8(smem + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
+  af = frag_fp8(smem, 128 * wn + r, g);
   for (int64_t kb = 0; kb < kblocks; ++kb) {
     const int buf = (int)(kb & 1);
-    if (kb + 1 < kblocks) fetch(kb + 1);
-    const float swv = nblk * 128 < a.n ? a.sw[nblk * kblocks + kb] : 0.0f;
-    // B fragments (activations) and combined scales for the wave's 8 m tiles
-    i32x8 bf[8];
-    float sc[8];
+    // The last block re-copies itself into the idle buffer, which nothing reads: the
+    // copies stay unconditional and the unrolled schedule below stays one basic block.
+    const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 128 * wm + 16 * j + r;
-      const uint8_t* p = Bs + (buf * kTile + row) * kRowBytes;
-      const uint4 lo = *(const uint4*)(p + swz(row, 2 * g) * 16);
-      const uint4 hi = *(const uint4*)(p + swz(row, 2 * g + 1) * 16);
-      i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      bf[j] = v;
-      sc[j] = Ss[buf * kTile + row] * swv;
+    for (int j = 0; j < 4; ++j) {
+      sc_prev[j] = sc[j];
+      sc[j] = sxn[j] * swn * swmask;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j] + kn];
+    swn = swp[kn];
+    const uint8_t* As = smem + buf * kStage;
+    const uint8_t* An = smem + (buf ^ 1) * kStage;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 128 * wn + 16 * i + r;
-      const uint8_t* p = As + (buf * kTile + row) * kRowBytes;
-      const uint4 lo = *(const uint4*)(p + swz(row, 2 * g) * 16);
-      const uint4 hi = *(const uint4*)(p + swz(row, 2 * g + 1) * 16);
-      i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 127, 0, 127);
-        acc[i][j] += sc[j] * pr;
+      if (i == 7) {
+        // this block's LDS reads are done and the next block's copies have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[7][j][e] += sc_prev[j] * p[j][e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i - 1][j][e] += sc[j] * p[j][e];
+        }
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 127, 0, 127);
+        if (j == 0) afn = i < 7 ? frag_fp8(As, 128 * wn + 16 * (i + 1) + r, g) : frag_fp8(An, 128 * wn + r, g);
+        if (i < 4 && (j == 1 || j == 2)) dma(kn, buf ^ 1, 2 * i + (j - 1));
+        if (i == 7) bf[j] = frag_fp8(An + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      af = afn;
     }
-    if (kb + 1 < kblocks) stash(buf ^ 1);
-    __syncthreads();
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
 
-  // Epilogue: lane holds m = m0 + 128 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
+  // Epilogue: lane holds m = m0 + 64 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t mrow = m0 + 128 * wm + 16 * j + r;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t mrow = m0 + 64 * wm + 16 * j + r;
       f32x4 v = acc[i][j];
       if (a.rank_pad > 0) {
         // MFMA tile: A operand rows n (B_lora), B operand columns m (t)
@@ -218,6 +286,9 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_
                            const uint8_t* wq, const float* sw, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,
                            hipStream_t s) {
+  // Copy offsets are 32-bit within a 256-row tile; k is a multiple of the 128 block.
+  if (k % 128 != 0 || k >= (int64_t(1) << 24)) return hipErrorInvalidValue;
+  if (m <= 0 || n <= 0) return hipSuccess;
   Fp8GemmArgs a;
   a.xq = xq;
   a.sx = sx;
@@ -233,7 +304,7 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_
   a.y = y;
   a.tiles_m = (m + kTile - 1) / kTile;
   a.tiles_n = (n + kTile - 1) / kTile;
-  const size_t lds = 4 * kTile * kRowBytes + 2 * kTile * sizeof(float);
+  const size_t lds = 4 * kTile * kRowBytes;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   if (out_f32) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
