@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16 (low half = a), round to nearest even, with gfx950's
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2v));
+}
+
 // |bf16| bit patterns of a packed pair, as two 16-bit unsigned lanes.
 __device__ __forceinline__ u16x2 abs_bits2(uint32_t v) {
   uint32_t a = v & 0x7FFF7FFFu;

@@ -24,6 +24,9 @@ namespace ql {
 constexpr int kGThreads = 512;
 constexpr int kTile = 256;     // rows of n and of m per workgroup
 constexpr int kRowBytes = 128; // one K block of fp8 per LDS row
+constexpr int kStagePitch = 272;                 // output staging: bytes per 128-column bf16 row
+constexpr int kStagePerWave = 64 * kStagePitch;  // 64 rows per wave
+constexpr size_t kFp8Lds = 8 * kStagePerWave;    // >= the two operand stages (128 KB)
 
 struct Fp8GemmArgs {
   const uint8_t* xq;
@@ -74,37 +77,48 @@ __device__ __forceinline__ void store4(void* y, int out_f32, int64_t n_total, in
     }
   } else {
     uint16_t* p = (uint16_t*)y + m * n_total + n;
-    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    const uint32_t lo = pack_bf16x2_rne(v[0], v[1]), hi = pack_bf16x2_rne(v[2], v[3]);
     if (n + 4 <= n_lim && (n_total & 3) == 0) {
-      *(uint2*)p = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      *(uint2*)p = make_uint2(lo, hi);
     } else {
-      const uint32_t b[4] = {b0, b1, b2, b3};
+      const uint32_t b[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
       for (int i = 0; i < 4; ++i)
         if (n + i < n_lim) p[i] = (uint16_t)b[i];
     }
   }
 }
 
-// LoRA up-projection for one 16 (n) x 16 (m) MFMA tile: C[n][m] += sum_j B[n][j] t[m][j].
+// LoRA up-projection for one 16 (n) x 16 (m) MFMA tile: C[n][m] += sum_j B[n][j] t[m][j],
+// with B = lora_b rows (MFMA A operand) and t rows (B operand, rank_pad columns, zero
+// padded).  VEC: rank % 8 == 0, so a lane's 8 consecutive rank entries are one aligned
+// 16-byte load (lora_b is 16-byte aligned) and are either all in range or all out.
+template <bool VEC>
 __device__ __forceinline__ f32x4 lora_tile(const uint16_t* __restrict__ lora_b,
                                            const uint16_t* __restrict__ t, int32_t rank,
                                            int32_t rank_pad, int64_t n_lim, int64_t m_lim,
                                            int64_t nrow, int64_t mrow, int g, f32x4 c) {
+  const int64_t nr = nrow < n_lim ? nrow : n_lim - 1;
+  const int64_t mr = mrow < m_lim ? mrow : m_lim - 1;
   for (int j0 = 0; j0 < rank_pad; j0 += 32) {
-    uint32_t bw[4], tw[4];
+    const int j = j0 + 8 * g;
+    i32x4 bi, ti;
+    if (VEC) {
+      const int jc = j < rank ? j : 0;
+      bi = *(const i32x4*)(lora_b + nr * rank + jc);
+      if (j >= rank) bi = i32x4{0, 0, 0, 0};
+      ti = *(const i32x4*)(t + mr * rank_pad + j);
+    } else {
+      uint32_t bw[4], tw[4];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int j = j0 + 8 * g + e;
-      const uint32_t b0 = (nrow < n_lim && j < rank) ? lora_b[nrow * rank + j] : 0u;
-      const uint32_t b1 = (nrow < n_lim && j + 1 < rank) ? lora_b[nrow * rank + j + 1] : 0u;
-      bw[e / 2] = b0 | (b1 << 16);
-      const uint32_t t0 = mrow < m_lim ? t[mrow * rank_pad + j] : 0u;
-      const uint32_t t1 = mrow < m_lim ? t[mrow * rank_pad + j + 1] : 0u;
-      tw[e / 2] = t0 | (t1 << 16);
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t b0 = j + e < rank ? lora_b[nr * rank + j + e] : 0u;
+        const uint32_t b1 = j + e + 1 < rank ? lora_b[nr * rank + j + e + 1] : 0u;
+        bw[e / 2] = b0 | (b1 << 16);
+        tw[e / 2] = (uint32_t)t[mr * rank_pad + j + e] | ((uint32_t)t[mr * rank_pad + j + e + 1] << 16);
+      }
+      bi = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
+      ti = i32x4{(int)tw[0], (int)tw[1], (int)tw[2], (int)tw[3]};
     }
-    i32x4 bi = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
-    i32x4 ti = {(int)tw[0], (int)tw[1], (int)tw[2], (int)tw[3]};
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bi),
                                                 __builtin_bit_cast(bf16x8, ti), c, 0, 0, 0);
   }
@@ -265,19 +279,49 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
 
   // Epilogue: lane holds m = m0 + 64 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
+  if (a.rank_pad > 0) {
+    const bool vec = (a.rank & 7) == 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t mrow = m0 + 64 * wm + 16 * j + r;
-      f32x4 v = acc[i][j];
-      if (a.rank_pad > 0) {
-        // MFMA tile: A operand rows n (B_lora), B operand columns m (t)
-        const int64_t nrow = n0 + 128 * wn + 16 * i + r;
-        f32x4 lz = lora_tile(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, zero);
-        v += lz;
+      for (int j = 0; j < 4; ++j) {
+        const int64_t mrow = m0 + 64 * wm + 16 * j + r;
+        const int64_t nrow = n0 + 128 * wn + 16 * i + r;  // A operand row of this lane
+        acc[i][j] = vec ? lora_tile<true>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j])
+                        : lora_tile<false>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j]);
       }
-      if (mrow < a.m) store4(a.y, OUT_F32, a.n, mrow, n0 + 128 * wn + 16 * i + 4 * g, v, a.n);
+    }
+  }
+  if (!OUT_F32 && m0 + kTile <= a.m && n0 + kTile <= a.n && (a.n & 7) == 0) {
+    // Interior bf16 tile: the wave's 64 (m) x 128 (n) block is transposed through LDS (row
+    // pitch 272 bytes keeps the 8-byte writes conflict-free) and leaves as whole 256-byte
+    // rows, four rows per store instruction.
+    __syncthreads();  // every wave is done with the operand buffers
+    uint8_t* stage = smem + wave * kStagePerWave;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = acc[i][j];
+        *(uint2*)(stage + (16 * j + r) * kStagePitch + (16 * i + 4 * g) * 2) =
+            make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    uint16_t* ybase = (uint16_t*)a.y + (m0 + 64 * wm) * a.n + n0 + 128 * wn + (lane & 15) * 8;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 4 * q + (lane >> 4);
+      *(i32x4*)(ybase + row * a.n) = *(const i32x4*)(stage + row * kStagePitch + (lane & 15) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t mrow = m0 + 64 * wm + 16 * j + r;
+        if (mrow < a.m) store4(a.y, OUT_F32, a.n, mrow, n0 + 128 * wn + 16 * i + 4 * g, acc[i][j], a.n);
+      }
     }
   }
 }
@@ -304,7 +348,8 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_
   a.y = y;
   a.tiles_m = (m + kTile - 1) / kTile;
   a.tiles_n = (n + kTile - 1) / kTile;
-  const size_t lds = 4 * kTile * kRowBytes;
+  const size_t lds = kFp8Lds;
+  static_assert(kFp8Lds >= 4 * kTile * kRowBytes, "staging must cover the operand buffers");
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   if (out_f32) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
