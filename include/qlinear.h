@@ -140,8 +140,11 @@ size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
  * x bf16 [m][k].  lora_a bf16 [rank][k], lora_b bf16 [n][rank]; rank == 0 or NULL
  * adapters mean no LoRA term.  y: bf16 [m][n] (QL_OUT_BF16, rounded to nearest even
  * from the float32 result) or f32 [m][n] (QL_OUT_F32).  Accumulation is float32.
- * NVFP4: the dequantized weights (E2M1 x E4M3 products, exact in bf16) meet the
- * bf16 activations in bf16 MFMA; S is applied in float32 after the K loop.
+ * NVFP4: the dequantized weights (E2M1 x E4M3 products, exact in bf16 and in f16)
+ * meet the activations in MFMA; S is applied in float32 after the K loop.  For m > 64
+ * and k % 64 == 0 the activations are first copied into the workspace as f16, each row
+ * scaled by a power of two that puts its largest magnitude in [2^14, 2^15) (exact but
+ * for magnitudes below about 2^-29 of the row maximum), and f16 MFMA is used.
  * FP8: x is quantized per 1x128 segment into the workspace, then an FP8 MFMA GEMM
  * rescales each 128-deep partial sum by sx * sw.
  * The LoRA intermediate s*t is rounded to bf16 before the up-projection.

@@ -145,6 +145,7 @@ size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k
       const SkinnyPlan p = ql::plan_skinny(m, n, k, rank);
       return up(ql::skinny_workspace(p, m, k));
     }
+    if (k % 64 == 0) return up(ql::gemm_nvfp4_f16_workspace(m, k, rank));
     return lora_ws(m, k, rank).total();
   }
   if (format == QL_FP8_BLOCK128) return fp8_act_bytes(m, k) + lora_ws(m, k, rank).total();
@@ -199,6 +200,9 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
       return hip_status(ql::launch_skinny_forward(p, x, m, w->n, w->k, codes, scales, w->tensor_scale,
                                                   lora_a, lora_b, r, lora_scale, y, out_f32, wsb, s));
     }
+    if (w->k % 64 == 0)
+      return hip_status(ql::launch_gemm_nvfp4_f16(x, m, w->n, w->k, codes, scales, w->tensor_scale,
+                                                  lora_a, lora_b, r, lora_scale, y, out_f32, wsb, s));
     const LoraWs lw = lora_ws(m, w->k, r);
     uint16_t* t = nullptr;
     if (r > 0) {

@@ -5,17 +5,27 @@
 // QeRL speeds up prefill as well as decoding with the NVFP4 weight path
 // (tldrocket.com QeRL page, paragraph after "Key Features of QeRL").  NVFP4's
 // E4M3-scaled 16-element blocks have no counterpart in gfx950's block-scaled MFMA
-// (power-of-two scales per 32 elements), but every E2M1 x E4M3 product is an exact
-// bf16, so weight tiles are dequantized exactly into LDS as bf16 and multiplied with
-// the bf16 activations by 16x16x32 bf16 MFMAs; S is applied in float32 after the K
-// loop and the LoRA up-projection (t = s.x.A^T rounded to bf16, computed beforehand)
-// is one more MFMA K chunk per 32 ranks.
+// (power-of-two scales per 32 elements), so weights are dequantized in registers and
+// multiplied by 16x16x32 f16 MFMAs; S is applied in float32 after the K loop and the
+// LoRA up-projection (t = s.x.A^T rounded to bf16, computed beforehand) is one more
+// bf16 MFMA K chunk per 32 ranks.
 //
-// Tiling: 256 (n) x 256 (m) per workgroup of four waves (2 x 2), 128 x 128 per wave,
-// K step 64 (two MFMAs per tile and step).  Each thread dequantizes one weight row's
-// 64 elements per step (32 bytes of codes, 4 block scales).  Both bf16 tiles (32 KB
-// each) are double-buffered in LDS with a 16-byte XOR swizzle.
+// Exact f16 dequantization: every E2M1 x E4M3 product is an f16 (at most 5 significant
+// bits, magnitude in [2^-10, 2688]).  The scaled fp4 conversion multiplies by the
+// exponent of its float scale only, so the codes are converted with scale 2^8 and then
+// multiplied (packed f16) by the E4M3 byte shifted left by 7, whose f16 reading is
+// exactly scale * 2^-8.  Activations are brought to f16 by a pre-pass that scales each
+// row by a power of two putting its largest magnitude in [2^14, 2^15): bf16's 8-bit
+// significands fit, so the conversion is exact except for values below about 2^-29 of
+// the row maximum, and the row factor is undone in float32 in the epilogue.
+//
+// Tiling (K % 64 == 0): 256 (n) x 256 (m) per workgroup of eight waves (4 along n x 2
+// along m), 64 x 128 per wave (4 x 8 MFMA tiles), K stage 64.  Each stage (activations
+// 32 KB, codes 8 KB, scales 1 KB) is copied straight into LDS; three stages are in
+// flight.  Other K take the generic kernel at the end of this file, which dequantizes
+// into LDS as bf16.
 #include "common.hpp"
+#include "gemm_common.hpp"
 #include "launch.hpp"
 
 namespace ql {
@@ -86,7 +96,7 @@ __device__ __forceinline__ void nv_store4(void* y, int out_f32, int64_t n_total,
 }
 
 template <int OUT_F32>
-__global__ __launch_bounds__(kNThreads, 1) void gemm_nvfp4_kernel(Nvfp4GemmArgs a) {
+__global__ __launch_bounds__(kNThreads, 1) void gemm_nvfp4_generic_kernel(Nvfp4GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* As = smem;                                 // [2][256][128 B] dequantized weights
   uint8_t* Bs = smem + 2 * kNTile * kNRowBytes;       // [2][256][128 B] activations
@@ -226,10 +236,419 @@ __global__ __launch_bounds__(kNThreads, 1) void gemm_nvfp4_kernel(Nvfp4GemmArgs 
   }
 }
 
+// ------------------------------------------------------------ f16 path (K % 64 == 0)
+
+constexpr int kQThreads = 512;
+constexpr int kQTile = 256;
+constexpr int kQK = 64;
+constexpr int kQStages = 3;
+constexpr int kQXBytes = kQTile * 128;       // activations: 256 rows x 64 f16
+constexpr int kQCBytes = kQTile * 32;        // codes: 256 rows x 32 bytes
+constexpr int kQSBytes = (kQTile + 32) * 4;  // scales: 256 rows x 4 bytes (+32 rows of overrun)
+constexpr int kQStage = kQXBytes + kQCBytes + kQSBytes;
+constexpr int kQPitch = 144;                 // output staging row: 64 bf16 + 16 bytes
+constexpr int kQStagePerWave = 128 * kQPitch;
+constexpr size_t kQLds = kQStages * kQStage > 8 * kQStagePerWave ? kQStages * kQStage : 8 * kQStagePerWave;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct Nvfp4F16Args {
+  const uint16_t* x16;  // f16 [m][k], row r scaled by 1 / rs[r]
+  const float* rs;      // [m] row factors (powers of two)
+  int64_t m, n, k;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  const uint16_t* t;
+  const uint16_t* lora_b;
+  int32_t rank, rank_pad;
+  void* y;
+  int64_t tiles_m, tiles_n;
+};
+
+// Activation pre-pass, in two kernels.
+//
+// nv_stats_kernel: workgroup (split, tile) covers rows 64 tile .. +64 (16 per wave) and
+// k in [kchunk split, kchunk (split + 1)).  It streams the rows in MFMA operand layout
+// (lane (r, g) holds row r, 8 consecutive k at 8 g of each 32-wide step), records each
+// row's largest bf16 magnitude (bit pattern) in amax_part[split][row] and, with RT > 0,
+// accumulates x A^T over RT 16-row tiles of A with bf16 MFMAs (A rows past the rank
+// read as zero) into t_part[split][row][16 RT].  Workgroups of one split are adjacent
+// so that they share the same range of A in L2.
+template <int RT>
+__global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
+                                                       const uint16_t* __restrict__ lora_a, int32_t rank,
+                                                       int64_t tiles, int64_t kchunk,
+                                                       uint32_t* __restrict__ amax_part,
+                                                       float* __restrict__ t_part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t split = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int64_t row = tile * 64 + 16 * wave + r;
+  const int64_t rowc = row < m ? row : m - 1;
+  const int64_t k0 = split * kchunk;
+  const int64_t k1 = k0 + kchunk < k ? k0 + kchunk : k;
+  const uint16_t* xr = x + rowc * k + 8 * g;
+  const uint16_t* ar[RT > 0 ? RT : 1];
+  bool aok[RT > 0 ? RT : 1];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int j = 16 * i + r;
+    aok[i] = j < rank;
+    ar[i] = lora_a + (int64_t)(aok[i] ? j : 0) * k + 8 * g;
+  }
+  f32x4 acc[RT > 0 ? RT : 1];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  uint32_t mx = 0;
+  auto step = [&](int64_t kk) {
+    const i32x4 xv = *(const i32x4*)(xr + kk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = (uint32_t)xv[e];
+      const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+      mx = mx > lo ? mx : lo;
+      mx = mx > hi ? mx : hi;
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      i32x4 av = *(const i32x4*)(ar[i] + kk);
+      if (!aok[i]) av = i32x4{0, 0, 0, 0};
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                       __builtin_bit_cast(bf16x8, xv), acc[i], 0, 0, 0);
+    }
+  };
+  int64_t kk = k0;
+  for (; kk + 96 < k1; kk += 128) {
+    step(kk);
+    step(kk + 32);
+    step(kk + 64);
+    step(kk + 96);
+  }
+  for (; kk < k1; kk += 32) step(kk);
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+  if (row < m) {
+    if (g == 0) amax_part[split * m + row] = mx;
+    // lane (r, g) of tile i holds rank 16 i + 4 g + (0..3) of row r
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      *(f32x4*)(t_part + (split * m + row) * (16 * RT) + 16 * i + 4 * g) = acc[i];
+  }
+}
+
+// nv_finish_kernel: one row per wave.  Row maximum over the splits -> e putting it in
+// [2^14, 2^15) (zero, Inf and NaN rows keep e = 0), rs[row] = 2^-e, the row as f16
+// scaled by 2^e, and t[row] = bf16(lora_scale * sum over splits of t_part) for ranks
+// below `rank`, zero up to rank_pad.
+__global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
+                                                        int64_t splits, const uint32_t* __restrict__ amax_part,
+                                                        const float* __restrict__ t_part, int32_t rank,
+                                                        int32_t rank_pad, float lora_scale,
+                                                        uint16_t* __restrict__ x16, float* __restrict__ rs,
+                                                        uint16_t* __restrict__ t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  uint32_t mx = 0;
+  for (int64_t sp = lane; sp < splits; sp += 64) mx = max(mx, amax_part[sp * m + row]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  const int be = (int)(mx >> 7);  // bf16 biased exponent of the row maximum
+  int e = (mx == 0 || be == 0xFF) ? 0 : 141 - (be > 0 ? be : 1);
+  e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  if (lane == 0) rs[row] = __uint_as_float((uint32_t)(127 - e) << 23);
+  for (int j = lane; j < rank_pad; j += 64) {
+    float sum = 0.0f;
+    for (int64_t sp = 0; sp < splits; ++sp) sum += t_part[(sp * m + row) * rank_pad + j];
+    t[row * rank_pad + j] = (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
+  }
+  const float up = __uint_as_float((uint32_t)(e + 127) << 23);
+  const uint4* src = (const uint4*)(x + row * k);
+  uint4* dst = (uint4*)(x16 + row * k);
+  const int64_t n8 = k / 8;
+  for (int64_t c = lane; c < n8; c += 64) {
+    const uint4 v = src[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float a0 = __uint_as_float(w[e2] << 16) * up, a1 = __uint_as_float(w[e2] & 0xFFFF0000u) * up;
+      o[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a0, a1}, f16x2));
+    }
+    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Eight weights (one codes dword, low nibble first) times their block scale, as f16.
+__device__ __forceinline__ f16x8 nv_dequant8_f16(uint32_t codes, uint32_t scale_byte) {
+  const uint32_t s = (scale_byte << 7) & 0x3F80u;  // f16 bits of scale * 2^-8
+  const f16x2 sp = __builtin_bit_cast(f16x2, s | (s << 16));
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sp;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sp;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sp;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sp;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int OUT_F32>
+__global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int64_t tm, tn;
+  gemm_tile_coords(a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t n0 = tn * kQTile, m0 = tm * kQTile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int wn = wave & 3, wm = wave >> 2;  // wave tile: n 64 wn .. +64, m 128 wm .. +128
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t kst = a.k / kQK;
+  const int64_t n_last = a.n - 1 - n0, m_last = a.m - 1 - m0;
+
+  // Copies of one stage, per wave: 4 x activations (8 rows of 128 bytes each, swizzled
+  // 16-byte slots), 1 x codes (32 rows of 32 bytes; the two halves of rows with bit 3
+  // set are swapped so that 16 lanes reading one half of 16 rows spread over all
+  // banks), 1 x scales (64 rows of 4 bytes from row 32 wave: neighbouring waves overlap
+  // by 32 rows with identical data, and the last one runs 32 rows into the padding).
+  // Rows past the matrix edge copy the last row; their outputs are never stored.
+  uint32_t xo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * (wave + 8 * q) + (lane >> 3);
+    xo[q] = (uint32_t)((row < m_last ? row : m_last) * a.k * 2 + swz(row, lane & 7) * 16);
+  }
+  uint32_t co, so;
+  {
+    const int row = 32 * wave + (lane >> 1);
+    co = (uint32_t)((row < n_last ? row : n_last) * (a.k / 2) + (((lane & 1) ^ ((row >> 3) & 1)) * 16));
+    const int srow = 32 * wave + lane;
+    so = (uint32_t)((srow < n_last ? srow : n_last) * (a.k / 16));
+  }
+  const uint8_t* xb = (const uint8_t*)(a.x16 + m0 * a.k);
+  const uint8_t* cb = a.codes + n0 * (a.k / 2);
+  const uint8_t* sb = a.scales + n0 * (a.k / 16);
+  auto dma = [&](int64_t st, int buf) {
+    const int64_t kk = st * kQK;
+    const uint32_t lb = lds_addr(smem) + buf * kQStage;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_copy16(xb + kk * 2, xo[q], lb + 8 * (wave + 8 * q) * 128);
+    lds_copy16(cb + kk / 2, co, lb + kQXBytes + wave * 1024);
+    lds_copy4(sb + kk / 16, so, lb + kQXBytes + kQCBytes + wave * 128);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  dma(0, 0);
+  dma(kst > 1 ? 1 : 0, 1);
+  int buf = 0;
+  for (int64_t st = 0; st < kst; ++st) {
+    // Stage st has landed once only the 6 copies of stage st + 1 are outstanding; after
+    // the barrier every wave is past stage st - 1, whose buffer takes stage st + 2.
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __syncthreads();
+    const int nbuf = buf == 0 ? 2 : buf - 1;
+    dma(st + 2 < kst ? st + 2 : kst - 1, nbuf);
+    const uint8_t* xs = smem + buf * kQStage;
+    const uint8_t* cs = xs + kQXBytes;
+    const uint8_t* ss = cs + kQCBytes;
+    uint32_t sd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sd[i] = *(const uint32_t*)(ss + (64 * wn + 16 * i + r) * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f16x8 bfr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 128 * wm + 16 * j + r;
+        bfr[j] = *(const f16x8*)(xs + row * 128 + swz(row, 4 * h + g) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wn + 16 * i + r;
+        const uint32_t cw = *(const uint32_t*)(cs + row * 32 + ((h ^ ((row >> 3) & 1)) * 16) + 4 * g);
+        const f16x8 af = nv_dequant8_f16(cw, (sd[i] >> (8 * (2 * h + (g >> 1)))) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: lane holds n = n0 + 64 wn + 16 i + 4 g + (0..3), m = m0 + 128 wm + 16 j + r.
+  const float S = *a.tensor_scale;
+  float fac[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t mr = m0 + 128 * wm + 16 * j + r;
+    fac[j] = S * a.rs[mr < a.m ? mr : a.m - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] *= fac[j];
+  if (a.rank_pad > 0) {
+    const bool vec = (a.rank & 7) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t mrow = m0 + 128 * wm + 16 * j + r;
+        const int64_t nrow = n0 + 64 * wn + 16 * i + r;  // A operand row of this lane
+        acc[i][j] = vec ? lora_tile<true>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j])
+                        : lora_tile<false>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j]);
+      }
+    }
+  }
+  if (!OUT_F32 && m0 + kQTile <= a.m && n0 + kQTile <= a.n && (a.n & 7) == 0) {
+    // Interior bf16 tile: the wave's 128 (m) x 64 (n) block is transposed through LDS (row
+    // pitch 144 bytes keeps the 8-byte writes conflict-free) and leaves as whole 128-byte
+    // rows, eight rows per store instruction.
+    __syncthreads();  // every wave is done with the operand buffers
+    uint8_t* stage = smem + wave * kQStagePerWave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = acc[i][j];
+        *(uint2*)(stage + (16 * j + r) * kQPitch + (16 * i + 4 * g) * 2) =
+            make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+    }
+    uint16_t* ybase = (uint16_t*)a.y + (m0 + 128 * wm) * a.n + n0 + 64 * wn + (lane & 7) * 8;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      *(i32x4*)(ybase + row * a.n) = *(const i32x4*)(stage + row * kQPitch + (lane & 7) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t mrow = m0 + 128 * wm + 16 * j + r;
+        if (mrow < a.m) store4(a.y, OUT_F32, a.n, mrow, n0 + 64 * wn + 16 * i + 4 * g, acc[i][j], a.n);
+      }
+    }
+  }
+}
+
+namespace {
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+int32_t nv_rank_pad(int32_t rank) { return rank > 0 ? (rank + 31) / 32 * 32 : 0; }
+
+// Pre-pass splits along K: about four (tile, split) workgroups per compute unit, so that
+// enough loads are in flight, with at least 256 k per split.
+int64_t nv_prep_splits(int64_t m, int64_t k) {
+  const int64_t tiles = (m + 63) / 64;
+  int64_t sp = (1024 + tiles - 1) / tiles;
+  const int64_t smax = k / 256 > 0 ? k / 256 : 1;
+  return sp < 1 ? 1 : (sp > smax ? smax : sp);
+}
+
+struct NvPrepWs {
+  uint16_t* x16;
+  float* rs;
+  uint16_t* t;
+  uint32_t* amax_part;
+  float* t_part;
+  size_t bytes;
+};
+
+NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t k, int32_t rank) {
+  const int64_t sp = nv_prep_splits(m, k);
+  const size_t rp = (size_t)nv_rank_pad(rank);
+  NvPrepWs w;
+  char* p = (char*)ws;
+  size_t off = 0;
+  w.x16 = (uint16_t*)(p + off);
+  off += up256((size_t)m * (size_t)k * 2);
+  w.rs = (float*)(p + off);
+  off += up256((size_t)m * 4);
+  w.t = (uint16_t*)(p + off);
+  off += up256((size_t)m * rp * 2);
+  w.amax_part = (uint32_t*)(p + off);
+  off += up256((size_t)sp * (size_t)m * 4);
+  w.t_part = (float*)(p + off);
+  off += up256((size_t)sp * (size_t)m * rp * 4);
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t k, int32_t rank) {
+  if (m <= 0 || k <= 0 || k % kQK != 0) return 0;
+  return nv_prep_ws(nullptr, m, k, rank).bytes;
+}
+
+hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scale, const uint16_t* lora_a,
+                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
+                                 int out_f32, void* ws, hipStream_t s) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  // Copy offsets are 32-bit within a 256-row tile.
+  if (k % kQK != 0 || k >= (int64_t(1) << 22) || !ws || rank < 0 || rank > 128)
+    return hipErrorInvalidValue;
+  const int32_t rank_pad = nv_rank_pad(rank);
+  const NvPrepWs w = nv_prep_ws(ws, m, k, rank);
+  const int64_t tiles = (m + 63) / 64, sp = nv_prep_splits(m, k);
+  const int64_t kchunk = ((k + sp - 1) / sp + 31) / 32 * 32;
+  const unsigned sgrid = (unsigned)(tiles * sp);
+  switch (rank_pad / 16) {
+    case 0: nv_stats_kernel<0><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    case 2: nv_stats_kernel<2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    case 4: nv_stats_kernel<4><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    case 6: nv_stats_kernel<6><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    case 8: nv_stats_kernel<8><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    default: return hipErrorInvalidValue;
+  }
+  nv_finish_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank, rank_pad,
+                                                            lora_scale, w.x16, w.rs, w.t);
+  uint16_t* x16 = w.x16;
+  float* rs = w.rs;
+  uint16_t* t = rank > 0 ? w.t : nullptr;
+  Nvfp4F16Args a;
+  a.x16 = x16;
+  a.rs = rs;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.codes = codes;
+  a.scales = scales;
+  a.tensor_scale = tensor_scale;
+  a.t = t;
+  a.lora_b = lora_b;
+  a.rank = rank;
+  a.rank_pad = rank_pad;
+  a.y = y;
+  a.tiles_m = (m + kQTile - 1) / kQTile;
+  a.tiles_n = (n + kQTile - 1) / kQTile;
+  const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
+  if (out_f32) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_f16_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQLds);
+    if (e != hipSuccess) return e;
+    gemm_nvfp4_f16_kernel<1><<<grid, kQThreads, kQLds, s>>>(a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_f16_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQLds);
+    if (e != hipSuccess) return e;
+    gemm_nvfp4_f16_kernel<0><<<grid, kQThreads, kQLds, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              const uint16_t* t, const uint16_t* lora_b, int32_t rank, void* y,
                              int out_f32, hipStream_t s) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  const int32_t rk = t ? rank : 0;
+  const int32_t rk_pad = t ? (rank + 31) / 32 * 32 : 0;
   Nvfp4GemmArgs a;
   a.x = x;
   a.m = m;
@@ -240,21 +659,21 @@ hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   a.tensor_scale = tensor_scale;
   a.t = t;
   a.lora_b = lora_b;
-  a.rank = t ? rank : 0;
-  a.rank_pad = t ? (rank + 31) / 32 * 32 : 0;
+  a.rank = rk;
+  a.rank_pad = rk_pad;
   a.y = y;
   a.tiles_m = (m + kNTile - 1) / kNTile;
   a.tiles_n = (n + kNTile - 1) / kNTile;
   const size_t lds = 4 * kNTile * kNRowBytes;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   if (out_f32) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_generic_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    gemm_nvfp4_kernel<1><<<grid, kNThreads, lds, s>>>(a);
+    gemm_nvfp4_generic_kernel<1><<<grid, kNThreads, lds, s>>>(a);
   } else {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_generic_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    gemm_nvfp4_kernel<0><<<grid, kNThreads, lds, s>>>(a);
+    gemm_nvfp4_generic_kernel<0><<<grid, kNThreads, lds, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -92,10 +92,19 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
                       float lora_scale, void* y, int out_f32, void* ws, hipStream_t s);
 
 // ---- large-M GEMMs (gemm_nvfp4.hip, gemm_fp8.hip)
+// Generic K (k % 16 == 0): t = bf16(s x A^T) computed beforehand, or null.
 hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              const uint16_t* t, const uint16_t* lora_b, int32_t rank, void* y,
                              int out_f32, hipStream_t s);
+// k % 64 == 0: f16 activations, row factors and the LoRA intermediate are formed in the
+// workspace (gemm_nvfp4_f16_workspace bytes) by a pre-pass.
+hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scale, const uint16_t* lora_a,
+                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
+                                 int out_f32, void* ws, hipStream_t s);
+size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t k, int32_t rank);
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_t n, int64_t k,
                            const uint8_t* wq, const float* sw, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,

@@ -34,7 +34,15 @@ def test_workspace_queries():
     assert b.qlinear_quantize_workspace(b.QL_NVFP4, 256, 512) == 4096
     assert b.qlinear_quantize_workspace(b.QL_FP8_BLOCK128, 256, 512) == 0
     assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 3584, 3584, 32) > 0
-    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 27648, 5120, 0) == 0
+    # NVFP4 prefill (k % 64 == 0) holds f16 activations (m*k*2 bytes), m row factors, the
+    # LoRA intermediate (m * rank rounded up to 32, bf16) and the pre-pass partials:
+    # per K split, m row maxima and m * rank_pad float32 LoRA sums (16 splits here)
+    m, k = 4096, 5120
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 0) == m * k * 2 + m * 4 + 16 * m * 4
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 40) == (
+        m * k * 2 + m * 4 + m * 64 * 2 + 16 * m * 4 + 16 * m * 64 * 4)
+    # other k take the kernel that reads bf16 activations directly
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 256, 5136, 0) == 0
     # FP8 forward holds the quantized activations (m*k bytes + scales)
     assert b.qlinear_forward_workspace(b.QL_FP8_BLOCK128, 8192, 4096, 14336, 0) >= 8192 * 14336
     assert b.qlinear_forward_workspace(b.QL_NVFP4, 0, 16, 16, 0) == 0
