@@ -145,7 +145,7 @@ size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k
       const SkinnyPlan p = ql::plan_skinny(m, n, k, rank);
       return up(ql::skinny_workspace(p, m, k));
     }
-    if (k % 64 == 0) return up(ql::gemm_nvfp4_f16_workspace(m, k, rank));
+    if (k % 64 == 0) return up(ql::gemm_nvfp4_f16_workspace(m, n, k, rank));
     return lora_ws(m, k, rank).total();
   }
   if (format == QL_FP8_BLOCK128) return fp8_act_bytes(m, k) + lora_ws(m, k, rank).total();

@@ -6,26 +6,66 @@
 
 namespace ql {
 
-// Workgroup id -> (tile along m, tile along n): XCD-contiguous, grouped by 8 along m.
-__device__ __forceinline__ void gemm_tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                                 int64_t& tn) {
-  const int64_t nb = (int64_t)gridDim.x;
-  int64_t id = blockIdx.x;
-  if (nb % 8 == 0) id = (id % 8) * (nb / 8) + id / 8;
+// Tile index -> (tile along m, tile along n), in groups of 8 tiles along m.
+__device__ __forceinline__ void gemm_group_tile(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                                int64_t& tn) {
   const int64_t group = 8;
   const int64_t per_group = group * tiles_n;
-  const int64_t g = id / per_group;
+  const int64_t g = t / per_group;
   const int64_t first_m = g * group;
   const int64_t gsize = tiles_m - first_m < group ? tiles_m - first_m : group;
-  const int64_t in = id % per_group;
+  const int64_t in = t % per_group;
   tm = first_m + in % gsize;
   tn = in / gsize;
 }
 
-// 16-byte slot of logical chunk `chunk` in LDS row `row`.  A fragment read has 16 lanes
-// reading one chunk column of 16 consecutive rows; with 128-byte rows, rows r and r + 8
-// would share banks under a 64-bank LDS, so bit 3 of the row flips the slot as well.
-// Conflict-free for 8-lane / 32-bank and 16-lane / 64-bank service alike.
+// Within a launch phase of n workgroups, consecutive indices go to one XCD (workgroups
+// are dealt to the 8 XCDs round-robin), so that the tiles one L2 serves are neighbours.
+__device__ __forceinline__ int64_t gemm_xcd_remap(int64_t b, int64_t n) {
+  return n % 8 == 0 ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
+// Workgroup id -> (tile along m, tile along n): XCD-contiguous, grouped by 8 along m.
+__device__ __forceinline__ void gemm_tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                                 int64_t& tn) {
+  gemm_group_tile(gemm_xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+}
+
+// Schedule with a split tail: the first `full` workgroups take whole tiles; the tiles
+// left over after the last full round are each split `tail_split` ways along K, so that
+// the final round fills the chip.  slot numbers the split workgroups (tile-major).
+struct GemmWork {
+  int64_t tm, tn;
+  int64_t slot;  // -1 for a whole tile
+  int split, nsplit;
+};
+__device__ __forceinline__ GemmWork gemm_schedule(int64_t tiles_m, int64_t tiles_n, int64_t full,
+                                                  int tail_split) {
+  GemmWork w;
+  const int64_t b = blockIdx.x;
+  int64_t t;
+  if (b < full) {
+    t = gemm_xcd_remap(b, full);
+    w.slot = -1;
+    w.split = 0;
+    w.nsplit = 1;
+  } else {
+    const int64_t id = gemm_xcd_remap(b - full, (int64_t)gridDim.x - full);
+    t = full + id / tail_split;
+    w.slot = id;
+    w.split = (int)(id % tail_split);
+    w.nsplit = tail_split;
+  }
+  gemm_group_tile(t, tiles_m, tiles_n, w.tm, w.tn);
+  return w;
+}
+
+// 16-byte slot of logical chunk `chunk` in LDS row `row` (128-byte rows, 8 slots).  A
+// fragment read has 16 lanes (fixed g) reading chunk 2 g or 2 g + 1 of 16 consecutive
+// rows.  With the row's low three bits alone, rows r and r + 8 collide; flipping the
+// slot with bit 3 as well makes this pattern conflict-free on gfx950 (measured with
+// the LDS bank-conflict counter; other chunk-per-lane patterns, e.g. chunk 4 h + g, do
+// conflict under this swizzle).
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 
 // Store a float4 of outputs for one m and four consecutive n.
@@ -52,41 +92,53 @@ __device__ __forceinline__ void store4(void* y, int out_f32, int64_t n_total, in
   }
 }
 
-// LoRA up-projection for one 16 (n) x 16 (m) MFMA tile: C[n][m] += sum_j B[n][j] t[m][j],
-// with B = lora_b rows (MFMA A operand) and t rows (B operand, rank_pad columns, zero
-// padded).  VEC: rank % 8 == 0, so a lane's 8 consecutive rank entries are one aligned
+// LoRA up-projection for a wave's NI x NJ grid of 16 (n) x 16 (m) output tiles:
+//   acc[i][j][n][m] += sum_q B[n][q] t[m][q],  n = nbase + 16 i + ..., m = mbase + 16 j + ...
+// with B = lora_b [n][rank] (MFMA A operand, rows clamped to n_lim) and t [m][rank_pad]
+// (B operand, zero padded to rank_pad, rows clamped to m_lim); lane (r, g) supplies
+// ranks q0 + 8 g .. + 7 of row r.  Per 32-rank chunk every fragment is loaded once and
+// all NI x NJ MFMAs follow.  With rank % 8 == 0 a lane's 8 ranks are one aligned
 // 16-byte load (lora_b is 16-byte aligned) and are either all in range or all out.
-template <bool VEC>
-__device__ __forceinline__ f32x4 lora_tile(const uint16_t* __restrict__ lora_b,
-                                           const uint16_t* __restrict__ t, int32_t rank,
-                                           int32_t rank_pad, int64_t n_lim, int64_t m_lim,
-                                           int64_t nrow, int64_t mrow, int g, f32x4 c) {
-  const int64_t nr = nrow < n_lim ? nrow : n_lim - 1;
-  const int64_t mr = mrow < m_lim ? mrow : m_lim - 1;
-  for (int j0 = 0; j0 < rank_pad; j0 += 32) {
-    const int j = j0 + 8 * g;
-    i32x4 bi, ti;
-    if (VEC) {
-      const int jc = j < rank ? j : 0;
-      bi = *(const i32x4*)(lora_b + nr * rank + jc);
-      if (j >= rank) bi = i32x4{0, 0, 0, 0};
-      ti = *(const i32x4*)(t + mr * rank_pad + j);
-    } else {
-      uint32_t bw[4], tw[4];
+template <int NI, int NJ>
+__device__ __forceinline__ void lora_wave(const uint16_t* __restrict__ lora_b, const uint16_t* __restrict__ t,
+                                          int32_t rank, int32_t rank_pad, int64_t n_lim, int64_t m_lim,
+                                          int64_t nbase, int64_t mbase, int r, int g,
+                                          f32x4 (&acc)[NI][NJ]) {
+  const bool vec = (rank & 7) == 0;
+  for (int q0 = 0; q0 < rank_pad; q0 += 32) {
+    const int q = q0 + 8 * g;
+    i32x4 af[NI], bfr[NJ];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t b0 = j + e < rank ? lora_b[nr * rank + j + e] : 0u;
-        const uint32_t b1 = j + e + 1 < rank ? lora_b[nr * rank + j + e + 1] : 0u;
-        bw[e / 2] = b0 | (b1 << 16);
-        tw[e / 2] = (uint32_t)t[mr * rank_pad + j + e] | ((uint32_t)t[mr * rank_pad + j + e + 1] << 16);
+    for (int i = 0; i < NI; ++i) {
+      const int64_t nr0 = nbase + 16 * i + r;
+      const int64_t nr = nr0 < n_lim ? nr0 : n_lim - 1;
+      if (vec) {
+        af[i] = *(const i32x4*)(lora_b + nr * rank + (q < rank ? q : 0));
+        if (q >= rank) af[i] = i32x4{0, 0, 0, 0};
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t b0 = q + e < rank ? lora_b[nr * rank + q + e] : 0u;
+          const uint32_t b1 = q + e + 1 < rank ? lora_b[nr * rank + q + e + 1] : 0u;
+          w[e / 2] = b0 | (b1 << 16);
+        }
+        af[i] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       }
-      bi = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
-      ti = i32x4{(int)tw[0], (int)tw[1], (int)tw[2], (int)tw[3]};
     }
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bi),
-                                                __builtin_bit_cast(bf16x8, ti), c, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t mr0 = mbase + 16 * j + r;
+      const int64_t mr = mr0 < m_lim ? mr0 : m_lim - 1;
+      bfr[j] = *(const i32x4*)(t + mr * rank_pad + q);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                            __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
   }
-  return c;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;

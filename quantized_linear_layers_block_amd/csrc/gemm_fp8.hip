@@ -182,19 +182,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
 
   // Epilogue: lane holds m = m0 + 64 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
-  if (a.rank_pad > 0) {
-    const bool vec = (a.rank & 7) == 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t mrow = m0 + 64 * wm + 16 * j + r;
-        const int64_t nrow = n0 + 128 * wn + 16 * i + r;  // A operand row of this lane
-        acc[i][j] = vec ? lora_tile<true>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j])
-                        : lora_tile<false>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j]);
-      }
-    }
-  }
+  if (a.rank_pad > 0)
+    lora_wave<8, 4>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, n0 + 128 * wn, m0 + 64 * wm, r, g, acc);
   if (!OUT_F32 && m0 + kTile <= a.m && n0 + kTile <= a.n && (a.n & 7) == 0) {
     // Interior bf16 tile: the wave's 64 (m) x 128 (n) block is transposed through LDS (row
     // pitch 272 bytes keeps the 8-byte writes conflict-free) and leaves as whole 256-byte

@@ -265,6 +265,9 @@ struct Nvfp4F16Args {
   int32_t rank, rank_pad;
   void* y;
   int64_t tiles_m, tiles_n;
+  int64_t full_tiles;  // workgroups that take whole tiles
+  int32_t tail_split;  // K splits of each remaining tile
+  float* part;         // [split workgroup][256 m][256 n] float32 partial tiles
 };
 
 // Activation pre-pass, in two kernels.
@@ -395,21 +398,23 @@ __device__ __forceinline__ f16x8 nv_dequant8_f16(uint32_t codes, uint32_t scale_
 template <int OUT_F32>
 __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int64_t tm, tn;
-  gemm_tile_coords(a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t n0 = tn * kQTile, m0 = tm * kQTile;
+  const GemmWork work = gemm_schedule(a.tiles_m, a.tiles_n, a.full_tiles, a.tail_split);
+  const int64_t n0 = work.tn * kQTile, m0 = work.tm * kQTile;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int wn = wave & 3, wm = wave >> 2;  // wave tile: n 64 wn .. +64, m 128 wm .. +128
   const int r = lane & 15, g = lane >> 4;
-  const int64_t kst = a.k / kQK;
+  // K stages [st0, st1) of this workgroup (all of K for a whole tile)
+  const int64_t kst_all = a.k / kQK;
+  const int64_t kper = (kst_all + work.nsplit - 1) / work.nsplit;
+  const int64_t st0 = work.split * kper;
+  const int64_t st1 = st0 + kper < kst_all ? st0 + kper : kst_all;
   const int64_t n_last = a.n - 1 - n0, m_last = a.m - 1 - m0;
 
   // Copies of one stage, per wave: 4 x activations (8 rows of 128 bytes each, swizzled
-  // 16-byte slots), 1 x codes (32 rows of 32 bytes; the two halves of rows with bit 3
-  // set are swapped so that 16 lanes reading one half of 16 rows spread over all
-  // banks), 1 x scales (64 rows of 4 bytes from row 32 wave: neighbouring waves overlap
-  // by 32 rows with identical data, and the last one runs 32 rows into the padding).
+  // 16-byte slots), 1 x codes (32 rows of 32 bytes), 1 x scales (64 rows of 4 bytes from
+  // row 32 wave: neighbouring waves overlap by 32 rows with identical data, and the last
+  // one runs 32 rows into the padding).
   // Rows past the matrix edge copy the last row; their outputs are never stored.
   uint32_t xo[4];
 #pragma unroll
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   uint32_t co, so;
   {
     const int row = 32 * wave + (lane >> 1);
-    co = (uint32_t)((row < n_last ? row : n_last) * (a.k / 2) + (((lane & 1) ^ ((row >> 3) & 1)) * 16));
+    co = (uint32_t)((row < n_last ? row : n_last) * (a.k / 2) + (lane & 1) * 16);
     const int srow = 32 * wave + lane;
     so = (uint32_t)((srow < n_last ? srow : n_last) * (a.k / 16));
   }
@@ -442,39 +447,70 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  dma(0, 0);
-  dma(kst > 1 ? 1 : 0, 1);
+  if (st1 > st0) {
+    dma(st0, 0);
+    dma(st0 + 1 < st1 ? st0 + 1 : st0, 1);
+  }
   int buf = 0;
-  for (int64_t st = 0; st < kst; ++st) {
+  for (int64_t st = st0; st < st1; ++st) {
     // Stage st has landed once only the 6 copies of stage st + 1 are outstanding; after
     // the barrier every wave is past stage st - 1, whose buffer takes stage st + 2.
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     __syncthreads();
     const int nbuf = buf == 0 ? 2 : buf - 1;
-    dma(st + 2 < kst ? st + 2 : kst - 1, nbuf);
+    dma(st + 2 < st1 ? st + 2 : st1 - 1, nbuf);
     const uint8_t* xs = smem + buf * kQStage;
     const uint8_t* cs = xs + kQXBytes;
     const uint8_t* ss = cs + kQCBytes;
-    uint32_t sd[4];
+    // K assignment inside a stage: MFMA step h, lane group g takes the 8 k of chunk
+    // 2 g + h (any assignment works as long as both operands use it).  A lane then reads
+    // activation chunks 2 g and 2 g + 1 of its rows (the conflict-free fragment pattern),
+    // both halves' codes as one 8-byte word at byte 8 g of the 32-byte code row, and one
+    // block scale (block g) for both steps.
+    // Software pipeline over the eight (step h, A fragment i) groups of the stage:
+    // group q = 4 h + i runs its eight MFMAs while the weights of group q + 1 are
+    // dequantized and, at the end of the first half, the B fragments of the second half
+    // are read.  All code and scale words of the stage are read up front.
+    uint32_t sb[4];
+    uint2 cw[4];
+    f16x8 bq[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sd[i] = *(const uint32_t*)(ss + (64 * wn + 16 * i + r) * 4);
+    for (int j = 0; j < 8; ++j) {
+      const int row = 128 * wm + 16 * j + r;
+      bq[0][j] = *(const f16x8*)(xs + row * 128 + swz(row, 2 * g) * 16);
+    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f16x8 bfr[8];
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wn + 16 * i + r;
+      sb[i] = (*(const uint32_t*)(ss + row * 4) >> (8 * g)) & 0xFFu;
+      cw[i] = *(const uint2*)(cs + row * 32 + 8 * g);
+    }
+    f16x8 af = nv_dequant8_f16(cw[0].x, sb[0]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int h = q >> 2, i = q & 3;
+      f16x8 an = af;
+      if (q < 7) {
+        const int h1 = (q + 1) >> 2, i1 = (q + 1) & 3;
+        an = nv_dequant8_f16(h1 ? cw[i1].y : cw[i1].x, sb[i1]);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int row = 128 * wm + 16 * j + r;
-        bfr[j] = *(const f16x8*)(xs + row * 128 + swz(row, 4 * h + g) * 16);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bq[h][j], acc[i][j], 0, 0, 0);
+        if (q == 3) {  // last use of the first half's fragment j: fetch the second half's
+          __builtin_amdgcn_sched_barrier(0);
+          const int row = 128 * wm + 16 * j + r;
+          bq[1][j] = *(const f16x8*)(xs + row * 128 + swz(row, 2 * g + 1) * 16);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wn + 16 * i + r;
-        const uint32_t cw = *(const uint32_t*)(cs + row * 32 + ((h ^ ((row >> 3) & 1)) * 16) + 4 * g);
-        const f16x8 af = nv_dequant8_f16(cw, (sd[i] >> (8 * (2 * h + (g >> 1)))) & 0xFFu);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ALU
+        if (q == 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
+      __builtin_amdgcn_sched_barrier(0);
+      af = an;
     }
     buf = buf == 2 ? 0 : buf + 1;
   }
@@ -492,18 +528,17 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] *= fac[j];
-  if (a.rank_pad > 0) {
-    const bool vec = (a.rank & 7) == 0;
+  if (a.rank_pad > 0 && work.split == 0)
+    lora_wave<4, 8>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g, acc);
+  if (work.slot >= 0) {
+    // split tile: scaled float32 partial (LoRA in split 0), summed by nv_tail_reduce_kernel
+    float* pt = a.part + work.slot * (kQTile * kQTile);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t mrow = m0 + 128 * wm + 16 * j + r;
-        const int64_t nrow = n0 + 64 * wn + 16 * i + r;  // A operand row of this lane
-        acc[i][j] = vec ? lora_tile<true>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j])
-                        : lora_tile<false>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, nrow, mrow, g, acc[i][j]);
-      }
-    }
+      for (int j = 0; j < 8; ++j)
+        *(f32x4*)(pt + (128 * wm + 16 * j + r) * kQTile + 64 * wn + 16 * i + 4 * g) = acc[i][j];
+    return;
   }
   if (!OUT_F32 && m0 + kQTile <= a.m && n0 + kQTile <= a.n && (a.n & 7) == 0) {
     // Interior bf16 tile: the wave's 128 (m) x 64 (n) block is transposed through LDS (row
@@ -538,6 +573,24 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   }
 }
 
+// Sum of the split partials of the tail tiles (fixed order), stored like the GEMM's
+// epilogue.  Workgroup: 4 rows of one tail tile, 4 consecutive n per thread.
+__global__ __launch_bounds__(256) void nv_tail_reduce_kernel(const float* __restrict__ part, int64_t tiles_m,
+                                                             int64_t tiles_n, int64_t full, int32_t splits,
+                                                             int64_t m, int64_t n, void* y, int out_f32) {
+  const int64_t tail = blockIdx.x / 64;
+  const int row = (int)(blockIdx.x % 64) * 4 + (int)(threadIdx.x >> 6);
+  const int col = (int)(threadIdx.x & 63) * 4;
+  int64_t tm, tn;
+  gemm_group_tile(full + tail, tiles_m, tiles_n, tm, tn);
+  const int64_t mr = tm * kQTile + row;
+  if (mr >= m) return;
+  const float* p = part + tail * splits * (kQTile * kQTile) + row * kQTile + col;
+  f32x4 v = *(const f32x4*)p;
+  for (int sp = 1; sp < splits; ++sp) v += *(const f32x4*)(p + sp * (kQTile * kQTile));
+  if (tn * kQTile + col < n) store4(y, out_f32, n, mr, tn * kQTile + col, v, n);
+}
+
 namespace {
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int32_t nv_rank_pad(int32_t rank) { return rank > 0 ? (rank + 31) / 32 * 32 : 0; }
@@ -551,18 +604,43 @@ int64_t nv_prep_splits(int64_t m, int64_t k) {
   return sp < 1 ? 1 : (sp > smax ? smax : sp);
 }
 
+// Whole-tile rounds on kQPlanCUs compute units, then the leftover tiles split along K
+// so that the last round fills the chip (only when at most half a round is left).
+constexpr int64_t kQPlanCUs = 256;
+struct NvTilePlan {
+  int64_t tiles_m, tiles_n, full;
+  int32_t split;
+  int64_t tail() const { return tiles_m * tiles_n - full; }
+};
+NvTilePlan nv_tile_plan(int64_t m, int64_t n, int64_t k) {
+  NvTilePlan p;
+  p.tiles_m = (m + kQTile - 1) / kQTile;
+  p.tiles_n = (n + kQTile - 1) / kQTile;
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  const int64_t rem = tiles % kQPlanCUs;
+  int64_t sp = rem > 0 && rem <= kQPlanCUs / 2 ? kQPlanCUs / rem : 1;
+  const int64_t kst = k / kQK;
+  if (sp > 16) sp = 16;
+  if (sp > kst) sp = kst;
+  p.split = (int32_t)(sp > 1 ? sp : 1);
+  p.full = p.split > 1 ? tiles - rem : tiles;
+  return p;
+}
+
 struct NvPrepWs {
   uint16_t* x16;
   float* rs;
   uint16_t* t;
   uint32_t* amax_part;
   float* t_part;
+  float* tile_part;
   size_t bytes;
 };
 
-NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t k, int32_t rank) {
+NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t n, int64_t k, int32_t rank) {
   const int64_t sp = nv_prep_splits(m, k);
   const size_t rp = (size_t)nv_rank_pad(rank);
+  const NvTilePlan tp = nv_tile_plan(m, n, k);
   NvPrepWs w;
   char* p = (char*)ws;
   size_t off = 0;
@@ -576,14 +654,16 @@ NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t k, int32_t rank) {
   off += up256((size_t)sp * (size_t)m * 4);
   w.t_part = (float*)(p + off);
   off += up256((size_t)sp * (size_t)m * rp * 4);
+  w.tile_part = (float*)(p + off);
+  if (tp.split > 1) off += (size_t)tp.tail() * (size_t)tp.split * kQTile * kQTile * 4;
   w.bytes = off;
   return w;
 }
 }  // namespace
 
-size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t k, int32_t rank) {
-  if (m <= 0 || k <= 0 || k % kQK != 0) return 0;
-  return nv_prep_ws(nullptr, m, k, rank).bytes;
+size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % kQK != 0) return 0;
+  return nv_prep_ws(nullptr, m, n, k, rank).bytes;
 }
 
 hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
@@ -596,7 +676,7 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
   if (k % kQK != 0 || k >= (int64_t(1) << 22) || !ws || rank < 0 || rank > 128)
     return hipErrorInvalidValue;
   const int32_t rank_pad = nv_rank_pad(rank);
-  const NvPrepWs w = nv_prep_ws(ws, m, k, rank);
+  const NvPrepWs w = nv_prep_ws(ws, m, n, k, rank);
   const int64_t tiles = (m + 63) / 64, sp = nv_prep_splits(m, k);
   const int64_t kchunk = ((k + sp - 1) / sp + 31) / 32 * 32;
   const unsigned sgrid = (unsigned)(tiles * sp);
@@ -627,9 +707,13 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
   a.rank = rank;
   a.rank_pad = rank_pad;
   a.y = y;
-  a.tiles_m = (m + kQTile - 1) / kQTile;
-  a.tiles_n = (n + kQTile - 1) / kQTile;
-  const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
+  const NvTilePlan tp = nv_tile_plan(m, n, k);
+  a.tiles_m = tp.tiles_m;
+  a.tiles_n = tp.tiles_n;
+  a.full_tiles = tp.full;
+  a.tail_split = tp.split;
+  a.part = w.tile_part;
+  const unsigned grid = (unsigned)(tp.full + (tp.split > 1 ? tp.tail() * tp.split : 0));
   if (out_f32) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_f16_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQLds);
     if (e != hipSuccess) return e;
@@ -639,6 +723,9 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
     if (e != hipSuccess) return e;
     gemm_nvfp4_f16_kernel<0><<<grid, kQThreads, kQLds, s>>>(a);
   }
+  if (tp.split > 1)
+    nv_tail_reduce_kernel<<<(unsigned)(tp.tail() * 64), 256, 0, s>>>(w.tile_part, tp.tiles_m, tp.tiles_n, tp.full,
+                                                                    tp.split, m, n, y, out_f32);
   return hipGetLastError();
 }
 

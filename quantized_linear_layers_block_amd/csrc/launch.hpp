@@ -104,7 +104,7 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
                                  const float* tensor_scale, const uint16_t* lora_a,
                                  const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
                                  int out_f32, void* ws, hipStream_t s);
-size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t k, int32_t rank);
+size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_t n, int64_t k,
                            const uint8_t* wq, const float* sw, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,
