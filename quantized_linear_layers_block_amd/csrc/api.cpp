@@ -22,7 +22,6 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest token counts served by the few-token (streaming) kernels.
 constexpr int64_t kG16MaxM = 64;
-constexpr int64_t kSkinnyMaxM = 64;
 
 bool elems_ok(int64_t n, int64_t k) {
   return n > 0 && k > 0 && n <= QLINEAR_MAX_ELEMS / k;
@@ -141,10 +140,6 @@ size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k
   if (m <= 0 || n <= 0 || k <= 0 || rank < 0) return 0;
   if (format == QL_NVFP4) {
     if (m <= kG16MaxM) return up(ql::g16_workspace(ql::plan_g16(m, n, k, rank), m));
-    if (m <= kSkinnyMaxM) {
-      const SkinnyPlan p = ql::plan_skinny(m, n, k, rank);
-      return up(ql::skinny_workspace(p, m, k));
-    }
     if (k % 64 == 0) return up(ql::gemm_nvfp4_f16_workspace(m, n, k, rank));
     return lora_ws(m, k, rank).total();
   }
@@ -194,11 +189,6 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
       const ql::G16Plan p = ql::plan_g16(m, w->n, w->k, r);
       return hip_status(ql::launch_g16(p, x, m, w->n, w->k, codes, scales, w->tensor_scale, lora_a,
                                        lora_b, r, lora_scale, y, out_f32, wsb, s));
-    }
-    if (m <= kSkinnyMaxM) {
-      const SkinnyPlan p = ql::plan_skinny(m, w->n, w->k, r);
-      return hip_status(ql::launch_skinny_forward(p, x, m, w->n, w->k, codes, scales, w->tensor_scale,
-                                                  lora_a, lora_b, r, lora_scale, y, out_f32, wsb, s));
     }
     if (w->k % 64 == 0)
       return hip_status(ql::launch_gemm_nvfp4_f16(x, m, w->n, w->k, codes, scales, w->tensor_scale,

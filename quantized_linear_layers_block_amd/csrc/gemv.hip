@@ -520,29 +520,6 @@ static hipError_t launch_gv_plan(const SkinnyPlan& p, GvArgs& a, char* ws, int64
   return launch_gv<4, 4, 1>(a, items, mrows_lds, s);
 }
 
-hipError_t launch_skinny_forward(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t n,
-                                 int64_t k, const uint8_t* codes, const uint8_t* scales,
-                                 const float* tensor_scale, const uint16_t* lora_a,
-                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
-                                 int out_f32, void* ws, hipStream_t s) {
-  GvArgs a = {};
-  a.x = x;
-  a.m = m;
-  a.k = k;
-  a.codes = codes;
-  a.scales = scales;
-  a.tensor_scale = tensor_scale;
-  a.lora_a = lora_a;
-  a.lora_b = lora_b;
-  a.rank = p.rows_l > 0 ? rank : 0;
-  a.lora_scale = lora_scale;
-  a.n = n;
-  a.y = y;
-  a.out_f32 = out_f32;
-  a.produce_y = 1;
-  return launch_gv_plan(p, a, (char*)ws, m, s);
-}
-
 hipError_t launch_lora_down(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
                             const uint16_t* lora_a, int32_t rank, float lora_scale, void* ws,
                             hipStream_t s) {

@@ -1,4 +1,4 @@
-// Few-token NVFP4 layer for up to 32 tokens on gfx950, one launch per call:
+// Few-token NVFP4 layer for up to 64 tokens on gfx950, one launch per call:
 //
 //   y = S . x . (E2M1 * E4M3)^T  +  bf16(s . x A^T) . B^T
 //
@@ -7,8 +7,8 @@
 // design is about keeping HBM busy from the first cycle and hiding every other latency
 // behind that stream.
 //
-// * A workgroup owns RT tiles of 16 weight rows (RT = 1 or 2) and a range of 256-wide K
-//   chunks; its four waves take the chunks in turn.  For each chunk a lane reads row
+// * Up to 32 tokens: a workgroup owns RT tiles of 16 weight rows (RT = 1 or 2) and a range
+//   of 256-wide K chunks; its four waves take the chunks in turn.  For each chunk a lane reads row
 //   (l % 16) of every row tile, K columns 64 (l / 16) .. +64 (32 bytes of codes and 4 block
 //   scales).  A wave issues up to four such (chunk, row tile) loads before using any.
 // * The activations of the workgroup's K range (at most 30 KB) are fetched into registers
@@ -18,6 +18,8 @@
 //   the codes dequantized in registers (E2M1 -> float by the hardware converter, times the
 //   E4M3 block scale in float32: exact, at most 6 significant bits, hence an exact bf16).
 //   The K order inside an MFMA is a permutation shared by both operands.
+// * 33 to 64 tokens (g16_stream_item): 64-row workgroups walk their K chunks with the
+//   activations double-buffered in LDS and the next chunk prefetched in registers.
 // * The four waves' tiles are added in LDS in a fixed order.  When the K range is split
 //   over several workgroups, the partial tiles go to the workspace with device-scope stores
 //   and the last arrival on the row tile's counter adds all of them in split order.

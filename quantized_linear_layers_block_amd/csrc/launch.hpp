@@ -55,20 +55,13 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int32_t rank);
 size_t skinny_workspace(const SkinnyPlan& p, int64_t m, int64_t k);
-// y = S x Wq^T + bf16(s x A^T) B^T in one launch (m <= 64).  ws must be zero before its
-// first use; the call leaves its counters zero.
-hipError_t launch_skinny_forward(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t n,
-                                 int64_t k, const uint8_t* codes, const uint8_t* scales,
-                                 const float* tensor_scale, const uint16_t* lora_a,
-                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
-                                 int out_f32, void* ws, hipStream_t s);
 // t = bf16(s x A^T) [m][rank_pad] into the workspace (plan from plan_skinny(m, 0, k, rank)).
 hipError_t launch_lora_down(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
                             const uint16_t* lora_a, int32_t rank, float lora_scale, void* ws,
                             hipStream_t s);
 uint16_t* lora_t_in_workspace(const SkinnyPlan& p, void* ws);
 
-// ---- NVFP4 layer for up to 32 tokens (gemv16.hip); workspace zero before first use
+// ---- NVFP4 layer for up to 64 tokens (gemv16.hip); workspace zero before first use
 struct G16Plan {
   int mt;             // m tiles of 16 (1 or 2)
   int rt;             // row tiles of 16 per workgroup (1 or 2)
