@@ -35,6 +35,29 @@ HBM_PEAK = 8.0e12          # B/s
 BF16_PEAK = 2.5e15         # dense MFMA flop/s
 FP8_PEAK = 5.0e15
 DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K, N)
+
+# HBM traffic of the decode layer kernel (g16_kernel) per launch, the mean over every
+# launch of the decode workload, from two counter runs over
+#   bench.py --rows none --no-cpu-baseline --steps 3 --warmup 1
+# under rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE.  Each counter is scaled by
+# what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
+# FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
+# was measured on (hash below); after any change to them it is reported as null.
+DECODE_TRAFFIC = {"bytes_per_launch": 31688783, "fetch_bytes": 27013487, "write_bytes": 4675296,
+                  "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
+                              "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
+                              "quantized_linear_layers_block_amd/csrc/common.hpp"],
+                  "sources_sha256": "c962ebb2d82209e1eea78df71e665a91926d04745760d9dfda6c01d5f1555668"}
+
+
+def decode_traffic():
+    """Measured bytes per launch if the decode kernel sources are those it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return DECODE_TRAFFIC["bytes_per_launch"] if h.hexdigest() == DECODE_TRAFFIC["sources_sha256"] else None
 DECODE_M = [1, 8, 64]
 RANK, LORA_S = 32, 2.0
 
@@ -55,7 +78,21 @@ def parse():
     ap.add_argument("--rows", default="all")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    """A plain copy of known size: what HBM counters read for it calibrates their units."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
 
 
 class Timer:
@@ -81,6 +118,9 @@ class Timer:
 
 def main():
     args = parse()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -199,7 +239,7 @@ def main():
                    "weight_copies_rotated": ncopy, "step_calls": len(order)},
         "roofline": {"bound": "hbm", "kernel": "qlinear_forward (NVFP4, M<=64)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": decode_traffic(),
                      "launches": launches, "mean_launch_us": round(kern_ms * 1e3, 3),
                      "bytes_per_launch_mean": round(tot_bytes / launches)},
         "decode_cases": cases,
