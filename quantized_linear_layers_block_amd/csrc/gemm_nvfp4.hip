@@ -21,9 +21,9 @@
 //
 // Tiling (K % 64 == 0): 256 (n) x 256 (m) per workgroup of eight waves (4 along n x 2
 // along m), 64 x 128 per wave (4 x 8 MFMA tiles), K stage 64.  Each stage (activations
-// 32 KB, codes 8 KB, scales 1 KB) is copied straight into LDS; three stages are in
-// flight.  Other K take the generic kernel at the end of this file, which dequantizes
-// into LDS as bf16.
+// 32 KB, codes 8 KB, scales 1 KB) is copied straight into LDS: activations three stages
+// deep, codes and scales six (they stream from HBM).  Other K take the generic kernel at
+// the end of this file, which dequantizes into LDS as bf16.
 #include "common.hpp"
 #include "gemm_common.hpp"
 #include "launch.hpp"
@@ -241,14 +241,16 @@ __global__ __launch_bounds__(kNThreads, 1) void gemm_nvfp4_generic_kernel(Nvfp4G
 constexpr int kQThreads = 512;
 constexpr int kQTile = 256;
 constexpr int kQK = 64;
-constexpr int kQStages = 3;
+constexpr int kQXSlots = 3;                  // activation ring: copies run 2 stages ahead
+constexpr int kQCSlots = 6;                  // code/scale ring: copies run 5 stages ahead
 constexpr int kQXBytes = kQTile * 128;       // activations: 256 rows x 64 f16
 constexpr int kQCBytes = kQTile * 32;        // codes: 256 rows x 32 bytes
 constexpr int kQSBytes = (kQTile + 32) * 4;  // scales: 256 rows x 4 bytes (+32 rows of overrun)
-constexpr int kQStage = kQXBytes + kQCBytes + kQSBytes;
+constexpr int kQCSBytes = kQCBytes + kQSBytes;
+constexpr int kQRingBytes = kQXSlots * kQXBytes + kQCSlots * kQCSBytes;
 constexpr int kQPitch = 144;                 // output staging row: 64 bf16 + 16 bytes
 constexpr int kQStagePerWave = 128 * kQPitch;
-constexpr size_t kQLds = kQStages * kQStage > 8 * kQStagePerWave ? kQStages * kQStage : 8 * kQStagePerWave;
+constexpr size_t kQLds = kQRingBytes > 8 * kQStagePerWave ? kQRingBytes : 8 * kQStagePerWave;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -363,16 +365,25 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
   e = e < -126 ? -126 : (e > 126 ? 126 : e);
   if (lane == 0) rs[row] = __uint_as_float((uint32_t)(127 - e) << 23);
   for (int j = lane; j < rank_pad; j += 64) {
-    float sum = 0.0f;
-    for (int64_t sp = 0; sp < splits; ++sp) sum += t_part[(sp * m + row) * rank_pad + j];
+    // fixed order: eight interleaved partial sums (split sp goes to sum sp % 8), then those
+    // eight in order; the loads of one round are independent so they overlap
+    float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += t_part[((sp + u) * m + row) * rank_pad + j];
+    }
+    for (int u = 0; sp < splits; ++sp, ++u) acc8[u] += t_part[(sp * m + row) * rank_pad + j];
+    float sum = acc8[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) sum += acc8[u];
     t[row * rank_pad + j] = (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
   }
   const float up = __uint_as_float((uint32_t)(e + 127) << 23);
   const uint4* src = (const uint4*)(x + row * k);
   uint4* dst = (uint4*)(x16 + row * k);
-  const int64_t n8 = k / 8;
-  for (int64_t c = lane; c < n8; c += 64) {
-    const uint4 v = src[c];
+  const int64_t n8 = k / 8;  // k % 64 == 0: a multiple of 8
+  auto conv = [&](const uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
 #pragma unroll
@@ -380,8 +391,17 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
       const float a0 = __uint_as_float(w[e2] << 16) * up, a1 = __uint_as_float(w[e2] & 0xFFFF0000u) * up;
       o[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a0, a1}, f16x2));
     }
-    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  int64_t c = lane;
+  for (; c + 192 < n8; c += 256) {  // four independent loads in flight per lane
+    const uint4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
+    dst[c] = conv(v0);
+    dst[c + 64] = conv(v1);
+    dst[c + 128] = conv(v2);
+    dst[c + 192] = conv(v3);
   }
+  for (; c < n8; c += 64) dst[c] = conv(src[c]);
 }
 
 // Eight weights (one codes dword, low nibble first) times their block scale, as f16.
@@ -432,14 +452,22 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   const uint8_t* xb = (const uint8_t*)(a.x16 + m0 * a.k);
   const uint8_t* cb = a.codes + n0 * (a.k / 2);
   const uint8_t* sb = a.scales + n0 * (a.k / 16);
-  auto dma = [&](int64_t st, int buf) {
+  // Copies of stage st into activation slot xb / code slot cb.  Activations are shared by
+  // every workgroup of an m tile (mostly L2 hits); codes stream from HBM once per m tile,
+  // so their ring is deeper.
+  auto dma_x = [&](int64_t st, int slot) {
     const int64_t kk = st * kQK;
-    const uint32_t lb = lds_addr(smem) + buf * kQStage;
+    const uint32_t lb = lds_addr(smem) + slot * kQXBytes;
 #pragma unroll
     for (int q = 0; q < 4; ++q) lds_copy16(xb + kk * 2, xo[q], lb + 8 * (wave + 8 * q) * 128);
-    lds_copy16(cb + kk / 2, co, lb + kQXBytes + wave * 1024);
-    lds_copy4(sb + kk / 16, so, lb + kQXBytes + kQCBytes + wave * 128);
   };
+  auto dma_c = [&](int64_t st, int slot) {
+    const int64_t kk = st * kQK;
+    const uint32_t lb = lds_addr(smem) + kQXSlots * kQXBytes + slot * kQCSBytes;
+    lds_copy16(cb + kk / 2, co, lb + wave * 1024);
+    lds_copy4(sb + kk / 16, so, lb + kQCBytes + wave * 128);
+  };
+  auto clamp_st = [&](int64_t st) { return st < st1 ? st : st1 - 1; };
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -447,72 +475,102 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  if (st1 > st0) {
-    dma(st0, 0);
-    dma(st0 + 1 < st1 ? st0 + 1 : st0, 1);
-  }
-  int buf = 0;
-  for (int64_t st = st0; st < st1; ++st) {
-    // Stage st has landed once only the 6 copies of stage st + 1 are outstanding; after
-    // the barrier every wave is past stage st - 1, whose buffer takes stage st + 2.
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    __syncthreads();
-    const int nbuf = buf == 0 ? 2 : buf - 1;
-    dma(st + 2 < st1 ? st + 2 : st1 - 1, nbuf);
-    const uint8_t* xs = smem + buf * kQStage;
-    const uint8_t* cs = xs + kQXBytes;
+  // K assignment inside a stage: MFMA step h, lane group g takes the 8 k of chunk 2 g + h
+  // (any assignment works as long as both operands use it).  A lane then reads activation
+  // chunks 2 g and 2 g + 1 of its rows (the conflict-free fragment pattern), both steps'
+  // codes as one 8-byte word at byte 8 g of the 32-byte code row, and one block scale
+  // (block g) for both steps.
+  //
+  // Software pipeline.  The eight (step h, A fragment i) groups of a stage run their
+  // eight MFMAs each while the weights of the next group are dequantized; the B fragments
+  // of the second step are read during group 3.  The stage barrier sits before group 7:
+  // by then every wave has read all it needs from the stage's buffer, so the buffer takes
+  // the copies of stage st + 3 (two stages of lead), and group 7 overlaps the reads of
+  // stage st + 1's codes, scales and first-step B fragments and the dequantization of its
+  // first group.  Stage s lives in buffer (s - st0) % 3.
+  uint32_t sbyte[4];
+  uint2 cw[4];
+  f16x8 bq[2][8];
+  f16x8 af;
+  auto read_stage_head = [&](int cslot) {
+    const uint8_t* cs = smem + kQXSlots * kQXBytes + cslot * kQCSBytes;
     const uint8_t* ss = cs + kQCBytes;
-    // K assignment inside a stage: MFMA step h, lane group g takes the 8 k of chunk
-    // 2 g + h (any assignment works as long as both operands use it).  A lane then reads
-    // activation chunks 2 g and 2 g + 1 of its rows (the conflict-free fragment pattern),
-    // both halves' codes as one 8-byte word at byte 8 g of the 32-byte code row, and one
-    // block scale (block g) for both steps.
-    // Software pipeline over the eight (step h, A fragment i) groups of the stage:
-    // group q = 4 h + i runs its eight MFMAs while the weights of group q + 1 are
-    // dequantized and, at the end of the first half, the B fragments of the second half
-    // are read.  All code and scale words of the stage are read up front.
-    uint32_t sb[4];
-    uint2 cw[4];
-    f16x8 bq[2][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 128 * wm + 16 * j + r;
-      bq[0][j] = *(const f16x8*)(xs + row * 128 + swz(row, 2 * g) * 16);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 64 * wn + 16 * i + r;
-      sb[i] = (*(const uint32_t*)(ss + row * 4) >> (8 * g)) & 0xFFu;
+      sbyte[i] = (*(const uint32_t*)(ss + row * 4) >> (8 * g)) & 0xFFu;
       cw[i] = *(const uint2*)(cs + row * 32 + 8 * g);
     }
-    f16x8 af = nv_dequant8_f16(cw[0].x, sb[0]);
+  };
+  // Issue order: codes of stages 0..2, then per stage s (virtually from s = -3) the
+  // activations of s + 3 and the codes of s + 6.  When stage st + 1 is needed (before
+  // group 7 of stage st) the only copies issued after its activations are the codes of
+  // st + 4 and the 6 copies of the last batch: vmcnt(8) leaves exactly those in flight.
+  if (st1 > st0) {
+    dma_c(st0, 0);
+    dma_c(clamp_st(st0 + 1), 1);
+    dma_c(clamp_st(st0 + 2), 2);
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      dma_x(clamp_st(st0 + v), v);
+      dma_c(clamp_st(st0 + 3 + v), 3 + v);
+    }
+    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");  // stage st0 has landed
+    __syncthreads();
+    read_stage_head(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 128 * wm + 16 * j + r;
+      bq[0][j] = *(const f16x8*)(smem + row * 128 + swz(row, 2 * g) * 16);
+    }
+    af = nv_dequant8_f16(cw[0].x, sbyte[0]);
+  }
+  int xslot = 0, cslot = 0;
+  for (int64_t st = st0; st < st1; ++st) {
+    const int xn_slot = xslot == kQXSlots - 1 ? 0 : xslot + 1;  // slots of stage st + 1
+    const int cn_slot = cslot == kQCSlots - 1 ? 0 : cslot + 1;
+    const uint8_t* xs = smem + xslot * kQXBytes;
+    const uint8_t* xn = smem + xn_slot * kQXBytes;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int h = q >> 2, i = q & 3;
+      if (q == 7) {
+        // stage st + 1 has landed; after the barrier no wave reads stage st's slots
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        dma_x(clamp_st(st + 3), xslot);
+        dma_c(clamp_st(st + 6), cslot);
+        read_stage_head(cn_slot);
+      }
       f16x8 an = af;
       if (q < 7) {
         const int h1 = (q + 1) >> 2, i1 = (q + 1) & 3;
-        an = nv_dequant8_f16(h1 ? cw[i1].y : cw[i1].x, sb[i1]);
+        an = nv_dequant8_f16(h1 ? cw[i1].y : cw[i1].x, sbyte[i1]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bq[h][j], acc[i][j], 0, 0, 0);
-        if (q == 3) {  // last use of the first half's fragment j: fetch the second half's
+        if (q == 3 || q == 7) {  // last use of fragment j of this step: fetch the next one
           __builtin_amdgcn_sched_barrier(0);
           const int row = 128 * wm + 16 * j + r;
-          bq[1][j] = *(const f16x8*)(xs + row * 128 + swz(row, 2 * g + 1) * 16);
+          if (q == 3)
+            bq[1][j] = *(const f16x8*)(xs + row * 128 + swz(row, 2 * g + 1) * 16);
+          else
+            bq[0][j] = *(const f16x8*)(xn + row * 128 + swz(row, 2 * g) * 16);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ALU
-        if (q == 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        if (q == 3 || q == 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
+      if (q == 7) an = nv_dequant8_f16(cw[0].x, sbyte[0]);  // next stage, group 0 (codes read at the barrier)
       __builtin_amdgcn_sched_barrier(0);
       af = an;
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    xslot = xn_slot;
+    cslot = cn_slot;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
