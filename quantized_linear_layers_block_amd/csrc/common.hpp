@@ -37,6 +37,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Eight E2M1 weights (one codes dword, low nibble first) times their E4M3 block scale, as
+// f16, exactly: the converter gives code * 256 (the power-of-two scale argument is applied
+// exactly), and (byte << 7) & 0x3F80 read as f16 is the E4M3 value times 2^-8 (same
+// mantissa, exponent rebased; E4M3 subnormals land on f16 subnormals).  The product has
+// at most 2 + 4 significant bits and lies in [2^-10, 2688], so the f16 multiply is exact.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, uint32_t scale_byte) {
+  const uint32_t s = (scale_byte << 7) & 0x3F80u;
+  const f16x2 sp = __builtin_bit_cast(f16x2, s | (s << 16));
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sp;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sp;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sp;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sp;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 // Two floats to packed bf16 (low half = a), round to nearest even, with gfx950's
 // v_cvt_pk_bf16_f32.

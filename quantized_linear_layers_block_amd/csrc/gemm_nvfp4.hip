@@ -252,9 +252,6 @@ constexpr int kQPitch = 144;                 // output staging row: 64 bf16 + 16
 constexpr int kQStagePerWave = 128 * kQPitch;
 constexpr size_t kQLds = kQRingBytes > 8 * kQStagePerWave ? kQRingBytes : 8 * kQStagePerWave;
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 struct Nvfp4F16Args {
   const uint16_t* x16;  // f16 [m][k], row r scaled by 1 / rs[r]
   const float* rs;      // [m] row factors (powers of two)
@@ -404,17 +401,6 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
   for (; c < n8; c += 64) dst[c] = conv(src[c]);
 }
 
-// Eight weights (one codes dword, low nibble first) times their block scale, as f16.
-__device__ __forceinline__ f16x8 nv_dequant8_f16(uint32_t codes, uint32_t scale_byte) {
-  const uint32_t s = (scale_byte << 7) & 0x3F80u;  // f16 bits of scale * 2^-8
-  const f16x2 sp = __builtin_bit_cast(f16x2, s | (s << 16));
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0) * sp;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1) * sp;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2) * sp;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3) * sp;
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 template <int OUT_F32>
 __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -523,7 +509,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
       const int row = 128 * wm + 16 * j + r;
       bq[0][j] = *(const f16x8*)(smem + row * 128 + swz(row, 2 * g) * 16);
     }
-    af = nv_dequant8_f16(cw[0].x, sbyte[0]);
+    af = dequant8_f16(cw[0].x, sbyte[0]);
   }
   int xslot = 0, cslot = 0;
   for (int64_t st = st0; st < st1; ++st) {
@@ -545,7 +531,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
       f16x8 an = af;
       if (q < 7) {
         const int h1 = (q + 1) >> 2, i1 = (q + 1) & 3;
-        an = nv_dequant8_f16(h1 ? cw[i1].y : cw[i1].x, sbyte[i1]);
+        an = dequant8_f16(h1 ? cw[i1].y : cw[i1].x, sbyte[i1]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -565,7 +551,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ALU
         if (q == 3 || q == 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
-      if (q == 7) an = nv_dequant8_f16(cw[0].x, sbyte[0]);  // next stage, group 0 (codes read at the barrier)
+      if (q == 7) an = dequant8_f16(cw[0].x, sbyte[0]);  // next stage, group 0 (codes read at the barrier)
       __builtin_amdgcn_sched_barrier(0);
       af = an;
     }

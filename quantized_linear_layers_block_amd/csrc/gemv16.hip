@@ -44,8 +44,9 @@ constexpr int kG16Pairs = 4;           // (chunk, row tile) code loads in flight
 constexpr int kG16XBytes = 30720;      // LDS for staged activations (5 workgroups per CU)
 constexpr int kG16XUnits = 8;          // 16-byte activation units per thread (8 * 256 * 16 >= 30720)
 constexpr int kG16XUnits1 = 2;         // the same for one token: 16 chunks of 32 units
-constexpr int kG16EarlyRank = 64;      // B rows of ranks up to 64 are fetched at the start
-constexpr int kG16MaxLoraChunks = 4;   // one chunk per wave
+constexpr int kG16EarlyRank = 64;      // B rows of ranks up to 64 are fetched at the start (64 tokens)
+constexpr int kG16EarlyRankFew = 32;   // the same for up to 32 tokens (one fragment: fewer registers)
+constexpr int kG16LoraGroups = 8;      // K groups of the LoRA partials (at most about)
 constexpr int kG16CUs = 256;           // workgroups that run at once: 5 per CU for one token tile, 4 for two
 
 struct G16Args {
@@ -67,7 +68,7 @@ struct G16Args {
   int64_t tiles_w;    // weight tiles of 16 * RT rows
   int64_t tiles_l;    // LoRA row tiles (16 rows of A)
   int64_t lgroups;    // LoRA chunk groups
-  int lc;             // chunks per LoRA item (at most four: one per wave)
+  int lc;             // chunks per LoRA item (a multiple of four: the waves take them in turn)
   int rank_pad;       // t row length (multiple of 32)
   int64_t n_pad;      // row length of the weight partials
   int xstride;        // LDS row stride of the activations (elements)
@@ -126,31 +127,46 @@ __device__ __forceinline__ uint4 ld16_or0(const void* p, bool ok, const void* du
   return mask4(v, opaque_mask(ok));
 }
 
+// One chunk (16 rows from `row0`, 256 K columns from `kl`) of a row tile.  The loads read
+// whole 64-byte runs per group of four lanes (lane l: row l / 4, chunk bytes 16 (l % 4) and
+// 64 + 16 (l % 4), scale bytes 4 (l % 4)), which streams markedly faster than lanes of one
+// quad reading four different rows; g16_transpose then moves the data into the MFMA operand
+// layout.  Rows past N and chunks past the range load from row 0 / column 0 and are masked
+// to zero.
 template <bool ALIGNED>
-__device__ __forceinline__ G16Chunk g16_load(const G16Args& a, int64_t row, bool ok, int64_t kl) {
+__device__ __forceinline__ G16Chunk g16_issue(const G16Args& a, int64_t row0, bool ok, int64_t kl) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int q = lane & 3;
+  const int64_t row = row0 + (lane >> 2);
+  ok = ok && row < a.n;
+  const int64_t rr = ok ? row : 0, kc = ok ? kl : 0;
+  const uint8_t* cp = a.codes + rr * (a.k / 2) + kc / 2 + 16 * q;
+  const uint8_t* sp = a.scales + rr * (a.k / 16) + kc / 16 + 4 * q;
   G16Chunk cr;
-  if (!ok) row = 0, kl = 0;
-  const uint8_t* cp = a.codes + row * (a.k / 2) + kl / 2;
-  const uint8_t* sp = a.scales + row * (a.k / 16) + kl / 16;
   if (ALIGNED) {  // K % 256 == 0: whole chunks, naturally aligned 16- and 4-byte loads
-    const uint4 c0 = *(const uint4*)cp, c1 = *(const uint4*)(cp + 16);
+    const uint4 c0 = *(const uint4*)cp, c1 = *(const uint4*)(cp + 64);
     const uint32_t sc = *(const uint32_t*)sp;
     const uint32_t m = opaque_mask(ok);
     cr.c0 = mask4(c0, m);
     cr.c1 = mask4(c1, m);
     cr.s = sc & m;
   } else {        // K % 16 == 0: whole 16-element blocks, 8-byte code loads, byte scales
+    // chunk byte 64 j + 16 q + 8 h holds block 8 j + 2 q + h; scale byte b is block 4 q + b
     uint32_t cw[8], sb[4];
 #pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool bok = ok && kl + 16 * (8 * j + 2 * q + h) < a.k;
+        const uint2 v = *(const uint2*)(cp + (bok ? 64 * j + 8 * h : 0));
+        const uint32_t m = opaque_mask(bok);
+        cw[4 * j + 2 * h] = v.x & m;
+        cw[4 * j + 2 * h + 1] = v.y & m;
+      }
+#pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const bool bok = ok && kl + 16 * b < a.k;
-      const int64_t off = bok ? 16 * b : 0;
-      const uint2 v = *(const uint2*)(cp + off / 2);
-      const uint32_t sv = sp[off / 16];
-      const uint32_t m = opaque_mask(bok);
-      cw[2 * b] = v.x & m;
-      cw[2 * b + 1] = v.y & m;
-      sb[b] = sv & m;
+      const bool bok = ok && kl + 16 * (4 * q + b) < a.k;
+      sb[b] = (uint32_t)sp[bok ? b : 0] & opaque_mask(bok);
     }
     cr.c0 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     cr.c1 = make_uint4(cw[4], cw[5], cw[6], cw[7]);
@@ -159,16 +175,36 @@ __device__ __forceinline__ G16Chunk g16_load(const G16Args& a, int64_t row, bool
   return cr;
 }
 
+// Loaded chunk -> MFMA layout.  Lane (r, g) takes from lane 4 r + g (row r, bytes 16 g and
+// 64 + 16 g): for K step t it then holds the 8 codes of row r at chunk columns
+// 128 (t / 4) + 32 g + 8 (t % 4) (g16_kcol), and in byte t / 2 of `s` their block scale
+// (blocks 2 g, 2 g + 1, 8 + 2 g, 9 + 2 g, from lanes 4 r + g / 2 and 4 r + 2 + g / 2).
+__device__ __forceinline__ int g16_kcol(int g, int t) { return 128 * (t >> 2) + 32 * g + 8 * (t & 3); }
+__device__ __forceinline__ G16Chunk g16_transpose(const G16Chunk& cr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, g = lane >> 4;
+  const int src = 4 * (4 * r + g);
+  auto bp = [](int addr, uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v); };
+  G16Chunk c;
+  c.c0 = make_uint4(bp(src, cr.c0.x), bp(src, cr.c0.y), bp(src, cr.c0.z), bp(src, cr.c0.w));
+  c.c1 = make_uint4(bp(src, cr.c1.x), bp(src, cr.c1.y), bp(src, cr.c1.z), bp(src, cr.c1.w));
+  const int sh = 16 * (g & 1);
+  const uint32_t lo = bp(4 * (4 * r + (g >> 1)), cr.s) >> sh;
+  const uint32_t hi = bp(4 * (4 * r + 2 + (g >> 1)), cr.s) >> sh;
+  c.s = (lo & 0xFFFFu) | (hi << 16);
+  return c;
+}
+
 // Activations x[0 .. mrows) x [c0*256, c1*256) in 16-byte units: thread i takes units
 // i + 256 j (j < XU).  They are issued into registers first, so that the code loads issued
 // after them do not delay the copy to LDS (memory operations complete in order).  Row i of
-// the copy starts at element i * xstride; xo is a unit's byte offset in LDS, or -1 for a unit
-// past the range.  With TAIL (K not
-// a multiple of 256) units past K are zeroed; K % 16 == 0 and units are 8-element aligned,
-// so a unit lies entirely inside or entirely past K.
+// the copy starts at element i * xstride (g16_x_off gives a unit's byte offset, or -1 for a
+// unit past the range).  With TAIL (K not a multiple of 256) units past K are zeroed;
+// K % 16 == 0 and units are 8-element aligned, so a unit lies entirely inside or entirely
+// past K.
 template <int XU, bool TAIL>
 __device__ __forceinline__ void g16_x_issue(const G16Args& a, int mrows, int64_t c0, int64_t c1,
-                                            i32x4 (&xv)[XU], int (&xo)[XU]) {
+                                            i32x4 (&xv)[XU]) {
   const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);
   const int units = mrows * per_row;
 #pragma unroll
@@ -184,15 +220,22 @@ __device__ __forceinline__ void g16_x_issue(const G16Args& a, int mrows, int64_t
     } else {
       xv[j] = v;
     }
-    xo[j] = u < units ? (i * a.xstride + (u - i * per_row) * 8) * 2 : -1;
   }
+}
+// LDS byte offset of unit u (row u / per_row, column 8 (u % per_row)), or -1 past the range.
+__device__ __forceinline__ int g16_x_off(const G16Args& a, int u, int per_row, int units) {
+  const int i = u / per_row;
+  return u < units ? (i * a.xstride + (u - i * per_row) * 8) * 2 : -1;
 }
 
 template <int XU>
-__device__ __forceinline__ void g16_x_store(uint16_t* xs, const i32x4 (&xv)[XU], const int (&xo)[XU]) {
+__device__ __forceinline__ void g16_x_store(const G16Args& a, uint16_t* xs, int per_row, int units,
+                                            const i32x4 (&xv)[XU]) {
 #pragma unroll
-  for (int j = 0; j < XU; ++j)
-    if (xo[j] >= 0) *(i32x4*)((char*)xs + xo[j]) = xv[j];
+  for (int j = 0; j < XU; ++j) {
+    const int xo = g16_x_off(a, threadIdx.x + kG16Threads * j, per_row, units);
+    if (xo >= 0) *(i32x4*)((char*)xs + xo) = xv[j];
+  }
 }
 
 // B operand: 8 activations of token 16 q + r at LDS column `col`.
@@ -209,14 +252,17 @@ template <int MT, int RT>
 __device__ __forceinline__ void g16_mul_chunk(const G16Args& a, const uint16_t* xs, int mrows,
                                               int col0, const G16Chunk (&cr)[RT], f32x4 (&acc)[RT][MT]) {
   const int g = (threadIdx.x & (kWave - 1)) >> 4;
+  G16Chunk ct[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) ct[rt] = g16_transpose(cr[rt]);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     bf16x8 xf[MT];
 #pragma unroll
-    for (int q = 0; q < MT; ++q) xf[q] = g16_xfrag(a, xs, mrows, q, col0 + 64 * g + 8 * t);
+    for (int q = 0; q < MT; ++q) xf[q] = g16_xfrag(a, xs, mrows, q, col0 + g16_kcol(g, t));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const G16Chunk& c = cr[rt];
+      const G16Chunk& c = ct[rt];
       const uint32_t w = t == 0 ? c.c0.x : t == 1 ? c.c0.y : t == 2 ? c.c0.z : t == 3 ? c.c0.w :
                          t == 4 ? c.c1.x : t == 5 ? c.c1.y : t == 6 ? c.c1.z : c.c1.w;
       const bf16x8 av = gv_dequant8(w, e4m3_value((c.s >> (8 * (t >> 1))) & 0xFFu));
@@ -312,43 +358,57 @@ __device__ __forceinline__ void g16_store(const G16Args& a, int64_t mi, int64_t 
 }
 
 // ------------------------------------------------------------------ LoRA item
-// 16 rows of A times chunks [c0, c1) of x (one chunk per wave).  The last item to finish
+// 16 rows of A times chunks [c0, c1) of x: wave w takes chunks c0 + w, c0 + w + 4, ... and
+// loads both MFMA operands straight from memory (each wave reads its own columns of x, so
+// staging them in LDS would save nothing).  The waves' tiles are added in LDS, the item's
+// partial is stored, and the last item to finish adds all partials in group order and
 // publishes t.
-template <int MT, int XU, bool TAIL>
+template <int MT, bool TAIL>
 __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, int* flag, int64_t id) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int mrows = (int)min((int64_t)16 * MT, a.m);
   const int64_t tile = id % a.tiles_l;
   const int64_t cg = id / a.tiles_l;
   const int64_t c0 = cg * a.lc, c1 = min(c0 + a.lc, a.kchunks);
-  const int64_t c = c0 + wave;
   const int64_t row = tile * 16 + r;
 
-  i32x4 xv[XU];
-  int xo[XU];
-  g16_x_issue<XU, TAIL>(a, mrows, c0, c1, xv, xo);
-  __builtin_amdgcn_sched_barrier(0);
-  uint4 av[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int64_t kk = c * kG16Chunk + 64 * g + 8 * t;
-    av[t] = ld16_or0(a.lora_a + row * a.k + kk, c < c1 && row < a.rank && kk < a.k, a.x);
-  }
-  g16_x_store<XU>(xs, xv, xo);
-  __syncthreads();
   f32x4 acc[1][MT];
 #pragma unroll
   for (int q = 0; q < MT; ++q) acc[0][q] = f32x4{0, 0, 0, 0};
-  if (c < c1) {
+  // rows past the rank or past the tokens read row 0 and are masked to zero
+  const uint16_t* abase = a.lora_a + (row < a.rank ? row : 0) * a.k + 64 * g;
+  const uint32_t amask = opaque_mask(row < a.rank);
+  const uint16_t* xbase[MT];
+  uint32_t xmask[MT];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    const int64_t mi = 16 * q + r;
+    xbase[q] = a.x + (mi < a.m ? mi : 0) * a.k + 64 * g;
+    xmask[q] = opaque_mask(mi < a.m);
+  }
+  for (int64_t c = c0 + wave; c < c1; c += kG16Waves) {
+    uint4 av[8], xv[8][MT];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t kk = c * kG16Chunk + 8 * t;  // column of lane group 0
+      if (TAIL) {  // K % 16 == 0: an 8-column unit is inside or past K
+        const bool kin = kk + 64 * g < a.k;
+        av[t] = ld16_or0(abase + kk, kin && row < a.rank, a.x);
+#pragma unroll
+        for (int q = 0; q < MT; ++q) xv[t][q] = ld16_or0(xbase[q] + kk, kin && 16 * q + r < a.m, a.x);
+      } else {
+        av[t] = mask4(*(const uint4*)(abase + kk), amask);
+#pragma unroll
+        for (int q = 0; q < MT; ++q) xv[t][q] = mask4(*(const uint4*)(xbase[q] + kk), xmask[q]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int q = 0; q < MT; ++q)
-        acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, av[t]),
-            g16_xfrag(a, xs, mrows, q, (int)(c - c0) * kG16Chunk + 64 * g + 8 * t), acc[0][q], 0, 0, 0);
+        acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[t]),
+                                                            __builtin_bit_cast(bf16x8, xv[t][q]), acc[0][q], 0, 0, 0);
   }
   const f32x4 v = g16_reduce<1, MT>(acc, xs);
   const int64_t lrow = a.tiles_l * 16;
@@ -358,29 +418,31 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
   }
   if (!g16_arrive(g16_ctr(a, g16_line_l(a)), (uint32_t)(a.tiles_l * a.lgroups), flag)) return;
 
-  // last LoRA item: t = bf16(s . (partials added in group order)), published once
-  const int rp2 = a.rank_pad / 2;
-  const int64_t stride = a.m * lrow;
-  for (int e = threadIdx.x; e < (int)a.m * rp2; e += kG16Threads) {
-    const int mi = e / rp2;
-    const int j = 2 * (e - mi * rp2);
-    const float* pp = a.part_l + (int64_t)mi * lrow + j;
-    float v0 = 0.0f, v1 = 0.0f;
-    for (int64_t g0 = 0; g0 < a.lgroups; g0 += 8) {  // 8 groups in flight, added in order
-      float p0[8], p1[8];
+  // last LoRA item: t = bf16(s . (partials added in group order)), published once.  A unit
+  // is four ranks of one token; all of its partials are loaded before any is added.
+  constexpr int kB = MT == 4 ? 16 : 8;  // partials in flight per unit
+  const int rp4 = a.rank_pad / 4;
+  const auto rs = dev_rsrc(a.part_l);
+  for (int u = threadIdx.x; u < (int)a.m * rp4; u += kG16Threads) {
+    const int mi = u / rp4;
+    const int j = 4 * (u - mi * rp4);
+    const bool in = j < lrow;
+    f32x4 sum = {0, 0, 0, 0};
+    for (int64_t g0 = 0; g0 < a.lgroups; g0 += kB) {
+      f32x4 pv[kB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = g0 + u < a.lgroups;
-        p0[u] = in && j < a.rank ? ld_dev(pp + (g0 + u) * stride) : 0.0f;
-        p1[u] = in && j + 1 < a.rank ? ld_dev(pp + (g0 + u) * stride + 1) : 0.0f;
+      for (int e = 0; e < kB; ++e) {
+        const int64_t gi = g0 + e < a.lgroups ? g0 + e : 0;
+        pv[e] = ld_dev4v(rs, (uint32_t)(((gi * a.m + mi) * lrow + (in ? j : 0)) * 4));
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        v0 += p0[u];
-        v1 += p1[u];
-      }
+      for (int e = 0; e < kB; ++e)
+        if (in && g0 + e < a.lgroups) sum += pv[e];
     }
-    st_dev_u32(a.t + e, f32_to_bf16_rne(a.lora_scale * v0) | (f32_to_bf16_rne(a.lora_scale * v1) << 16));
+    sum *= a.lora_scale;
+    uint32_t* tp = a.t + (mi * a.rank_pad + j) / 2;
+    st_dev_u32(tp, f32_to_bf16_rne(sum[0]) | (f32_to_bf16_rne(sum[1]) << 16));
+    st_dev_u32(tp + 1, f32_to_bf16_rne(sum[2]) | (f32_to_bf16_rne(sum[3]) << 16));
   }
   wait_stores();
   __syncthreads();
@@ -437,8 +499,7 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
     const int64_t cc = c < c1 ? c : c0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int64_t row = row0 + 16 * rt + r;
-      cr[rt] = g16_load<ALIGNED>(a, row, row < a.n, cc * kG16Chunk + 64 * g);
+      cr[rt] = g16_issue<ALIGNED>(a, row0 + 16 * rt, true, cc * kG16Chunk);
     }
   };
   f32x4 acc[RT][MT];
@@ -447,18 +508,21 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
 #pragma unroll
     for (int q = 0; q < MT; ++q) acc[rt][q] = f32x4{0, 0, 0, 0};
   auto compute = [&](int buf, const G16Chunk (&cr)[RT]) {
-    const uint16_t* xb = xs + buf * xbuf + r * a.xstride + 64 * g;
+    const uint16_t* xb = xs + buf * xbuf + r * a.xstride;
+    G16Chunk ct[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ct[rt] = g16_transpose(cr[rt]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       bf16x8 xf[MT];
 #pragma unroll
       for (int q = 0; q < MT; ++q) {
         xf[q] = gv_zero8();
-        if (16 * q + r < a.m) xf[q] = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + 16 * q * a.xstride + 8 * t));
+        if (16 * q + r < a.m) xf[q] = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + 16 * q * a.xstride + g16_kcol(g, t)));
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const G16Chunk& c = cr[rt];
+        const G16Chunk& c = ct[rt];
         const uint32_t w = t == 0 ? c.c0.x : t == 1 ? c.c0.y : t == 2 ? c.c0.z : t == 3 ? c.c0.w :
                            t == 4 ? c.c1.x : t == 5 ? c.c1.y : t == 6 ? c.c1.z : c.c1.w;
         const bf16x8 av = gv_dequant8(w, e4m3_value((c.s >> (8 * (t >> 1))) & 0xFFu));
@@ -514,27 +578,33 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
         if (mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g, acc[rt][q]);
       }
     if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
+    // the partials of all MT token tiles in flight together (4 splits each at a time),
+    // added in split order
+    const auto rs = dev_rsrc(a.part_w);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 sum[MT];
 #pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        f32x4 sum = {0, 0, 0, 0};
-        for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {  // 8 partials in flight, added in split order
-          f32x4 part[8];
+      for (int q = 0; q < MT; ++q) sum[q] = f32x4{0, 0, 0, 0};
+      for (int sp0 = 0; sp0 < a.splits; sp0 += 4) {
+        f32x4 part[4][MT];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int sp = sp0 + u;
-            part[u] = (sp < a.splits && mi < a.m)
-                          ? (sp == split ? acc[rt][q]
-                                         : ld_dev4(a.part_w + ((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g))
-                          : f32x4{0, 0, 0, 0};
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < MT; ++q) {
+            const int sp = sp0 + u < a.splits ? sp0 + u : 0;
+            const int64_t mi = min((int64_t)(16 * q + r), a.m - 1);
+            part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) sum += part[u];
-        }
-        acc[rt][q] = sum;
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < MT; ++q)
+            if (sp0 + u < a.splits) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
       }
+#pragma unroll
+      for (int q = 0; q < MT; ++q) acc[rt][q] = sum[q];
+    }
     if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, tile), 0u);
   }
 #pragma unroll
@@ -597,7 +667,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   const int64_t items_l = a.tiles_l * a.lgroups;
   int64_t id = blockIdx.x;
   if (id < items_l) {
-    g16_lora_item<MT, XU, !ALIGNED>(a, xs, &flag, id);
+    g16_lora_item<MT, !ALIGNED>(a, xs, &flag, id);
     return;
   }
 
@@ -613,8 +683,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   constexpr int kCB = kG16Pairs / RT;  // chunks per wave batch
 
   i32x4 xv[XU];
-  int xo[XU];
-  g16_x_issue<XU, !ALIGNED>(a, mrows, c0, c1, xv, xo);
+  g16_x_issue<XU, !ALIGNED>(a, mrows, c0, c1, xv);
   __builtin_amdgcn_sched_barrier(0);
 
   // waves w < RT*MT finish output tile (w / MT, w % MT); their B rows do not depend on
@@ -622,32 +691,29 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   const bool tile_wave = wave < RT * MT;
   const int rt_e = tile_wave ? wave / MT : 0, q_e = tile_wave ? wave % MT : 0;
   const int64_t brow = row0 + 16 * rt_e + r;
-  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
+  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRankFew && (a.rank & 7) == 0;
   const i32x4 bw0 = g16_b_frag_vec(a, brow, early_b && tile_wave && brow < a.n, 0);
-  const i32x4 bw1 = g16_b_frag_vec(a, brow, early_b && tile_wave && brow < a.n, 1);
   const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_sched_barrier(0);
 
-  // code loads: some before the activations are copied to LDS (that copy waits for the
-  // activations only), the rest after, which keeps fewer registers live at once
-  constexpr int kEarly = XU > 4 ? 1 : kG16Pairs / 2;
+  // every code load is issued before the activations are copied to LDS: that copy waits
+  // for the activations only (issued first), and the codes arrive while it runs
+  constexpr int kEarly = XU > 4 ? (RT == 1 ? 2 : 1) : kG16Pairs;
   G16Chunk ca[kCB][RT];
 #pragma unroll
   for (int p = 0; p < kEarly; ++p) {
     const int i = p / RT, rt = p % RT;
     const int64_t c = c0 + wave + kG16Waves * i;
-    const int64_t row = row0 + 16 * rt + r;
-    ca[i][rt] = g16_load<ALIGNED>(a, row, row < a.n && c < c1, c * kG16Chunk + 64 * g);
+    ca[i][rt] = g16_issue<ALIGNED>(a, row0 + 16 * rt, c < c1, c * kG16Chunk);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  g16_x_store<XU>(xs, xv, xo);
+  const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);
+  g16_x_store<XU>(a, xs, per_row, mrows * per_row, xv);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int p = kEarly; p < kG16Pairs; ++p) {
     const int i = p / RT, rt = p % RT;
     const int64_t c = c0 + wave + kG16Waves * i;
-    const int64_t row = row0 + 16 * rt + r;
-    ca[i][rt] = g16_load<ALIGNED>(a, row, row < a.n && c < c1, c * kG16Chunk + 64 * g);
+    ca[i][rt] = g16_issue<ALIGNED>(a, row0 + 16 * rt, c < c1, c * kG16Chunk);
   }
   __syncthreads();
 
@@ -664,25 +730,26 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   }
   f32x4 v = g16_reduce<RT, MT>(acc, xs);
 
-  // v is C[n][m] of tile (rt_e, q_e): m = 16 q_e + r, n = nb + i
+  // v is C[n][m] of tile (rt_e, q_e): m = 16 q_e + r, n = nb + i; undo the row factor
   const int64_t mi = 16 * q_e + r;
   const int64_t nb = row0 + 16 * rt_e + 4 * g;
   if (a.splits > 1) {
     if (tile_wave && mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + nb, v);
     if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, &flag)) return;
     if (tile_wave) {
+      const auto rs = dev_rsrc(a.part_w);
+      const int64_t mc = mi < a.m ? mi : a.m - 1;
       f32x4 s = {0, 0, 0, 0};
       for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {  // 8 partials in flight, added in order
         f32x4 part[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int sp = sp0 + u;
-          part[u] = (sp < a.splits && mi < a.m)
-                        ? (sp == split ? v : ld_dev4(a.part_w + ((int64_t)sp * a.m + mi) * a.n_pad + nb))
-                        : f32x4{0, 0, 0, 0};
+          const int sp = sp0 + u < a.splits ? sp0 + u : 0;
+          part[u] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mc) * a.n_pad + nb) * 4));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += part[u];
+        for (int u = 0; u < 8; ++u)
+          if (sp0 + u < a.splits) s += sp0 + u == split ? v : part[u];
       }
       v = s;
     }
@@ -701,7 +768,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
 #pragma unroll
       for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
         if (c >= rc) break;
-        const i32x4 b = early_b ? (c == 0 ? bw0 : bw1) : g16_b_frag_any(a, brow, brow < a.n, c);
+        const i32x4 b = early_b ? bw0 : g16_b_frag_any(a, brow, brow < a.n, c);
         i32x4 tv = {0, 0, 0, 0};
         if (mi < a.m) {
           const uint32_t* tp = a.t + (mi * a.rank_pad + 32 * c + 8 * g) / 2;
@@ -733,6 +800,10 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.kchunks = g16_cdiv(k, kG16Chunk);
   p.tiles_l = rank > 0 ? g16_cdiv(rank, 16) : 0;
   p.rank_pad = rank > 0 ? (int)(g16_cdiv(rank, 32) * 32) : 0;
+  // LoRA items: four chunks per wave pass, as many passes as keep the partials to about
+  // kG16LoraGroups K groups (their sum is on the path to t)
+  p.lc = kG16Waves * (int)g16_cdiv(p.kchunks, (int64_t)kG16Waves * kG16LoraGroups);
+  p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   if (m > 32) {
     // 33..64 tokens: 64-row workgroups running over their K chunks; split K only when there
     // are too few row tiles to fill the chip
@@ -744,8 +815,6 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
     if (splits < 1) splits = 1;
     p.cps = g16_cdiv(p.kchunks, splits);
     p.splits = (int)g16_cdiv(p.kchunks, p.cps);
-    p.lc = 1;
-    p.lgroups = rank > 0 ? p.kchunks : 0;
     p.n_pad = p.tiles_w * 64;
     p.xstride = kG16Chunk + 8;
     p.lds_bytes = (size_t)2 * 64 * (size_t)p.xstride * 2;  // two chunks of 64 tokens
@@ -755,8 +824,6 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   // K chunks whose activations fit the LDS budget (at least one for m <= 32)
   int64_t cps_lds = ((int64_t)kG16XBytes / 2 / m - 8) / kG16Chunk;
   if (cps_lds < 1) cps_lds = 1;
-  p.lc = (int)(cps_lds < kG16MaxLoraChunks ? cps_lds : kG16MaxLoraChunks);
-  p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   const int64_t items_l = p.tiles_l * p.lgroups;
   // Smallest K split with one batch of loads per wave; one row tile per workgroup if the
   // grid then runs in one round, else two (halves the workgroups of a split).
@@ -773,7 +840,7 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
     if (items_l + p.tiles_w * splits <= (int64_t)kG16CUs * (p.mt == 1 ? 5 : 4)) break;
   }
   p.n_pad = p.tiles_w * 16 * p.rt;
-  const int64_t xcols = (p.cps > p.lc ? p.cps : p.lc) * kG16Chunk;
+  const int64_t xcols = p.cps * kG16Chunk;
   p.xstride = (int)(xcols + 8);
   p.lds_bytes = (size_t)m * (size_t)p.xstride * 2;
   const size_t red_bytes = (size_t)kG16Waves * p.rt * p.mt * kWave * 16;  // the wave reduction reuses it
@@ -832,6 +899,10 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.tiles_w * p.splits);
   const bool aligned = (k % kG16Chunk) == 0;
   if (p.mt < 4 && p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return hipErrorInvalidValue;  // plan invariant
+  // partials are read through buffer descriptors with 32-bit byte offsets
+  if ((double)p.splits * (double)m * (double)p.n_pad * 4.0 >= 2147483648.0 ||
+      (double)p.lgroups * (double)m * (double)(p.tiles_l * 16) * 4.0 >= 2147483648.0)
+    return hipErrorInvalidValue;
   hipError_t e;
 #define QL_G16_LAUNCH(MT, RT, AL, XU)                                                          \
   e = hipFuncSetAttribute((const void*)g16_kernel<MT, RT, AL, XU>,                             \

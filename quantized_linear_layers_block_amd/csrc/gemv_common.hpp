@@ -50,6 +50,17 @@ __device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// 16-byte loads with the same cache policy as the device-scope loads above (sc1), through
+// a raw buffer descriptor over `base` (byte offsets below 2^31): one instruction where
+// ld_dev4 needs four, so that a thread can keep many partial tiles in flight at once.
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_dev4v(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, kCpolSc1));
+}
+
 // Bounded wait for a flag raised by another workgroup, for the calling wave only (lane 0
 // polls with device-scope loads while the other lanes are masked off).
 __device__ __forceinline__ void wave_wait_flag(const uint32_t* f) {
