@@ -578,18 +578,19 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
         if (mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g, acc[rt][q]);
       }
     if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
-    // the partials of all MT token tiles in flight together (4 splits each at a time),
-    // added in split order
+    // the partials of all MT token tiles in flight together (up to kSB splits each at a time:
+    // a device-scope round trip costs microseconds), added in split order
+    constexpr int kSB = 8;
     const auto rs = dev_rsrc(a.part_w);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 sum[MT];
 #pragma unroll
       for (int q = 0; q < MT; ++q) sum[q] = f32x4{0, 0, 0, 0};
-      for (int sp0 = 0; sp0 < a.splits; sp0 += 4) {
-        f32x4 part[4][MT];
+      for (int sp0 = 0; sp0 < a.splits; sp0 += kSB) {
+        f32x4 part[kSB][MT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kSB; ++u)
 #pragma unroll
           for (int q = 0; q < MT; ++q) {
             const int sp = sp0 + u < a.splits ? sp0 + u : 0;
@@ -597,7 +598,7 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
             part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
           }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kSB; ++u)
 #pragma unroll
           for (int q = 0; q < MT; ++q)
             if (sp0 + u < a.splits) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
@@ -805,12 +806,15 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.lc = kG16Waves * (int)g16_cdiv(p.kchunks, (int64_t)kG16Waves * kG16LoraGroups);
   p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   if (m > 32) {
-    // 33..64 tokens: 64-row workgroups running over their K chunks; split K only when there
-    // are too few row tiles to fill the chip
+    // 33..64 tokens: 64-row workgroups running over their K chunks.  K is split only when
+    // there are too few row tiles to fill the chip (two workgroups on a CU slow each other
+    // down more than a longer K loop costs), and into at most eight parts: the last arrival
+    // reads the partials in one batch of loads.
     p.mt = 4;
     p.rt = 1;
     p.tiles_w = g16_cdiv(n, 64);
     int64_t splits = g16_cdiv(224, p.tiles_w);
+    if (splits > 8) splits = 8;
     if (splits > p.kchunks) splits = p.kchunks;
     if (splits < 1) splits = 1;
     p.cps = g16_cdiv(p.kchunks, splits);
