@@ -52,6 +52,7 @@ __device__ __forceinline__ u16x2 nvfp4_chunk_max(const uint4* __restrict__ w, in
 struct Nvfp4TensorScale {
   float S;
   float six_S;
+  double r6;  // 1 / (double)six_S (0 when S is 0): amax_b / six_S as an exact quotient
 };
 
 __device__ __forceinline__ Nvfp4TensorScale nvfp4_tensor_scale(uint32_t amax_bits) {
@@ -59,12 +60,24 @@ __device__ __forceinline__ Nvfp4TensorScale nvfp4_tensor_scale(uint32_t amax_bit
   const float amax = __uint_as_float(amax_bits << 16);
   t.S = amax / 2688.0f;
   t.six_S = 6.0f * t.S;
+  t.r6 = t.six_S > 0.0f ? 1.0 / (double)t.six_S : 0.0;
   return t;
+}
+
+// Reciprocals of every block divisor a tensor can use: rtab[e] = 1 / (double)(E4M3(e) * S)
+// for the 256 scale codes (0 where the divisor is not positive), so that the encoder looks
+// them up instead of dividing once per block.  All threads of the workgroup call this, and
+// a barrier must separate it from the table's readers (and from earlier readers).
+__device__ __forceinline__ void nvfp4_fill_rtab(double* rtab, float S) {
+  for (int e = threadIdx.x; e < 256; e += kQThreads) {
+    const float d = e4m3_value((uint32_t)e) * S;
+    rtab[e] = d > 0.0f ? 1.0 / (double)d : 0.0;
+  }
 }
 
 // Encode one chunk: lanes (2i, 2i+1) hold the two halves of one 16-element block.
 __device__ __forceinline__ void nvfp4_encode_chunk(const uint4* __restrict__ w, int64_t nvec,
-                                                   int64_t chunk, Nvfp4TensorScale ts,
+                                                   int64_t chunk, Nvfp4TensorScale ts, const double* rtab,
                                                    uint32_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
   const int64_t base = chunk * kChunkVec + threadIdx.x;
@@ -82,10 +95,9 @@ __device__ __forceinline__ void nvfp4_encode_chunk(const uint4* __restrict__ w, 
     m = max_u16x2(m, abs_bits2(v[j].z));
     m = max_u16x2(m, abs_bits2(v[j].w));
     const uint32_t blk_bits = max_pair(hmax_u16x2(m));
-    uint32_t e = 0;
-    if (ts.S != 0.0f) e = e4m3_encode(__uint_as_float(blk_bits << 16) / ts.six_S);
-    const float d = e4m3_value(e) * ts.S;
-    const double r = d > 0.0f ? 1.0 / (double)d : 0.0;
+    uint32_t e = 0;  // fl32(amax_b / (6 S)) -> E4M3; the quotient is exact_quotient's
+    if (ts.S != 0.0f) e = e4m3_encode(exact_quotient(__uint_as_float(blk_bits << 16), ts.r6));
+    const double r = rtab[e];  // 1 / (double)(E4M3(e) * S)
     float q[8];
     q[0] = exact_quotient(bf16_lo(v[j].x), r);
     q[1] = exact_quotient(bf16_hi(v[j].x), r);
@@ -120,10 +132,13 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_encode_kernel(
     const uint32_t* __restrict__ partials, int nparts, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int32_t* status) {
   __shared__ uint32_t red[kQThreads / kWave];
+  __shared__ double rtab[256];
   uint32_t v = 0;
   for (int i = threadIdx.x; i < nparts; i += kQThreads) v = umax(v, partials[i]);
   const uint32_t amax_bits = max_block<kQThreads>(v, red);
   const Nvfp4TensorScale ts = nvfp4_tensor_scale(amax_bits);
+  nvfp4_fill_rtab(rtab, ts.S);
+  __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *tensor_scale = ts.S;
     if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_encode_kernel(
   // Back to front: the tail of the tensor, read last by the maximum pass, is the part
   // most likely still held in the memory-side cache.
   for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x)
-    nvfp4_encode_chunk(w, nvec, nchunks - 1 - c, ts, codes, scales);
+    nvfp4_encode_chunk(w, nvec, nchunks - 1 - c, ts, rtab, codes, scales);
 }
 
 static int stream_grid(int64_t nchunks, int cap) {
@@ -339,20 +354,28 @@ __global__ __launch_bounds__(kQThreads) void requant_encode_kernel(const Requant
                                                                    const RequantDesc* __restrict__ d,
                                                                    const uint32_t* __restrict__ amax,
                                                                    int32_t* status) {
+  __shared__ double rtab[256];
   const int64_t total = h->total_units;
   const int count = h->count;
+  int t_tab = -1;  // tensor whose divisors rtab holds (uniform over the workgroup)
   // Back to front over the whole table: the most recently read tensors go first.
   for (int64_t i = blockIdx.x; i < total; i += gridDim.x) {
     const int64_t u = total - 1 - i;
     const int t = find_tensor(d, count, u);
     const uint32_t amax_bits = amax[t];
     const Nvfp4TensorScale ts = nvfp4_tensor_scale(amax_bits);
+    if (t != t_tab) {
+      __syncthreads();  // the previous tensor's table is no longer read
+      nvfp4_fill_rtab(rtab, ts.S);
+      __syncthreads();
+      t_tab = t;
+    }
     const int64_t chunk = u - d[t].unit_begin;
     if (chunk == 0 && threadIdx.x == 0) {
       *d[t].tensor_scale = ts.S;
       if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
     }
-    nvfp4_encode_chunk((const uint4*)d[t].w, d[t].n * d[t].k / 8, chunk, ts,
+    nvfp4_encode_chunk((const uint4*)d[t].w, d[t].n * d[t].k / 8, chunk, ts, rtab,
                        (uint32_t*)d[t].codes, (uint8_t*)d[t].scales);
   }
 }
