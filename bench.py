@@ -13,8 +13,10 @@ copy it has not read for >= 1 GiB of other traffic, so no call is served from th
 256 MB memory-side cache.
 
 The JSON line also carries:
-  roofline      the decode layer kernel: bytes per launch / mean launch time (HIP
-                events on the launch stream), against 8 TB/s;
+  roofline      the decode layer kernel: algorithmic bytes per launch / mean launch time
+                (back-to-back launches in HIP graphs on the launch stream, HIP events
+                around the replays), against 8 TB/s;
+  hbm_copy_ceiling  a plain device copy at the same traffic, for scale;
   rows          one measurement per hot-path step (quantizers, prefill GEMMs, FP8
                 GEMM, whole-policy requantization and decode step), each against its
                 own roofline;
@@ -60,6 +62,7 @@ def decode_traffic():
     return DECODE_TRAFFIC["bytes_per_launch"] if h.hexdigest() == DECODE_TRAFFIC["sources_sha256"] else None
 DECODE_M = [1, 8, 64]
 RANK, LORA_S = 32, 2.0
+REP = 32                   # per-call timing: launches per captured graph
 
 
 def log(msg):
@@ -93,6 +96,23 @@ def copy_calibration(nbytes):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+
+
+def copy_ceiling(torch, dev):
+    """What the chip streams for a plain device-to-device copy (torch copy_), timed as
+    back-to-back launches in a HIP graph over rotated buffers: traffic = read + write bytes.
+    Sizes: the traffic of one 3584x18944 decode layer call (39.7 MB) and 1 GiB."""
+    out = []
+    for traffic in (39677956, 1 << 30):
+        half = traffic // 2 // 4096 * 4096
+        nb = max(4, -(-(2 << 30) // half))
+        bufs = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nb + 1)]
+        fns = [(lambda i=i: bufs[i + 1].copy_(bufs[i])) for i in range(nb)]
+        ms = _graph_ms(torch, fns)
+        out.append({"traffic_bytes": 2 * half, "us": round(ms * 1e3, 2),
+                    "GB/s": round(2 * half / (ms * 1e-3) / 1e9, 1)})
+        del bufs, fns
+    return out
 
 
 class Timer:
@@ -194,32 +214,54 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
 
-    # Per-launch kernel times: queue a cushion of graph replays so that the host runs
-    # ahead, then bracket every layer call with its own pair of events.
-    reps = 10
-    for j in range(40):
-        graphs[j % len(graphs)].replay()
-    timers = {key: Timer(torch) for key in order}
-    for rep in range(reps):
-        for i, (si, m) in enumerate(order):
-            c = copies[(len(order) * (rep + 7) + i) % ncopy][si]
-            e0 = timers[(si, m)].start()
-            call(c, si, m)
-            timers[(si, m)].stop(e0)
+    # Per-launch kernel times.  A pair of HIP events around a single launch adds several
+    # microseconds of event overhead on this GPU (an empty kernel reads ~6.6 us that way,
+    # ~1.6 us back to back), so each layer call is timed as back-to-back launches captured
+    # in HIP graphs of REP launches on the launch stream, events around the replays.  The
+    # launches walk a pool of distinct weight copies holding >= 1 GiB per shape, so no
+    # launch reads a weight still held by the memory-side cache.
+    pools = []
+    for si, (k, n) in enumerate(DECODE_SHAPES):
+        need = max(2 * REP, int(np.ceil(2 ** 30 / (n * k * 0.5625))))
+        pool = [copies[j][si] for j in range(ncopy)]
+        while len(pool) < need:
+            src = pool[len(pool) % ncopy]
+            pool.append(ql.NVFP4Weight(src.codes.clone(), src.scales.clone(), src.tensor_scale.clone(), n, k))
+        pools.append(pool)
     torch.cuda.synchronize()
-    cases, tot_bytes, tot_ms = [], 0.0, 0.0
+    cases, tot_bytes, tot_us, launches = [], 0.0, 0.0, 0
     for si, m in order:
         k, n = DECODE_SHAPES[si]
-        ms = timers[(si, m)].total_ms() / reps
+        pool = pools[si]
+        graphs_c = []
+        for g0 in range(0, len(pool), REP):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                for i in range(REP):
+                    call(pool[(g0 + i) % len(pool)], si, m)
+            graphs_c.append(gph)
+        for gph in graphs_c:
+            gph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for gph in graphs_c:
+            gph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        nl = REP * len(graphs_c)
+        us = e0.elapsed_time(e1) * 1e3 / nl
+        del graphs_c
         by = decode_bytes(m, n, k, RANK)
-        tot_bytes += by * reps
-        tot_ms += ms * reps
-        gbs = by / (ms * 1e-3) / 1e9
-        cases.append({"K": k, "N": n, "M": m, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                      "frac": round(gbs * 1e9 / HBM_PEAK, 4)})
-    launches = reps * len(order)
-    kern_ms = tot_ms / launches
-    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
+        tot_bytes += by
+        tot_us += us
+        launches += nl
+        gbs = by / (us * 1e-6) / 1e9
+        cases.append({"K": k, "N": n, "M": m, "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "frac": round(gbs * 1e9 / HBM_PEAK, 4), "launches_timed": nl})
+    del pools
+    ceiling = copy_ceiling(torch, dev)
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
 
     result = {
         "metric": "NVFP4/FP8 qlinear TFLOP/s & HBM GB/s (% roofline); requant GB/s",
@@ -240,9 +282,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "qlinear_forward (NVFP4, M<=64)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": decode_traffic(),
-                     "launches": launches, "mean_launch_us": round(kern_ms * 1e3, 3),
-                     "bytes_per_launch_mean": round(tot_bytes / launches)},
+                     "launches": launches, "mean_launch_us": round(tot_us / len(order), 3),
+                     "bytes_per_launch_mean": round(tot_bytes / len(order))},
         "decode_cases": cases,
+        "hbm_copy_ceiling": ceiling,
         "setup_s": round(setup_s, 1),
     }
 
@@ -273,6 +316,34 @@ def _events_ms(torch, fn, reps):
     return t.total_ms() / reps
 
 
+def _graph_ms(torch, fns, reps=None):
+    """Mean time per launch of a HIP graph that calls fns[0], fns[1], ... in turn (reps
+    launches, default one per callable), replayed four times, events around the replays.
+    Rotating callables over distinct buffers keeps repeated calls from being served by
+    the 256 MB memory-side cache."""
+    reps = reps or len(fns)
+    fns[0]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fns[i % len(fns)]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (4 * reps)
+
+
+def _copies_for(nbytes):
+    """Distinct buffer copies so that one pass over them moves >= 1 GiB (2 to 48)."""
+    return int(min(48, max(2, -(-(1 << 30) // int(nbytes)))))
+
+
 def _row(kind, work, ms, peak, unit_work):
     rate = work / (ms * 1e-3)
     if kind == "hbm":
@@ -293,13 +364,18 @@ def run_rows(rows, torch, ql, dev):
         res = []
         for si, (k, n) in enumerate(DECODE_SHAPES):
             w = sg.normal_bf16((n, k), 0.02, sg.gen(sg.seed_of(2, si, 1)), 0.005, 20.0, dev)
-            q = ql.NVFP4Weight.empty(n, k, dev)
-            ws = torch.empty(4096, dtype=torch.uint8, device=dev)
-            ms = _events_ms(torch, lambda: ql.binding.qlinear_quantize_nvfp4(w, q.codes, q.scales, q.tensor_scale, ws), 10)
+            nc = _copies_for(n * k * 2.5625)
+            ws_ = [w] + [w.clone() for _ in range(nc - 1)]
+            qs = [ql.NVFP4Weight.empty(n, k, dev) for _ in range(nc)]
+            wsp = torch.zeros(ql.binding.qlinear_quantize_workspace(ql.QL_NVFP4, n, k) + 16,
+                              dtype=torch.uint8, device=dev)
+            fns = [(lambda w_=w_, q=q: ql.binding.qlinear_quantize_nvfp4(w_, q.codes, q.scales, q.tensor_scale, wsp))
+                   for w_, q in zip(ws_, qs)]
+            ms = _graph_ms(torch, fns)
             r = _row("hbm", n * k * 2.5625, ms, HBM_PEAK, "B")
-            r.update({"K": k, "N": n})
+            r.update({"K": k, "N": n, "copies_rotated": nc})
             res.append(r)
-            del w, q
+            del w, ws_, qs
         out["a1_quantize_nvfp4"] = res
         log("a1 done")
 
@@ -312,11 +388,15 @@ def run_rows(rows, torch, ql, dev):
         if "a2" in rows:
             res = []
             for k, n, w, x in c4:
-                q = ql.FP8Weight.empty(n, k, dev)
-                ms = _events_ms(torch, lambda: ql.binding.qlinear_quantize_fp8_block(w, q.codes, q.scales), 10)
+                ws_ = [w, w.clone(), w.clone()]
+                qs = [ql.FP8Weight.empty(n, k, dev) for _ in ws_]
+                fns = [(lambda w_=w_, q=q: ql.binding.qlinear_quantize_fp8_block(w_, q.codes, q.scales))
+                       for w_, q in zip(ws_, qs)]
+                ms = _graph_ms(torch, fns, 6)
                 r = _row("hbm", n * k * 3 + (n // 128) * (k // 128) * 4, ms, HBM_PEAK, "B")
                 r.update({"K": k, "N": n})
                 res.append(r)
+                del ws_, qs
             out["a2_quantize_fp8_weight"] = res
         if "a3" in rows:
             res = []
@@ -324,10 +404,13 @@ def run_rows(rows, torch, ql, dev):
                 m = x.shape[0]
                 xq = torch.empty((m, k), dtype=torch.uint8, device=dev)
                 sx = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
-                ms = _events_ms(torch, lambda: ql.binding.qlinear_quantize_act_fp8(x, xq, sx), 10)
+                xs_ = [x, x.clone(), x.clone()]
+                fns = [(lambda x_=x_: ql.binding.qlinear_quantize_act_fp8(x_, xq, sx)) for x_ in xs_]
+                ms = _graph_ms(torch, fns, 6)
                 r = _row("hbm", m * k * 3 + m * (k // 128) * 4, ms, HBM_PEAK, "B")
                 r.update({"M": m, "K": k})
                 res.append(r)
+                del xs_
             out["a3_quantize_fp8_act"] = res
         if "a6" in rows:
             res = []
