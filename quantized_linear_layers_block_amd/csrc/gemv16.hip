@@ -32,6 +32,7 @@
 //   flag are returned to zero by the call that used them.
 #include "../../include/qlinear.h"
 #include "common.hpp"
+#include "gemm_common.hpp"
 #include "gemv_common.hpp"
 #include "launch.hpp"
 
@@ -72,6 +73,8 @@ struct G16Args {
   int rank_pad;       // t row length (multiple of 32)
   int64_t n_pad;      // row length of the weight partials
   int xstride;        // LDS row stride of the activations (elements)
+  int64_t kst;        // 128-wide K stages (33..64 tokens with K % 128 == 0), else 0
+  int64_t sps;        // stages per K split
   uint32_t* ctr;      // counters and flags, one per 128-byte line (g16_line_*)
   uint32_t* t;        // [m][rank_pad / 2] bf16 pairs
   float* part_w;      // [splits][m][n_pad]
@@ -414,7 +417,7 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
   const int64_t lrow = a.tiles_l * 16;
   if (wave < MT) {
     const int64_t mi = 16 * wave + r;
-    if (mi < a.m) st_dev4(a.part_l + (cg * a.m + mi) * lrow + tile * 16 + 4 * g, v);
+    if (mi < a.m) st_dev4v(dev_rsrc(a.part_l), (uint32_t)(((cg * a.m + mi) * lrow + tile * 16 + 4 * g) * 4), v);
   }
   if (!g16_arrive(g16_ctr(a, g16_line_l(a)), (uint32_t)(a.tiles_l * a.lgroups), flag)) return;
 
@@ -449,6 +452,105 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
   if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, g16_line_t(a)), 1u);
 }
 
+
+// Finishing a 64-row streaming tile (wave w: rows row0 .. +16 RT, all four token tiles):
+// split partials (device scope) and the last arrival's fixed-order sum, S, the LoRA term
+// once t is published, and the store.
+template <int RT>
+__device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, int64_t tile, int64_t split,
+                                                  int64_t row0, f32x4 (&acc)[RT][4], const i32x4 (&bw)[RT][2],
+                                                  bool early_b, float ts) {
+  constexpr int MT = 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, g = lane >> 4;
+  // tiles (rt, q): acc[rt][q] is C[n][m] with m = 16 q + r, n = row0 + 16 rt + 4 g + i
+  if (a.splits > 1) {
+    const auto ws_rs = dev_rsrc(a.part_w);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mi = 16 * q + r;
+        if (mi < a.m)
+          st_dev4v(ws_rs, (uint32_t)(((split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4), acc[rt][q]);
+      }
+    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
+    // the partials of all MT token tiles in flight together (up to kSB splits each at a time:
+    // a device-scope round trip costs microseconds), added in split order
+    constexpr int kSB = 8;
+    const auto rs = dev_rsrc(a.part_w);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 sum[MT];
+#pragma unroll
+      for (int q = 0; q < MT; ++q) sum[q] = f32x4{0, 0, 0, 0};
+      for (int sp0 = 0; sp0 < a.splits; sp0 += kSB) {
+        f32x4 part[kSB][MT];
+#pragma unroll
+        for (int u = 0; u < kSB; ++u)
+#pragma unroll
+          for (int q = 0; q < MT; ++q) {
+            const int sp = sp0 + u < a.splits ? sp0 + u : 0;
+            const int64_t mi = min((int64_t)(16 * q + r), a.m - 1);
+            part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
+          }
+#pragma unroll
+        for (int u = 0; u < kSB; ++u)
+#pragma unroll
+          for (int q = 0; q < MT; ++q)
+            if (sp0 + u < a.splits) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
+      }
+#pragma unroll
+      for (int q = 0; q < MT; ++q) acc[rt][q] = sum[q];
+    }
+    if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, tile), 0u);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[rt][q] *= ts;
+  if (a.rank > 0) {
+    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
+      int it = 0;
+      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
+    }
+    __syncthreads();
+    const int rc = a.rank_pad / 32;
+#pragma unroll
+    for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
+      if (c >= rc) break;
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        const int64_t mi = 16 * q + r;
+        i32x4 tv = {0, 0, 0, 0};
+        if (mi < a.m) {
+          const uint32_t* tp = a.t + (mi * a.rank_pad + 32 * c + 8 * g) / 2;
+          tv = i32x4{(int)ld_dev_u32(tp), (int)ld_dev_u32(tp + 1), (int)ld_dev_u32(tp + 2), (int)ld_dev_u32(tp + 3)};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int64_t brow = row0 + 16 * rt + r;
+          const i32x4 b = early_b ? (c == 0 ? bw[rt][0] : bw[rt][1]) : g16_b_frag_any(a, brow, brow < a.n, c);
+          acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                               __builtin_bit_cast(bf16x8, tv), acc[rt][q], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave of this workgroup has read t
+    if (threadIdx.x == 0 && g16_fin(a, tile)) {
+      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
+      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+      const int64_t mi = 16 * q + r;
+      const int64_t nb = row0 + 16 * rt + 4 * g;
+      if (mi < a.m && nb < a.n) g16_store(a, mi, nb, acc[rt][q]);
+    }
+}
 
 // ------------------------------------------------------------------ many-token weight item
 // 33 to 64 tokens: the activations of a whole K range no longer fit in LDS, so the
@@ -568,91 +670,159 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
     __syncthreads();
   }
 
-  // tiles (rt, q): acc[rt][q] is C[n][m] with m = 16 q + r, n = row0 + 16 rt + 4 g + i
-  if (a.splits > 1) {
+  g16_stream_finish<RT>(a, flag, tile, split, row0, acc, bw, early_b, ts);
+}
+
+// ------------------------------------------------------------------ 128-wide stage item
+// 33 to 64 tokens, K % 128 == 0.  A workgroup owns 64 weight rows and all (up to) 64 tokens
+// over its K range, walked in stages of 128 columns.  Each stage's activations (16 KB),
+// codes (4 KB) and block scales are copied straight from global memory into LDS
+// (global_load_lds), activations three stages deep and codes and scales six, so the codes
+// stream five stages ahead of the multiply and no register holds data in flight.  Wave w
+// takes MFMA K step w (32 columns) of every stage for all 64 rows and all 64 tokens: each
+// activation byte is then read from LDS by one wave only, and the four waves' tiles are
+// added in LDS in a fixed order at the end (wave w keeps rows 16 w .. +16).
+//
+// LDS (bytes): activations [0, 49152) as 3 slots of 64 token rows x 256 B, the 16-byte unit
+// u of token t at slot u ^ (t % 16); codes [49152, 73728) as 6 slots of 64 rows x 4 parts
+// of 16 B (part p = columns 32 p .. +32), part p of row j at position (p + j / 4) % 4 of the
+// row's four; scales [73728, 79872) as 6 slots of 64 rows x 8 B (waves 2 and 3 copy a
+// second, unread image).  Both placements make every fragment read conflict-free.
+
+// Global -> LDS copies through the compiler's LDS-DMA builtin (16 or 4 bytes per lane, to
+// lds + 16 lane or lds + 4 lane; lds uniform): the compiler then knows them for what they
+// are and waits only where the explicit vmcnt waits below say (issued as inline assembly
+// it inserted vmcnt waits before unrelated LDS reads, which emptied the prefetch queue).
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+__device__ __forceinline__ void lds_copy16_b(const uint8_t* base, uint32_t off, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4_b(const uint8_t* base, uint32_t off, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)lds, 4, 0, 0);
+}
+constexpr int kS128X = 16384, kS128C = 4096, kS128S = 1024;
+constexpr int kS128XSlots = 3, kS128CSlots = 6;
+constexpr int kS128COff = kS128XSlots * kS128X;
+constexpr int kS128SOff = kS128COff + kS128CSlots * kS128C;
+constexpr int kS128Lds = kS128SOff + kS128CSlots * kS128S;  // 79872: two workgroups per CU
+
+__device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* xs16, int* flag, int64_t id) {
+  constexpr int MT = 4;
+  uint8_t* smem = (uint8_t*)xs16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t tile = id % a.tiles_w;
+  const int64_t split = id / a.tiles_w;
+  const int64_t s0 = split * a.sps, s1 = min(s0 + a.sps, a.kst);
+  const int64_t rbase = tile * 64;
+
+  // LoRA B rows of this wave's finishing rows (16 w .. +16) and S, before the stream
+  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
+  const int64_t row_f = rbase + 16 * wave;
+  i32x4 bw[1][2];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+  for (int c = 0; c < 2; ++c) bw[0][c] = g16_b_frag_vec(a, row_f + r, early_b && row_f + r < a.n, c);
+  const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // per-lane global byte offsets (stage 0) of this wave's copies
+  uint32_t xo[4];
 #pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        if (mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g, acc[rt][q]);
-      }
-    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
-    // the partials of all MT token tiles in flight together (up to kSB splits each at a time:
-    // a device-scope round trip costs microseconds), added in split order
-    constexpr int kSB = 8;
-    const auto rs = dev_rsrc(a.part_w);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 sum[MT];
-#pragma unroll
-      for (int q = 0; q < MT; ++q) sum[q] = f32x4{0, 0, 0, 0};
-      for (int sp0 = 0; sp0 < a.splits; sp0 += kSB) {
-        f32x4 part[kSB][MT];
-#pragma unroll
-        for (int u = 0; u < kSB; ++u)
-#pragma unroll
-          for (int q = 0; q < MT; ++q) {
-            const int sp = sp0 + u < a.splits ? sp0 + u : 0;
-            const int64_t mi = min((int64_t)(16 * q + r), a.m - 1);
-            part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
-          }
-#pragma unroll
-        for (int u = 0; u < kSB; ++u)
-#pragma unroll
-          for (int q = 0; q < MT; ++q)
-            if (sp0 + u < a.splits) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
-      }
-#pragma unroll
-      for (int q = 0; q < MT; ++q) acc[rt][q] = sum[q];
-    }
-    if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, tile), 0u);
+  for (int j = 0; j < 4; ++j) {
+    const int t = 16 * wave + 4 * j + (lane >> 4);
+    const int64_t tc = t < a.m ? t : a.m - 1;
+    const int u = (lane & 15) ^ (t & 15);
+    xo[j] = (uint32_t)((tc * a.k + 8 * u) * 2);
   }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int q = 0; q < MT; ++q) acc[rt][q] *= ts;
-  if (a.rank > 0) {
-    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
-      int it = 0;
-      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
-    }
-    __syncthreads();
-    const int rc = a.rank_pad / 32;
-#pragma unroll
-    for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
-      if (c >= rc) break;
-#pragma unroll
-      for (int q = 0; q < MT; ++q) {
-        const int64_t mi = 16 * q + r;
-        i32x4 tv = {0, 0, 0, 0};
-        if (mi < a.m) {
-          const uint32_t* tp = a.t + (mi * a.rank_pad + 32 * c + 8 * g) / 2;
-          tv = i32x4{(int)ld_dev_u32(tp), (int)ld_dev_u32(tp + 1), (int)ld_dev_u32(tp + 2), (int)ld_dev_u32(tp + 3)};
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int64_t brow = row0 + 16 * rt + r;
-          const i32x4 b = early_b ? (c == 0 ? bw[rt][0] : bw[rt][1]) : g16_b_frag_any(a, brow, brow < a.n, c);
-          acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
-                                                               __builtin_bit_cast(bf16x8, tv), acc[rt][q], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // every wave of this workgroup has read t
-    if (threadIdx.x == 0 && g16_fin(a, tile)) {
-      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
-      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
-    }
+  uint32_t co, so;
+  {
+    const int rho = 16 * wave + (lane >> 2);
+    const int64_t gr = rbase + rho < a.n ? rbase + rho : a.n - 1;
+    const int part = ((lane & 3) - ((rho >> 2) & 3)) & 3;
+    co = (uint32_t)(gr * (a.k / 2) + 16 * part);
+    const int srow = 32 * (wave & 1) + (lane >> 1);
+    const int64_t gs = rbase + srow < a.n ? rbase + srow : a.n - 1;
+    so = (uint32_t)(gs * (a.k / 16) + 4 * (lane & 1));
   }
+  auto dma_x = [&](int64_t st, int slot) {
+    const uint8_t* base = (const uint8_t*)a.x + st * 256;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int j = 0; j < 4; ++j) lds_copy16_b(base, xo[j], smem + slot * kS128X + (4 * wave + j) * 1024);
+  };
+  auto dma_c = [&](int64_t st, int slot) {
+    lds_copy16_b(a.codes + st * 64, co, smem + kS128COff + slot * kS128C + wave * 1024);
+    lds_copy4_b(a.scales + st * 8, so, smem + kS128SOff + slot * kS128S + wave * 256);
+  };
+  auto cl = [&](int64_t st) { return st < s1 ? st : s1 - 1; };
+
+  f32x4 acc[4][MT];
 #pragma unroll
-    for (int q = 0; q < MT; ++q) {
-      const int64_t mi = 16 * q + r;
-      const int64_t nb = row0 + 16 * rt + 4 * g;
-      if (mi < a.m && nb < a.n) g16_store(a, mi, nb, acc[rt][q]);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) acc[i][q] = f32x4{0, 0, 0, 0};
+
+  // issue order: C(s0) X(s0) C(s0+1) X(s0+1) C(s0+2) C(s0+3) C(s0+4), then per stage st the
+  // batch X(st+2) C(st+5) (six copies per wave).  Copies complete in issue order, so when
+  // stage st is needed the wait leaves in flight the C(st+3) issued after X(st) and the
+  // last batch (eight copies; more only in the prologue, where vmcnt(8) merely waits a
+  // little longer): codes keep their lead over the activations.
+  dma_c(s0, 0);
+  dma_x(s0, 0);
+  dma_c(cl(s0 + 1), 1);
+  dma_x(cl(s0 + 1), 1);
+  dma_c(cl(s0 + 2), 2);
+  dma_c(cl(s0 + 3), 3);
+  dma_c(cl(s0 + 4), 4);
+  int xsl = 0, csl = 0;
+  for (int64_t st = s0; st < s1; ++st) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();  // stage st landed for every wave; nobody reads stage st - 1 any more
+    const int xsl2 = xsl + 2 >= kS128XSlots ? xsl + 2 - kS128XSlots : xsl + 2;
+    const int csl5 = csl + 5 >= kS128CSlots ? csl + 5 - kS128CSlots : csl + 5;
+    dma_x(cl(st + 2), xsl2);
+    dma_c(cl(st + 5), csl5);
+    const uint8_t* X = smem + xsl * kS128X;
+    const uint8_t* C = smem + kS128COff + csl * kS128C;
+    const uint8_t* Sc = smem + kS128SOff + csl * kS128S;
+    bf16x8 av[4], bv[MT];
+#pragma unroll
+    for (int q = 0; q < MT; ++q)
+      bv[q] = *(const bf16x8*)(X + (16 * q + r) * 256 + 16 * ((4 * wave + g) ^ r));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rho = 16 * i + r;
+      const uint32_t cw = *(const uint32_t*)(C + (4 * rho + ((wave + (r >> 2)) & 3)) * 16 + 4 * g);
+      const uint32_t sb = Sc[rho * 8 + 2 * wave + (g >> 1)];
+      av[i] = gv_dequant8(cw, e4m3_value(sb));
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < MT; ++q)
+        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[q], acc[i][q], 0, 0, 0);
+    xsl = xsl + 1 == kS128XSlots ? 0 : xsl + 1;
+    csl = csl + 1 == kS128CSlots ? 0 : csl + 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped copies past the range too
+  __syncthreads();
+
+  // the four waves' K steps added in wave order; wave w keeps row tile w
+  f32x4* red = (f32x4*)smem;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < MT; ++q) red[((wave * 4 + i) * MT + q) * kWave + lane] = acc[i][q];
+  __syncthreads();
+  f32x4 v[1][MT];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    f32x4 sum = red[((0 * 4 + wave) * MT + q) * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += red[((w * 4 + wave) * MT + q) * kWave + lane];
+    v[0][q] = sum;
+  }
+  g16_stream_finish<1>(a, flag, tile, split, row_f, v, bw, early_b, ts);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -674,7 +844,10 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
 
   // -------------------------------------------------------------------- weight item
   if constexpr (MT == 4) {
-    g16_stream_item<RT, ALIGNED>(a, xs, &flag, id - items_l);
+    if (a.kst > 0)
+      g16_stream128_item(a, xs, &flag, id - items_l);
+    else
+      g16_stream_item<RT, ALIGNED>(a, xs, &flag, id - items_l);
   } else {
   id -= items_l;
   const int64_t tile = id % a.tiles_w;
@@ -735,7 +908,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   const int64_t mi = 16 * q_e + r;
   const int64_t nb = row0 + 16 * rt_e + 4 * g;
   if (a.splits > 1) {
-    if (tile_wave && mi < a.m) st_dev4(a.part_w + (split * a.m + mi) * a.n_pad + nb, v);
+    if (tile_wave && mi < a.m) st_dev4v(dev_rsrc(a.part_w), (uint32_t)(((split * a.m + mi) * a.n_pad + nb) * 4), v);
     if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, &flag)) return;
     if (tile_wave) {
       const auto rs = dev_rsrc(a.part_w);
@@ -806,20 +979,37 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.lc = kG16Waves * (int)g16_cdiv(p.kchunks, (int64_t)kG16Waves * kG16LoraGroups);
   p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   if (m > 32) {
-    // 33..64 tokens: 64-row workgroups running over their K chunks.  K is split only when
-    // there are too few row tiles to fill the chip (two workgroups on a CU slow each other
-    // down more than a longer K loop costs), and into at most eight parts: the last arrival
-    // reads the partials in one batch of loads.
     p.mt = 4;
     p.rt = 1;
     p.tiles_w = g16_cdiv(n, 64);
+    p.n_pad = p.tiles_w * 64;
+    if (k % 128 == 0 && 64.0 * (double)k * 2.0 < 2147483648.0 && (double)n * (double)(k / 2) < 2147483648.0) {
+      // 33..64 tokens, 128-wide stages (g16_stream128_item).  K is split into as many parts
+      // as keep every workgroup on a CU of its own (two on one CU run markedly slower than
+      // one), at most eight and of at least four stages each: split partials cost 4 M N
+      // bytes each way.
+      p.kst = k / 128;
+      int64_t splits = 256 / p.tiles_w;
+      if (splits > 8) splits = 8;
+      if (splits > p.kst / 4) splits = p.kst / 4;
+      if (splits < 1) splits = 1;
+      p.sps = g16_cdiv(p.kst, splits);
+      p.splits = (int)g16_cdiv(p.kst, p.sps);
+      p.cps = 0;
+      p.xstride = 0;
+      p.lds_bytes = (size_t)kS128Lds;
+      return p;
+    }
+    // other K: 64-row workgroups running over 256-wide K chunks.  K is split only when
+    // there are too few row tiles to fill the chip (two workgroups on a CU slow each other
+    // down more than a longer K loop costs), and into at most eight parts: the last arrival
+    // reads the partials in one batch of loads.
     int64_t splits = g16_cdiv(224, p.tiles_w);
     if (splits > 8) splits = 8;
     if (splits > p.kchunks) splits = p.kchunks;
     if (splits < 1) splits = 1;
     p.cps = g16_cdiv(p.kchunks, splits);
     p.splits = (int)g16_cdiv(p.kchunks, p.cps);
-    p.n_pad = p.tiles_w * 64;
     p.xstride = kG16Chunk + 8;
     p.lds_bytes = (size_t)2 * 64 * (size_t)p.xstride * 2;  // two chunks of 64 tokens
     return p;
@@ -892,6 +1082,8 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.rank_pad = p.rank_pad;
   a.n_pad = p.n_pad;
   a.xstride = p.xstride;
+  a.kst = p.kst;
+  a.sps = p.sps;
   char* w = (char*)ws;
   a.ctr = (uint32_t*)w;
   size_t off = g16_counter_bytes(p);

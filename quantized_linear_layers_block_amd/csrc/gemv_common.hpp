@@ -60,6 +60,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base) {
 __device__ __forceinline__ f32x4 ld_dev4v(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, kCpolSc1));
 }
+// The matching 16-byte store (same sc1 policy as st_dev, one instruction instead of four):
+// partial tiles leave as whole 16-byte pieces.
+__device__ __forceinline__ void st_dev4v(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rs, (int)byte_off, 0, kCpolSc1);
+}
 
 // Bounded wait for a flag raised by another workgroup, for the calling wave only (lane 0
 // polls with device-scope loads while the other lanes are masked off).

@@ -75,6 +75,8 @@ struct G16Plan {
   int splits;
   int64_t n_pad;
   int xstride;        // LDS row stride of the staged activations
+  int64_t kst = 0;    // 128-wide K stages of the 33..64-token stage path (0: not used)
+  int64_t sps = 0;    // stages per K split on that path
   size_t lds_bytes;
 };
 G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank);

@@ -70,7 +70,11 @@ def test_nvfp4_decode_config2_full_size(shape_idx, m):
 
 
 @pytest.mark.parametrize("m,n,k,r", [(1, 16, 16, 0), (3, 200, 272, 8), (5, 130, 1040, 40), (17, 64, 4096, 16),
-                                     (40, 300, 784, 32), (64, 96, 8192, 128), (2, 4096, 512, 0)])
+                                     (40, 300, 784, 32), (64, 96, 8192, 128), (2, 4096, 512, 0),
+                                     # 33..64 tokens with K % 128 == 0: one stage, K % 256 != 0,
+                                     # several K splits, ragged N, rank not a multiple of 8
+                                     (64, 72, 128, 0), (33, 200, 1152, 8), (48, 1000, 2048, 32),
+                                     (50, 4100, 3840, 40), (37, 130, 640, 20), (64, 512, 3584, 32)])
 def test_nvfp4_skinny_ragged(m, n, k, r):
     g = np.random.default_rng(m * 1000 + n + k)
     w = synth.normal_bf16((n, k), 0.02, g, 0.01, 15.0)
