@@ -38,18 +38,18 @@ BF16_PEAK = 2.5e15         # dense MFMA flop/s
 FP8_PEAK = 5.0e15
 DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K, N)
 
-# HBM traffic of the decode layer kernel (g16_kernel) per launch, the mean over every
-# launch of the decode workload, from two counter runs over
-#   bench.py --rows none --no-cpu-baseline --steps 3 --warmup 1
+# HBM traffic of the decode layer kernel (g16_kernel) per launch, the mean over the 12
+# layer calls of the decode workload, from two counter runs over
+#   bench.py --rows none --no-cpu-baseline --steps-only --steps 3 --warmup 1
 # under rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE.  Each counter is scaled by
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 31688783, "fetch_bytes": 27013487, "write_bytes": 4675296,
+DECODE_TRAFFIC = {"bytes_per_launch": 27849651, "fetch_bytes": 26559630, "write_bytes": 1290021,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "c962ebb2d82209e1eea78df71e665a91926d04745760d9dfda6c01d5f1555668"}
+                  "sources_sha256": "87a0a9f52be535189d0027a81016604070236523f8bd1eb7252b8f00fdf0ec7a"}
 
 
 def decode_traffic():
@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--rows", default="all")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="time the decode step only (no per-call launches, no copy ceiling): every layer "
+                         "call is launched equally often, as hardware-counter runs need")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -214,53 +217,56 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
 
-    # Per-launch kernel times.  A pair of HIP events around a single launch adds several
-    # microseconds of event overhead on this GPU (an empty kernel reads ~6.6 us that way,
-    # ~1.6 us back to back), so each layer call is timed as back-to-back launches captured
-    # in HIP graphs of REP launches on the launch stream, events around the replays.  The
-    # launches walk a pool of distinct weight copies holding >= 1 GiB per shape, so no
-    # launch reads a weight still held by the memory-side cache.
-    pools = []
-    for si, (k, n) in enumerate(DECODE_SHAPES):
-        need = max(2 * REP, int(np.ceil(2 ** 30 / (n * k * 0.5625))))
-        pool = [copies[j][si] for j in range(ncopy)]
-        while len(pool) < need:
-            src = pool[len(pool) % ncopy]
-            pool.append(ql.NVFP4Weight(src.codes.clone(), src.scales.clone(), src.tensor_scale.clone(), n, k))
-        pools.append(pool)
-    torch.cuda.synchronize()
-    cases, tot_bytes, tot_us, launches = [], 0.0, 0.0, 0
-    for si, m in order:
-        k, n = DECODE_SHAPES[si]
-        pool = pools[si]
-        graphs_c = []
-        for g0 in range(0, len(pool), REP):
-            gph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gph):
-                for i in range(REP):
-                    call(pool[(g0 + i) % len(pool)], si, m)
-            graphs_c.append(gph)
-        for gph in graphs_c:
-            gph.replay()
+    if args.steps_only:
+        cases, tot_bytes, tot_us, launches, ceiling = [], 1.0, float('nan'), 0, None
+    else:
+        # Per-launch kernel times.  A pair of HIP events around a single launch adds several
+        # microseconds of event overhead on this GPU (an empty kernel reads ~6.6 us that way,
+        # ~1.6 us back to back), so each layer call is timed as back-to-back launches captured
+        # in HIP graphs of REP launches on the launch stream, events around the replays.  The
+        # launches walk a pool of distinct weight copies holding >= 1 GiB per shape, so no
+        # launch reads a weight still held by the memory-side cache.
+        pools = []
+        for si, (k, n) in enumerate(DECODE_SHAPES):
+            need = max(2 * REP, int(np.ceil(2 ** 30 / (n * k * 0.5625))))
+            pool = [copies[j][si] for j in range(ncopy)]
+            while len(pool) < need:
+                src = pool[len(pool) % ncopy]
+                pool.append(ql.NVFP4Weight(src.codes.clone(), src.scales.clone(), src.tensor_scale.clone(), n, k))
+            pools.append(pool)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for gph in graphs_c:
-            gph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        nl = REP * len(graphs_c)
-        us = e0.elapsed_time(e1) * 1e3 / nl
-        del graphs_c
-        by = decode_bytes(m, n, k, RANK)
-        tot_bytes += by
-        tot_us += us
-        launches += nl
-        gbs = by / (us * 1e-6) / 1e9
-        cases.append({"K": k, "N": n, "M": m, "us": round(us, 2), "GB/s": round(gbs, 1),
-                      "frac": round(gbs * 1e9 / HBM_PEAK, 4), "launches_timed": nl})
-    del pools
-    ceiling = copy_ceiling(torch, dev)
+        cases, tot_bytes, tot_us, launches = [], 0.0, 0.0, 0
+        for si, m in order:
+            k, n = DECODE_SHAPES[si]
+            pool = pools[si]
+            graphs_c = []
+            for g0 in range(0, len(pool), REP):
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph):
+                    for i in range(REP):
+                        call(pool[(g0 + i) % len(pool)], si, m)
+                graphs_c.append(gph)
+            for gph in graphs_c:
+                gph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for gph in graphs_c:
+                gph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            nl = REP * len(graphs_c)
+            us = e0.elapsed_time(e1) * 1e3 / nl
+            del graphs_c
+            by = decode_bytes(m, n, k, RANK)
+            tot_bytes += by
+            tot_us += us
+            launches += nl
+            gbs = by / (us * 1e-6) / 1e9
+            cases.append({"K": k, "N": n, "M": m, "us": round(us, 2), "GB/s": round(gbs, 1),
+                          "frac": round(gbs * 1e9 / HBM_PEAK, 4), "launches_timed": nl})
+        del pools
+        ceiling = copy_ceiling(torch, dev)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
 
     result = {
