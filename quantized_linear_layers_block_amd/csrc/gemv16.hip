@@ -47,7 +47,8 @@ constexpr int kG16XUnits = 8;          // 16-byte activation units per thread (8
 constexpr int kG16XUnits1 = 2;         // the same for one token: 16 chunks of 32 units
 constexpr int kG16EarlyRank = 64;      // B rows of ranks up to 64 are fetched at the start (64 tokens)
 constexpr int kG16EarlyRankFew = 32;   // the same for up to 32 tokens (one fragment: fewer registers)
-constexpr int kG16LoraGroups = 8;      // K groups of the LoRA partials (at most about)
+constexpr int kG16LoraGroupsFew = 32;  // K groups of the LoRA partials (at most about), <= 32 tokens
+constexpr int kG16LoraGroups64 = 16;   // the same for 33..64 tokens
 constexpr int kG16CUs = 256;           // workgroups that run at once: 5 per CU for one token tile, 4 for two
 
 struct G16Args {
@@ -975,8 +976,12 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.tiles_l = rank > 0 ? g16_cdiv(rank, 16) : 0;
   p.rank_pad = rank > 0 ? (int)(g16_cdiv(rank, 32) * 32) : 0;
   // LoRA items: four chunks per wave pass, as many passes as keep the partials to about
-  // kG16LoraGroups K groups (their sum is on the path to t)
-  p.lc = kG16Waves * (int)g16_cdiv(p.kchunks, (int64_t)kG16Waves * kG16LoraGroups);
+  // 32 K groups (16 for more than 32 tokens, whose items cost more per chunk).  The item
+  // chain ends in t, which every finishing row tile waits for: at K = 18944 and one token,
+  // 32 groups take the call from 18.1 to 16.3 us against 8 groups; at 64 tokens 32 groups
+  // cost more than they save.
+  const int lgroups_max = m <= 32 ? kG16LoraGroupsFew : kG16LoraGroups64;
+  p.lc = kG16Waves * (int)g16_cdiv(p.kchunks, (int64_t)kG16Waves * lgroups_max);
   p.lgroups = rank > 0 ? g16_cdiv(p.kchunks, p.lc) : 0;
   if (m > 32) {
     p.mt = 4;
