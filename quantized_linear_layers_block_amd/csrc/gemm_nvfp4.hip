@@ -340,10 +340,14 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
   }
 }
 
-// nv_finish_kernel: one row per wave.  Row maximum over the splits -> e putting it in
-// [2^14, 2^15) (zero, Inf and NaN rows keep e = 0), rs[row] = 2^-e, the row as f16
-// scaled by 2^e, and t[row] = bf16(lora_scale * sum over splits of t_part) for ranks
-// below `rank`, zero up to rank_pad.
+// nv_finish_kernel: one (row, chunk) unit per wave, chunk c covering the row's 16-byte
+// units 256 c .. +256 (four per lane, so a K = 5120 row takes three waves).  Row maximum
+// over the splits -> e putting it in [2^14, 2^15) (zero, Inf and NaN rows keep e = 0),
+// the chunk as f16 scaled by 2^e; chunk 0 also writes rs[row] = 2^-e and t[row] =
+// bf16(lora_scale * sum over splits of t_part) for ranks below `rank`, zero up to
+// rank_pad.  The split maxima and the chunk are loaded together: one round trip to
+// memory before the conversion instead of one per step of a whole row.
+constexpr int64_t kNvChunk8 = 256;  // 16-byte units per wave
 __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                         int64_t splits, const uint32_t* __restrict__ amax_part,
                                                         const float* __restrict__ t_part, int32_t rank,
@@ -351,8 +355,20 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ x16, float* __restrict__ rs,
                                                         uint16_t* __restrict__ t) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n8 = k / 8;  // k % 64 == 0: a multiple of 8
+  const int64_t chunks = (n8 + kNvChunk8 - 1) / kNvChunk8;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = unit / chunks, chunk = unit % chunks;
   if (row >= m) return;
+  const uint4* src = (const uint4*)(x + row * k);
+  uint4* dst = (uint4*)(x16 + row * k);
+  const int64_t c0 = chunk * kNvChunk8 + lane;
+  uint4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t c = c0 + 64 * u;
+    v[u] = c < n8 ? src[c] : make_uint4(0, 0, 0, 0);
+  }
   uint32_t mx = 0;
   for (int64_t sp = lane; sp < splits; sp += 64) mx = max(mx, amax_part[sp * m + row]);
 #pragma unroll
@@ -360,6 +376,23 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
   const int be = (int)(mx >> 7);  // bf16 biased exponent of the row maximum
   int e = (mx == 0 || be == 0xFF) ? 0 : 141 - (be > 0 ? be : 1);
   e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  const float up = __uint_as_float((uint32_t)(e + 127) << 23);
+  auto conv = [&](const uint4 w4) {
+    const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float a0 = __uint_as_float(w[e2] << 16) * up, a1 = __uint_as_float(w[e2] & 0xFFFF0000u) * up;
+      o[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a0, a1}, f16x2));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t c = c0 + 64 * u;
+    if (c < n8) dst[c] = conv(v[u]);
+  }
+  if (chunk != 0) return;
   if (lane == 0) rs[row] = __uint_as_float((uint32_t)(127 - e) << 23);
   for (int j = lane; j < rank_pad; j += 64) {
     // fixed order: eight interleaved partial sums (split sp goes to sum sp % 8), then those
@@ -376,29 +409,6 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
     for (int u = 1; u < 8; ++u) sum += acc8[u];
     t[row * rank_pad + j] = (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
   }
-  const float up = __uint_as_float((uint32_t)(e + 127) << 23);
-  const uint4* src = (const uint4*)(x + row * k);
-  uint4* dst = (uint4*)(x16 + row * k);
-  const int64_t n8 = k / 8;  // k % 64 == 0: a multiple of 8
-  auto conv = [&](const uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float a0 = __uint_as_float(w[e2] << 16) * up, a1 = __uint_as_float(w[e2] & 0xFFFF0000u) * up;
-      o[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a0, a1}, f16x2));
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-  };
-  int64_t c = lane;
-  for (; c + 192 < n8; c += 256) {  // four independent loads in flight per lane
-    const uint4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
-    dst[c] = conv(v0);
-    dst[c + 64] = conv(v1);
-    dst[c + 128] = conv(v2);
-    dst[c + 192] = conv(v3);
-  }
-  for (; c < n8; c += 64) dst[c] = conv(src[c]);
 }
 
 template <int OUT_F32>
@@ -732,8 +742,9 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
     case 8: nv_stats_kernel<8><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
     default: return hipErrorInvalidValue;
   }
-  nv_finish_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank, rank_pad,
-                                                            lora_scale, w.x16, w.rs, w.t);
+  const int64_t fin_units = m * ((k / 8 + kNvChunk8 - 1) / kNvChunk8);
+  nv_finish_kernel<<<(unsigned)((fin_units + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank,
+                                                                    rank_pad, lora_scale, w.x16, w.rs, w.t);
   uint16_t* x16 = w.x16;
   float* rs = w.rs;
   uint16_t* t = rank > 0 ? w.t : nullptr;
