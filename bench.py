@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27843543, "fetch_bytes": 26550173, "write_bytes": 1293370,
+DECODE_TRAFFIC = {"bytes_per_launch": 27860981, "fetch_bytes": 26567615, "write_bytes": 1293365,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "89ce434b6ec795604f4972e7c946f18f91baf41def9d2362bf86c3d8743c9e4c"}
+                  "sources_sha256": "0cd737143e3cc52fc5925b4e6ab26e7fa8776e45a06af2af3f92d7fe78f06454"}
 
 
 def decode_traffic():

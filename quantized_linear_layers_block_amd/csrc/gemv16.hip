@@ -135,8 +135,8 @@ __device__ __forceinline__ uint4 ld16_or0(const void* p, bool ok, const void* du
 // whole 64-byte runs per group of four lanes (lane l: row l / 4, chunk bytes 16 (l % 4) and
 // 64 + 16 (l % 4), scale bytes 4 (l % 4)), which streams markedly faster than lanes of one
 // quad reading four different rows; g16_transpose then moves the data into the MFMA operand
-// layout.  Rows past N and chunks past the range load from row 0 / column 0 and are masked
-// to zero.
+// layout.  Rows past N and chunks past the range load from row 0 / column 0; for K not a
+// multiple of 256 those loads and the blocks past K are masked to zero.
 template <bool ALIGNED>
 __device__ __forceinline__ G16Chunk g16_issue(const G16Args& a, int64_t row0, bool ok, int64_t kl) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -148,12 +148,11 @@ __device__ __forceinline__ G16Chunk g16_issue(const G16Args& a, int64_t row0, bo
   const uint8_t* sp = a.scales + rr * (a.k / 16) + kc / 16 + 4 * q;
   G16Chunk cr;
   if (ALIGNED) {  // K % 256 == 0: whole chunks, naturally aligned 16- and 4-byte loads
-    const uint4 c0 = *(const uint4*)cp, c1 = *(const uint4*)(cp + 64);
-    const uint32_t sc = *(const uint32_t*)sp;
-    const uint32_t m = opaque_mask(ok);
-    cr.c0 = mask4(c0, m);
-    cr.c1 = mask4(c1, m);
-    cr.s = sc & m;
+    // Nothing to mask: a chunk past the range is never multiplied, and a row past N only
+    // feeds outputs that are never stored (it reads row 0).
+    cr.c0 = *(const uint4*)cp;
+    cr.c1 = *(const uint4*)(cp + 64);
+    cr.s = *(const uint32_t*)sp;
   } else {        // K % 16 == 0: whole 16-element blocks, 8-byte code loads, byte scales
     // chunk byte 64 j + 16 q + 8 h holds block 8 j + 2 q + h; scale byte b is block 4 q + b
     uint32_t cw[8], sb[4];
@@ -242,34 +241,48 @@ __device__ __forceinline__ void g16_x_store(const G16Args& a, uint16_t* xs, int 
   }
 }
 
-// B operand: 8 activations of token 16 q + r at LDS column `col`.
-__device__ __forceinline__ bf16x8 g16_xfrag(const G16Args& a, const uint16_t* xs, int mrows, int q,
-                                            int col) {
-  const int r = threadIdx.x & 15;
-  const int mi = 16 * q + r;
-  if (mi >= mrows) return gv_zero8();
-  return __builtin_bit_cast(bf16x8, *(const uint4*)(xs + mi * a.xstride + col));
-}
+// LDS elements after the staged activation rows that read as zero: the B fragments of
+// tokens past M come from there (offsets up to 128 + 24 + 8 elements), so that every
+// fragment read is one unconditional LDS load at an immediate offset from a per-chunk base.
+constexpr int kG16ZeroElems = 160;
 
 // One 256-wide chunk of RT row tiles: 8 K steps of 32, each MFMA'd against MT token tiles.
 template <int MT, int RT>
 __device__ __forceinline__ void g16_mul_chunk(const G16Args& a, const uint16_t* xs, int mrows,
                                               int col0, const G16Chunk (&cr)[RT], f32x4 (&acc)[RT][MT]) {
+  const int r = threadIdx.x & 15;
   const int g = (threadIdx.x & (kWave - 1)) >> 4;
   G16Chunk ct[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) ct[rt] = g16_transpose(cr[rt]);
+  // B fragment of token 16 q + r at K step t: 8 elements at column col0 + g16_kcol(g, t)
+  const uint16_t* xb[MT];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    const int mi = 16 * q + r;
+    xb[q] = mi < mrows ? xs + mi * a.xstride + col0 + 32 * g : xs + mrows * a.xstride;
+  }
+  // block scales of K steps 2 b and 2 b + 1: byte b of s
+  float sc[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    sc[rt][0] = __builtin_amdgcn_cvt_f32_fp8((int)ct[rt].s, 0);
+    sc[rt][1] = __builtin_amdgcn_cvt_f32_fp8((int)ct[rt].s, 1);
+    sc[rt][2] = __builtin_amdgcn_cvt_f32_fp8((int)ct[rt].s, 2);
+    sc[rt][3] = __builtin_amdgcn_cvt_f32_fp8((int)ct[rt].s, 3);
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     bf16x8 xf[MT];
 #pragma unroll
-    for (int q = 0; q < MT; ++q) xf[q] = g16_xfrag(a, xs, mrows, q, col0 + g16_kcol(g, t));
+    for (int q = 0; q < MT; ++q)
+      xf[q] = __builtin_bit_cast(bf16x8, *(const uint4*)(xb[q] + 128 * (t >> 2) + 8 * (t & 3)));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const G16Chunk& c = ct[rt];
       const uint32_t w = t == 0 ? c.c0.x : t == 1 ? c.c0.y : t == 2 ? c.c0.z : t == 3 ? c.c0.w :
                          t == 4 ? c.c1.x : t == 5 ? c.c1.y : t == 6 ? c.c1.z : c.c1.w;
-      const bf16x8 av = gv_dequant8(w, e4m3_value((c.s >> (8 * (t >> 1))) & 0xFFu));
+      const bf16x8 av = gv_dequant8(w, sc[rt][t >> 1]);
 #pragma unroll
       for (int q = 0; q < MT; ++q)
         acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xf[q], acc[rt][q], 0, 0, 0);
@@ -883,6 +896,8 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   }
   const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);
   g16_x_store<XU>(a, xs, per_row, mrows * per_row, xv);
+  if (threadIdx.x < kG16ZeroElems / 8)  // the zero fragments of tokens past M
+    *(uint4*)(xs + mrows * a.xstride + 8 * threadIdx.x) = make_uint4(0, 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int p = kEarly; p < kG16Pairs; ++p) {
@@ -1041,7 +1056,7 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.n_pad = p.tiles_w * 16 * p.rt;
   const int64_t xcols = p.cps * kG16Chunk;
   p.xstride = (int)(xcols + 8);
-  p.lds_bytes = (size_t)m * (size_t)p.xstride * 2;
+  p.lds_bytes = (size_t)m * (size_t)p.xstride * 2 + kG16ZeroElems * 2;
   const size_t red_bytes = (size_t)kG16Waves * p.rt * p.mt * kWave * 16;  // the wave reduction reuses it
   if (p.lds_bytes < red_bytes) p.lds_bytes = red_bytes;
   return p;
