@@ -71,6 +71,9 @@ def test_nvfp4_decode_config2_full_size(shape_idx, m):
 
 @pytest.mark.parametrize("m,n,k,r", [(1, 16, 16, 0), (3, 200, 272, 8), (5, 130, 1040, 40), (17, 64, 4096, 16),
                                      (40, 300, 784, 32), (64, 96, 8192, 128), (2, 4096, 512, 0),
+                                     # up to 32 tokens, K % 256 == 0 and N % 16 != 0: the rows past N
+                                     # of the last row tile read row 0 unmasked and must not be stored
+                                     (1, 1000, 1024, 8), (8, 100, 2048, 0), (20, 50, 512, 16),
                                      # 33..64 tokens with K % 128 == 0: one stage, K % 256 != 0,
                                      # several K splits, ragged N, rank not a multiple of 8
                                      (64, 72, 128, 0), (33, 200, 1152, 8), (48, 1000, 2048, 32),
