@@ -151,8 +151,10 @@ size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
  * Needs a workspace of qlinear_forward_workspace(format, m, n, k, rank) bytes.  The
  * workspace must be zero-filled before its FIRST use: the few-token NVFP4 path (m <= 64)
  * and the LoRA down-projection coordinate their workgroups through integer counters kept
- * in it, and every call leaves those counters zero again.  Calls that share a workspace
- * must not overlap (same stream, or ordered by events).
+ * in it, and every such call leaves those counters zero again.  Calls with m > 64 and FP8
+ * calls use the workspace as scratch and leave it non-zero: a workspace they used must be
+ * zero-filled again before a few-token NVFP4 call (m <= 64) uses it.  Calls that share a
+ * workspace must not overlap (same stream, or ordered by events).
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE (m<=0, m > QLINEAR_MAX_M, sizes vs format),
  * QL_ERR_ARG (rank < 0 or > QLINEAR_MAX_RANK), QL_ERR_FORMAT, QL_ERR_ALIGN,
  * QL_ERR_WORKSPACE. */
