@@ -110,6 +110,22 @@ def test_nvfp4_prefill_config3_full_size_sampled(shape_idx):
     _nvfp4_case(w, x, a, b, synth.CFG3["lora_scale"], rows_m=rows_m, rows_n=rows_n)
 
 
+@pytest.mark.parametrize("li", [1, 3, 6])  # k 5120->1024, o 8192->5120, down 27648->5120
+def test_nvfp4_policy_decode_m256_full_size_sampled(li):
+    # one linear of the whole-policy decode step at its real size: 256 tokens, LoRA r32
+    name, k, n = synth.CFG5_LINEARS[li]
+    c = synth.CFG5
+    print(f"forward config5 {name} K={k} N={n} M={c['M']}", flush=True)
+    g = np.random.default_rng(5000 + li)
+    w = synth.normal_bf16((n, k), c["w_std"], g, c["w_out"], c["w_mult"])
+    x = synth.normal_bf16((c["M"], k), 1.0, g)
+    a = synth.normal_bf16((c["rank"], k), 0.01, g)
+    b = synth.normal_bf16((n, c["rank"]), 0.01, g)
+    rows_m = np.unique(np.concatenate([np.arange(0, c["M"], 3), [c["M"] - 1]]))
+    rows_n = np.unique(np.concatenate([np.arange(0, n, max(1, n // 257)), [n - 1]]))
+    _nvfp4_case(w, x, a, b, c["lora_scale"], rows_m=rows_m, rows_n=rows_n)
+
+
 def test_nvfp4_lora_off_equals_base():
     g = np.random.default_rng(3)
     w = to_dev(synth.normal_bf16((256, 512), 0.02, g))
