@@ -304,8 +304,7 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
 #pragma unroll
   for (int i = 0; i < RT; ++i) acc[i] = f32x4{0, 0, 0, 0};
   uint32_t mx = 0;
-  auto step = [&](int64_t kk) {
-    const i32x4 xv = *(const i32x4*)(xr + kk);
+  auto use = [&](const i32x4& xv, const i32x4 (&av)[RT > 0 ? RT : 1]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t w = (uint32_t)xv[e];
@@ -315,20 +314,32 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      i32x4 av = *(const i32x4*)(ar[i] + kk);
-      if (!aok[i]) av = i32x4{0, 0, 0, 0};
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+      const i32x4 a = aok[i] ? av[i] : i32x4{0, 0, 0, 0};
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, xv), acc[i], 0, 0, 0);
     }
   };
+  // four 32-wide steps per batch, all of their loads issued before any is used (used one by
+  // one they would cost a memory round trip each)
   int64_t kk = k0;
   for (; kk + 96 < k1; kk += 128) {
-    step(kk);
-    step(kk + 32);
-    step(kk + 64);
-    step(kk + 96);
+    i32x4 xq[4], aq[4][RT > 0 ? RT : 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xq[u] = *(const i32x4*)(xr + kk + 32 * u);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) aq[u][i] = *(const i32x4*)(ar[i] + kk + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) use(xq[u], aq[u]);
   }
-  for (; kk < k1; kk += 32) step(kk);
+  for (; kk < k1; kk += 32) {
+    i32x4 aq[RT > 0 ? RT : 1];
+    const i32x4 xq = *(const i32x4*)(xr + kk);
+#pragma unroll
+    for (int i = 0; i < RT; ++i) aq[i] = *(const i32x4*)(ar[i] + kk);
+    use(xq, aq);
+  }
   mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
   mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
   if (row < m) {
