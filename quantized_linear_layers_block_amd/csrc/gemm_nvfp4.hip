@@ -278,55 +278,71 @@ struct Nvfp4F16Args {
 // accumulates x A^T over RT 16-row tiles of A with bf16 MFMAs (A rows past the rank
 // read as zero) into t_part[split][row][16 RT].  Workgroups of one split are adjacent
 // so that they share the same range of A in L2.
-template <int RT>
+template <int RT, int MF>
 __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                        const uint16_t* __restrict__ lora_a, int32_t rank,
                                                        int64_t tiles, int64_t kchunk,
                                                        uint32_t* __restrict__ amax_part,
                                                        float* __restrict__ t_part) {
+  constexpr int RA = RT > 0 ? RT : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t split = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int64_t row = tile * 64 + 16 * wave + r;
-  const int64_t rowc = row < m ? row : m - 1;
   const int64_t k0 = split * kchunk;
   const int64_t k1 = k0 + kchunk < k ? k0 + kchunk : k;
-  const uint16_t* xr = x + rowc * k + 8 * g;
-  const uint16_t* ar[RT > 0 ? RT : 1];
-  bool aok[RT > 0 ? RT : 1];
+  int64_t row[MF];
+  const uint16_t* xr[MF];
+#pragma unroll
+  for (int h = 0; h < MF; ++h) {
+    row[h] = tile * (64 * MF) + 16 * (MF * wave + h) + r;
+    xr[h] = x + (row[h] < m ? row[h] : m - 1) * k + 8 * g;
+  }
+  const uint16_t* ar[RA];
+  bool aok[RA];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
     const int j = 16 * i + r;
     aok[i] = j < rank;
     ar[i] = lora_a + (int64_t)(aok[i] ? j : 0) * k + 8 * g;
   }
-  f32x4 acc[RT > 0 ? RT : 1];
+  f32x4 acc[MF][RA];
+  uint32_t mx[MF];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) acc[i] = f32x4{0, 0, 0, 0};
-  uint32_t mx = 0;
-  auto use = [&](const i32x4& xv, const i32x4 (&av)[RT > 0 ? RT : 1]) {
+  for (int h = 0; h < MF; ++h) {
+    mx[h] = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = (uint32_t)xv[e];
-      const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-      mx = mx > lo ? mx : lo;
-      mx = mx > hi ? mx : hi;
+    for (int i = 0; i < RT; ++i) acc[h][i] = f32x4{0, 0, 0, 0};
+  }
+  // one 32-wide step: each A fragment serves the MF row fragments of the wave
+  auto use = [&](const i32x4 (&xv)[MF], const i32x4 (&av)[RA]) {
+#pragma unroll
+    for (int h = 0; h < MF; ++h) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = (uint32_t)xv[h][e];
+        const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+        mx[h] = mx[h] > lo ? mx[h] : lo;
+        mx[h] = mx[h] > hi ? mx[h] : hi;
+      }
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       const i32x4 a = aok[i] ? av[i] : i32x4{0, 0, 0, 0};
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, xv), acc[i], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < MF; ++h)
+        acc[h][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, xv[h]), acc[h][i], 0, 0, 0);
     }
   };
   // four 32-wide steps per batch, all of their loads issued before any is used (used one by
   // one they would cost a memory round trip each)
   int64_t kk = k0;
   for (; kk + 96 < k1; kk += 128) {
-    i32x4 xq[4], aq[4][RT > 0 ? RT : 1];
+    i32x4 xq[4][MF], aq[4][RA];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      xq[u] = *(const i32x4*)(xr + kk + 32 * u);
+#pragma unroll
+      for (int h = 0; h < MF; ++h) xq[u][h] = *(const i32x4*)(xr[h] + kk + 32 * u);
 #pragma unroll
       for (int i = 0; i < RT; ++i) aq[u][i] = *(const i32x4*)(ar[i] + kk + 32 * u);
     }
@@ -334,20 +350,25 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
     for (int u = 0; u < 4; ++u) use(xq[u], aq[u]);
   }
   for (; kk < k1; kk += 32) {
-    i32x4 aq[RT > 0 ? RT : 1];
-    const i32x4 xq = *(const i32x4*)(xr + kk);
+    i32x4 xq[MF], aq[RA];
+#pragma unroll
+    for (int h = 0; h < MF; ++h) xq[h] = *(const i32x4*)(xr[h] + kk);
 #pragma unroll
     for (int i = 0; i < RT; ++i) aq[i] = *(const i32x4*)(ar[i] + kk);
     use(xq, aq);
   }
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-  if (row < m) {
-    if (g == 0) amax_part[split * m + row] = mx;
-    // lane (r, g) of tile i holds rank 16 i + 4 g + (0..3) of row r
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
-      *(f32x4*)(t_part + (split * m + row) * (16 * RT) + 16 * i + 4 * g) = acc[i];
+  for (int h = 0; h < MF; ++h) {
+    uint32_t v = mx[h];
+    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    if (row[h] < m) {
+      if (g == 0) amax_part[split * m + row[h]] = v;
+      // lane (r, g) of tile i holds rank 16 i + 4 g + (0..3) of row r
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        *(f32x4*)(t_part + (split * m + row[h]) * (16 * RT) + 16 * i + 4 * g) = acc[h][i];
+    }
   }
 }
 
@@ -662,6 +683,7 @@ int32_t nv_rank_pad(int32_t rank) { return rank > 0 ? (rank + 31) / 32 * 32 : 0;
 
 // Pre-pass splits along K: about four (tile, split) workgroups per compute unit, so that
 // enough loads are in flight, with at least 256 k per split.
+constexpr int64_t kNvStatsWideRows = 1024;  // from this many rows on, two row fragments per wave
 int64_t nv_prep_splits(int64_t m, int64_t k) {
   const int64_t tiles = (m + 63) / 64;
   int64_t sp = (1024 + tiles - 1) / tiles;
@@ -742,15 +764,26 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
     return hipErrorInvalidValue;
   const int32_t rank_pad = nv_rank_pad(rank);
   const NvPrepWs w = nv_prep_ws(ws, m, n, k, rank);
-  const int64_t tiles = (m + 63) / 64, sp = nv_prep_splits(m, k);
+  // Large m: 128 rows per workgroup, so each load of A serves two row fragments (the split
+  // count, and with it the workspace, is that of 64-row tiles either way).
+  const int mf = m >= kNvStatsWideRows ? 2 : 1;
+  const int64_t tiles = (m + 64 * mf - 1) / (64 * mf), sp = nv_prep_splits(m, k);
   const int64_t kchunk = ((k + sp - 1) / sp + 31) / 32 * 32;
   const unsigned sgrid = (unsigned)(tiles * sp);
+#define QL_NV_STATS(RT_)                                                                               \
+  case RT_ / 16:                                                                                      \
+    if (mf == 2)                                                                                      \
+      nv_stats_kernel<RT_ / 16, 2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); \
+    else                                                                                              \
+      nv_stats_kernel<RT_ / 16, 1><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); \
+    break;
   switch (rank_pad / 16) {
-    case 0: nv_stats_kernel<0><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
-    case 2: nv_stats_kernel<2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
-    case 4: nv_stats_kernel<4><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
-    case 6: nv_stats_kernel<6><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
-    case 8: nv_stats_kernel<8><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); break;
+    QL_NV_STATS(0)
+    QL_NV_STATS(32)
+    QL_NV_STATS(64)
+    QL_NV_STATS(96)
+    QL_NV_STATS(128)
+#undef QL_NV_STATS
     default: return hipErrorInvalidValue;
   }
   const int64_t fin_units = m * ((k / 8 + kNvChunk8 - 1) / kNvChunk8);

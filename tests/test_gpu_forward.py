@@ -87,7 +87,8 @@ def test_nvfp4_skinny_ragged(m, n, k, r):
     _nvfp4_case(w, x, a, b, 2.0 if r else 0.0)
 
 
-@pytest.mark.parametrize("m,n,k,r", [(65, 130, 272, 8), (300, 512, 1040, 40), (256, 256, 512, 0), (257, 1024, 4096, 64)])
+@pytest.mark.parametrize("m,n,k,r", [(65, 130, 272, 8), (300, 512, 1040, 40), (256, 256, 512, 0), (257, 1024, 4096, 64),
+                                       (1100, 512, 2048, 48)])
 def test_nvfp4_gemm_ragged(m, n, k, r):
     g = np.random.default_rng(m * 1000 + n + k)
     w = synth.normal_bf16((n, k), 0.02, g, 0.01, 15.0)
