@@ -427,7 +427,9 @@ def run_rows(rows, torch, ql, dev):
                 y = torch.empty((m, n), dtype=bf, device=dev)
                 ws = torch.zeros(ql.binding.qlinear_forward_workspace(ql.QL_FP8_BLOCK128, m, n, k, 0) + 16,
                                  dtype=torch.uint8, device=dev)
-                ms = _events_ms(torch, lambda: ql.forward_fp8_prequant(q, xq, sx, out=y), 10)
+                wsp = torch.zeros(ql.binding.qlinear_forward_prequant_workspace(m, n, k, 0), dtype=torch.uint8,
+                                  device=dev)
+                ms = _events_ms(torch, lambda: ql.forward_fp8_prequant(q, xq, sx, out=y, ws=wsp), 10)
                 r = _row("mfma", 2.0 * m * n * k, ms, FP8_PEAK, "flop")
                 ms_e2e = _events_ms(torch, lambda: ql.forward(q, x, out=y, ws=ws), 10)
                 r.update({"M": m, "K": k, "N": n, "e2e_us_with_act_quant": round(ms_e2e * 1e3, 2),

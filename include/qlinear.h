@@ -98,13 +98,29 @@ typedef struct {
 #define QLINEAR_MAX_RANK 128
 /* Largest token count accepted by qlinear_forward. */
 #define QLINEAR_MAX_M (((int64_t)1) << 24)
+/* Most tensors one qlinear_requantize_all call takes. */
+#define QLINEAR_MAX_REQUANT_ITEMS 65536
+
+/* Bits the kernels OR into a workspace's status word (never cleared by the library). */
+#define QLINEAR_STATUS_NONFINITE 1 /* a weight input held Inf or NaN (requantization)        */
+#define QLINEAR_STATUS_TIMEOUT 2   /* a bounded wait for another workgroup gave up; the
+                                      outputs that depended on it were stored as NaN        */
+#define QLINEAR_STATUS_BAD_ITEM 4  /* a requantization item failed its checks and was skipped */
 
 /* Human-readable name of a status code (static storage). */
 const char* qlinear_status_string(qlinear_status s);
 
+/* Device address of the status word of a forward or requantization workspace: its first
+ * int32 (host-side pointer arithmetic only; nothing is launched).  Kernels OR the
+ * QLINEAR_STATUS_* bits into it; read it after the stream has reached the call. */
+int32_t* qlinear_status_word(void* ws);
+
 /* ---------------------------------------------------------------- quantizers */
 
-/* NVFP4 weight quantizer.  W bf16 [n][k] -> codes u8 [n][k/2], scales u8 [n][k/16],
+/* NVFP4 weight quantizer (QeRL's weight format: tldrocket.com QeRL page, "Key Features of
+ * QeRL"; public NVFP4 definition: E2M1 elements, 16-element blocks along K, E4M3 block
+ * scales, an FP32 tensor scale; arithmetic as in the contract at the top of this file).
+ * W bf16 [n][k] -> codes u8 [n][k/2] (even k in the low nibble), scales u8 [n][k/16],
  * tensor_scale f32[1].  Needs a workspace of qlinear_quantize_workspace(QL_NVFP4, n, k)
  * bytes (per-workgroup partial maxima; its contents need no initialisation).
  * Two kernels: a tensor-wide |w| maximum, then the block/element encoder.
@@ -115,17 +131,20 @@ qlinear_status qlinear_quantize_nvfp4(const uint16_t* w, int64_t n, int64_t k,
                                       int32_t* status_word, void* ws, size_t ws_bytes,
                                       void* stream);
 
-/* Blockwise FP8 weight quantizer.  W bf16 [n][k] -> codes u8 [n][k] (E4M3),
- * scales f32 [n/128][k/128].  One workgroup per 128x128 tile, no workspace.
+/* Blockwise FP8 weight quantizer (mexc.co NeMo RL FP8 page, "De technische doorbraak":
+ * E4M3, one scale per 128x128 weight tile).  W bf16 [n][k] -> codes u8 [n][k] (E4M3),
+ * scales f32 [n/128][k/128] (dequantization multipliers amax/448).  One workgroup per
+ * 128x128 tile, no workspace.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE (n%128, k%128, n*k too big), QL_ERR_ALIGN. */
 qlinear_status qlinear_quantize_fp8_block(const uint16_t* w, int64_t n, int64_t k,
                                           uint8_t* codes, float* scales,
                                           int32_t* status_word, void* stream);
 
-/* Dynamic 1x128 FP8 activation quantizer (the step qlinear_forward runs on bf16
- * activations in the FP8 format; exported so callers can quantize one activation
- * tensor once and feed several projections).  x bf16 [m][k] -> xq u8 [m][k],
- * sx f32 [m][k/128].  Errors: QL_ERR_NULL, QL_ERR_SHAPE (k%128), QL_ERR_ALIGN. */
+/* Dynamic 1x128 FP8 activation quantizer (same page and section: one scale per 1x128
+ * activation segment), the step qlinear_forward runs on bf16 activations in the FP8
+ * format; exported so callers can quantize one activation tensor once and feed several
+ * projections.  x bf16 [m][k] -> xq u8 [m][k], sx f32 [m][k/128].
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (k%128), QL_ERR_ALIGN. */
 qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
                                         uint8_t* xq, float* sx, void* stream);
 
@@ -134,12 +153,16 @@ size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
 
 /* ------------------------------------------------------------------- forward */
 
-/* The layer:  y[m][n] = sum_k x[m][k] w_hat[n][k]  +  lora_scale * sum_j t[m][j] B[n][j],
+/* The rollout linear layer (QeRL: NVFP4 weight path plus a LoRA adapter kept in higher
+ * precision, tldrocket.com QeRL page, "Key Features of QeRL" and the paragraph after it,
+ * which puts the speedup in rollout prefill and decoding; the FP8 format follows the
+ * mexc.co NeMo RL FP8 page, "De technische doorbraak"):
+ *             y[m][n] = sum_k x[m][k] w_hat[n][k]  +  lora_scale * sum_j t[m][j] B[n][j],
  *             t[m][j] = sum_k x[m][k] A[j][k].
  * w (host struct): a quantized weight from the quantizers above.
- * x bf16 [m][k].  lora_a bf16 [rank][k], lora_b bf16 [n][rank]; rank == 0 or NULL
- * adapters mean no LoRA term.  y: bf16 [m][n] (QL_OUT_BF16, rounded to nearest even
- * from the float32 result) or f32 [m][n] (QL_OUT_F32).  Accumulation is float32.
+ * x bf16 [m][k].  lora_a bf16 [rank][k], lora_b bf16 [n][rank]; rank == 0, NULL adapters
+ * or lora_scale == 0 mean no LoRA term.  y: bf16 [m][n] (QL_OUT_BF16, rounded to nearest
+ * even from the float32 result) or f32 [m][n] (QL_OUT_F32).  Accumulation is float32.
  * NVFP4: the dequantized weights (E2M1 x E4M3 products, exact in bf16 and in f16)
  * meet the activations in MFMA; S is applied in float32 after the K loop.  For m > 64
  * and k % 64 == 0 the activations are first copied into the workspace as f16, each row
@@ -148,26 +171,34 @@ size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
  * FP8: x is quantized per 1x128 segment into the workspace, then an FP8 MFMA GEMM
  * rescales each 128-deep partial sum by sx * sw.
  * The LoRA intermediate s*t is rounded to bf16 before the up-projection.
- * Needs a workspace of qlinear_forward_workspace(format, m, n, k, rank) bytes.  The
- * workspace must be zero-filled before its FIRST use: the few-token NVFP4 path (m <= 64)
- * and the LoRA down-projection coordinate their workgroups through integer counters kept
- * in it, and every such call leaves those counters zero again.  Calls with m > 64 and FP8
- * calls use the workspace as scratch and leave it non-zero: a workspace they used must be
- * zero-filled again before a few-token NVFP4 call (m <= 64) uses it.  Calls that share a
- * workspace must not overlap (same stream, or ordered by events).
- * Errors: QL_ERR_NULL, QL_ERR_SHAPE (m<=0, m > QLINEAR_MAX_M, sizes vs format),
- * QL_ERR_ARG (rank < 0 or > QLINEAR_MAX_RANK), QL_ERR_FORMAT, QL_ERR_ALIGN,
- * QL_ERR_WORKSPACE. */
+ *
+ * Workspace: qlinear_forward_workspace(format, m, n, k, rank) bytes, 16-byte aligned,
+ * owned by the caller.  Its first QLINEAR_WS_RESERVED_BYTES hold the status word and the
+ * integer counters through which the workgroups of one launch coordinate; they must be
+ * zero before the first call, and every call returns the counters it used to zero.  No
+ * call uses that region as scratch, and everything after it is scratch that a call writes
+ * before reading.  So one zero-filled workspace, as large as the largest query, may serve
+ * calls of every shape, format and path in any order.  Calls that share a workspace must
+ * not overlap (same stream, or ordered by events).  The few-token NVFP4 path (m <= 64)
+ * waits for its LoRA intermediate with a bound in time; if the bound is reached (never in
+ * a launch whose workgroups all make progress) the affected outputs are NaN and
+ * QLINEAR_STATUS_TIMEOUT is set in the status word.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (m<=0, m > QLINEAR_MAX_M, sizes vs format, or a shape
+ * the kernels cannot run: FP8 k >= 2^24, few-token NVFP4 counters or partials beyond the
+ * workspace's reach -- the size query returns 0 for those), QL_ERR_ARG (rank < 0 or >
+ * QLINEAR_MAX_RANK), QL_ERR_FORMAT, QL_ERR_ALIGN, QL_ERR_WORKSPACE. */
+#define QLINEAR_WS_RESERVED_BYTES 131072
 qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int64_t m,
                                const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
                                float lora_scale, void* y, int32_t out_dtype,
                                void* ws, size_t ws_bytes, void* stream);
 
-/* FP8 layer on activations already quantized by qlinear_quantize_act_fp8:
- * xq u8 [m][k], sx f32 [m][k/128].  x (bf16 [m][k]) is read only for the LoRA
- * term and may be NULL when rank == 0.  Workspace: qlinear_forward_workspace with
- * format QL_FP8_BLOCK128 minus the activation buffers, i.e.
- * qlinear_forward_prequant_workspace(m, n, k, rank).  Errors as qlinear_forward. */
+/* FP8 layer on activations already quantized by qlinear_quantize_act_fp8 (the FP8 GEMM
+ * of the recipe, same page and section, without the activation step): xq u8 [m][k],
+ * sx f32 [m][k/128].  x (bf16 [m][k]) is read only for the LoRA term and may be NULL
+ * when there is none.  Workspace: qlinear_forward_prequant_workspace(m, n, k, rank)
+ * bytes, with the same layout and rules as qlinear_forward's.  Errors as
+ * qlinear_forward, plus QL_ERR_FORMAT if w is not QL_FP8_BLOCK128. */
 qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint8_t* xq,
                                             const float* sx, int64_t m, const uint16_t* x,
                                             const uint16_t* lora_a, const uint16_t* lora_b,
@@ -175,6 +206,7 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
                                             int32_t out_dtype, void* ws, size_t ws_bytes,
                                             void* stream);
 
+/* Workspace sizes (0 for invalid arguments and for shapes the kernels cannot run). */
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank);
 size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
 
@@ -182,34 +214,22 @@ size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32
 
 /* After every training step the RL recipe recalibrates the quantization of the
  * constantly updated policy weights (mexc.co NeMo RL FP8 page, section
- * "Praktische prestatiewinsten").  Here: re-run the per-tensor quantizer of
- * `format` on every tensor of the policy (new scales AND codes), grouped into
- * three launches (NVFP4: clear maxima, tensor maxima, encode) or one (FP8) over all
- * tensors instead of two launches per tensor.
- *
- * qlinear_requant_prepare (once, whenever the set of tensors changes): checks every
- * item of the host array `items` (count entries) like the per-tensor quantizer would,
- * writes a device table of qlinear_requant_table_bytes(count) bytes into `table`
- * (device memory owned by the caller), fills the host struct *plan, and
- * synchronises `stream` (the host array may be reused on return).
- * qlinear_requantize_all (every step): requantizes every tensor the table names.
- * The table also holds per-tensor scratch (tensor maxima), so two requantize_all
- * calls on one table must not overlap.
- * Errors: QL_ERR_NULL, QL_ERR_ARG (count <= 0 or > 65536, an item's format differs
- * from `format`, plan does not match), QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_FORMAT,
- * QL_ERR_WORKSPACE (table_bytes too small), QL_ERR_HIP (the table copy failed). */
-typedef struct {
-  int32_t count;
-  int32_t format;
-  int64_t total_units; /* workgroup-sized work units over all tensors */
-} qlinear_requant_plan;
-
-size_t qlinear_requant_table_bytes(int32_t count);
-qlinear_status qlinear_requant_prepare(const qlinear_requant_item* items, int32_t count,
-                                       int32_t format, void* table, size_t table_bytes,
-                                       qlinear_requant_plan* plan, void* stream);
-qlinear_status qlinear_requantize_all(const qlinear_requant_plan* plan, void* table,
-                                      int32_t* status_word, void* stream);
+ * "Praktische prestatiewinsten").  Here: re-run the per-tensor quantizer of `format` on
+ * every tensor of the policy (new scales AND codes), with a few launches over all tensors
+ * instead of two per tensor.
+ * items: DEVICE array of `count` entries (filled once by the caller; the same array may
+ * serve every step).  Every item must have q.format == format and pass the checks of the
+ * per-tensor quantizer; an item that does not is skipped and sets QLINEAR_STATUS_BAD_ITEM
+ * in the workspace's status word (the host never reads the array).  Non-finite weights
+ * set QLINEAR_STATUS_NONFINITE there.  ws: qlinear_requant_workspace(count) bytes,
+ * 16-byte aligned, owned by the caller; it holds the status word (zero it before the
+ * first call), the descriptor table rebuilt on the device by every call and the
+ * per-tensor maxima.  Two calls on one workspace must not overlap.
+ * Errors: QL_ERR_NULL, QL_ERR_ARG (count <= 0 or > QLINEAR_MAX_REQUANT_ITEMS),
+ * QL_ERR_FORMAT, QL_ERR_WORKSPACE, QL_ERR_ALIGN (items or ws). */
+qlinear_status qlinear_requantize_all(const qlinear_requant_item* items, int32_t count,
+                                      int32_t format, void* ws, size_t ws_bytes, void* stream);
+size_t qlinear_requant_workspace(int32_t count);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ from .binding import (QL_FP8_BLOCK128, QL_NVFP4, QL_OUT_BF16, QL_OUT_F32, Qlinea
                       make_qweight)
 
 __all__ = ["NVFP4Weight", "FP8Weight", "quantize_nvfp4", "quantize_fp8_block", "quantize_act_fp8",
-           "forward", "forward_fp8_prequant", "RequantTable", "QlinearError", "binding"]
+           "forward", "forward_fp8_prequant", "RequantTable", "QlinearError", "binding", "workspace_status"]
 
 
 def _dev(t):
@@ -68,8 +68,13 @@ def _u16(t):
 
 
 def _ws(nbytes, device):
-    # zero-filled: the library keeps workgroup counters in forward workspaces
+    # zero-filled: a workspace starts with the status word and the workgroup counters
     return torch.zeros((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+
+
+def workspace_status(ws):
+    """Status word (QLINEAR_STATUS_* bits) of a forward or requantization workspace."""
+    return int(ws[:4].view(torch.int32).item())
 
 
 def quantize_nvfp4(w, out=None, status_word=None):
@@ -132,14 +137,19 @@ def forward_fp8_prequant(qw, xq, sx, x=None, lora_a=None, lora_b=None, lora_scal
 
 
 class RequantTable:
-    """Device table for requantizing a whole policy (list of (bf16 weight, quantized weight))."""
+    """A whole policy to requantize after every training step: a list of (bf16 weight,
+    quantized weight) pairs, whose item array is copied to the device once."""
 
     def __init__(self, pairs, fmt=QL_NVFP4, device="cuda"):
         self.pairs = list(pairs)   # keep the tensors alive
         self.fmt = fmt
-        nbytes = binding.qlinear_requant_table_bytes(len(self.pairs))
-        self.table = torch.empty((nbytes,), dtype=torch.uint8, device=device)
-        self.plan = binding.qlinear_requant_prepare([(w, q.qweight()) for w, q in self.pairs], fmt, self.table)
+        img = binding.requant_items_bytes([(w, q.qweight()) for w, q in self.pairs])
+        self.items = torch.frombuffer(bytearray(img), dtype=torch.uint8).to(device)
+        self.ws = _ws(binding.qlinear_requant_workspace(len(self.pairs)), device)
 
-    def requantize_all(self, status_word=None):
-        binding.qlinear_requantize_all(self.plan, self.table, status_word)
+    def requantize_all(self):
+        binding.qlinear_requantize_all(self.items, len(self.pairs), self.fmt, self.ws)
+
+    def status(self):
+        """The workspace's status word (QLINEAR_STATUS_* bits); synchronises."""
+        return int(self.ws[:4].view(torch.int32).item())

@@ -28,10 +28,13 @@ EXPORTS = [
     "qlinear_forward_fp8_prequant",
     "qlinear_forward_workspace",
     "qlinear_forward_prequant_workspace",
-    "qlinear_requant_table_bytes",
-    "qlinear_requant_prepare",
+    "qlinear_requant_workspace",
     "qlinear_requantize_all",
+    "qlinear_status_word",
 ]
+
+QLINEAR_STATUS_NONFINITE, QLINEAR_STATUS_TIMEOUT, QLINEAR_STATUS_BAD_ITEM = 1, 2, 4
+QLINEAR_WS_RESERVED_BYTES = 131072
 
 
 class QlinearError(RuntimeError):
@@ -51,11 +54,6 @@ class RequantItem(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("q", QWeight)]
 
 
-class RequantPlan(ctypes.Structure):
-    _fields_ = [("count", ctypes.c_int32), ("format", ctypes.c_int32),
-                ("total_units", ctypes.c_int64)]
-
-
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -73,10 +71,9 @@ def _load():
                                           i32, vp, sz, vp], i32),
         "qlinear_forward_workspace": ([i32, i64, i64, i64, i32], sz),
         "qlinear_forward_prequant_workspace": ([i64, i64, i64, i32], sz),
-        "qlinear_requant_table_bytes": ([i32], sz),
-        "qlinear_requant_prepare": ([ctypes.POINTER(RequantItem), i32, i32, vp, sz,
-                                     ctypes.POINTER(RequantPlan), vp], i32),
-        "qlinear_requantize_all": ([ctypes.POINTER(RequantPlan), vp, vp, vp], i32),
+        "qlinear_requant_workspace": ([i32], sz),
+        "qlinear_requantize_all": ([vp, i32, i32, vp, sz, vp], i32),
+        "qlinear_status_word": ([vp], vp),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -172,22 +169,25 @@ def qlinear_forward_fp8_prequant(qw, xq, sx, y, out_dtype, ws=None, x=None, lora
 
 # --------------------------------------------------------------------- requant
 
-def qlinear_requant_table_bytes(count):
-    return LIB.qlinear_requant_table_bytes(count)
+def qlinear_requant_workspace(count):
+    return LIB.qlinear_requant_workspace(count)
 
 
-def qlinear_requant_prepare(items, fmt, table, stream=None):
-    """items: list of (w bf16 tensor, QWeight).  Returns the host RequantPlan."""
+def requant_items_bytes(items):
+    """items: list of (w bf16 tensor, QWeight) -> the host image of the device item array."""
     arr = (RequantItem * len(items))()
     for i, (w, qw) in enumerate(items):
         arr[i].w = _ptr(w)
         arr[i].q = qw
-    plan = RequantPlan()
-    _check(LIB.qlinear_requant_prepare(arr, len(items), fmt, _ptr(table), table.numel() * table.element_size(),
-                                       ctypes.byref(plan), _stream(stream)), "qlinear_requant_prepare")
-    return plan
+    return bytes(arr)
 
 
-def qlinear_requantize_all(plan, table, status_word=None, stream=None):
-    _check(LIB.qlinear_requantize_all(ctypes.byref(plan), _ptr(table), _ptr(status_word), _stream(stream)),
-           "qlinear_requantize_all")
+def qlinear_requantize_all(items_dev, count, fmt, ws, stream=None):
+    """items_dev: device tensor holding `count` qlinear_requant_item entries."""
+    _check(LIB.qlinear_requantize_all(_ptr(items_dev), count, fmt, _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "qlinear_requantize_all")
+
+
+def qlinear_status_word(ws):
+    """Device address of the workspace's status word (the first int32)."""
+    return LIB.qlinear_status_word(_ptr(ws))

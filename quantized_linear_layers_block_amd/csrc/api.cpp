@@ -1,24 +1,21 @@
 // C ABI of libqlinear (declared and documented in include/qlinear.h): host-side argument
 // checks, workspace carving and dispatch to the gfx950 kernels.  No device memory is
-// allocated here; every buffer, workspace and table comes from the caller.
+// allocated here; every buffer and workspace comes from the caller.  Every limit a kernel
+// has is checked here, so that a call either launches or returns an argument error
+// having enqueued nothing.
 #include "../../include/qlinear.h"
 
 #include <hip/hip_runtime.h>
-
-#include <cstring>
-#include <vector>
 
 #include "launch.hpp"
 
 namespace {
 
-using ql::SkinnyPlan;
-
 constexpr size_t kAlign = 256;
+static_assert(QLINEAR_WS_RESERVED_BYTES == ql::kWsReserved, "reserved region size");
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest token counts served by the few-token (streaming) kernels.
 constexpr int64_t kG16MaxM = 64;
@@ -48,31 +45,29 @@ int32_t lora_rank(const uint16_t* a, const uint16_t* b, int32_t rank, float scal
   return (rank > 0 && a && b && scale != 0.0f) ? rank : 0;
 }
 
-// Workspace of the LoRA down-projection for the GEMM paths (counters, t, partials).
-struct LoraWs {
-  SkinnyPlan plan;
-  size_t bytes = 0;
-  size_t total() const { return up(bytes); }
-};
-LoraWs lora_ws(int64_t m, int64_t k, int32_t rank) {
-  LoraWs w;
-  if (rank <= 0) return w;
-  w.plan = ql::plan_skinny(m, 0, k, rank);
-  w.bytes = ql::skinny_workspace(w.plan, m, k);
-  return w;
-}
-
 size_t fp8_act_bytes(int64_t m, int64_t k) { return up((size_t)m * (size_t)k) + up((size_t)m * (size_t)(k / 128) * 4); }
+
+// The NVFP4 path for m > 64: the f16 pre-pass GEMM when K allows it, else the generic one.
+bool nvfp4_f16_path(int64_t k) { return k % 64 == 0 && k < ql::kNvF16MaxK; }
 
 qlinear_status hip_status(hipError_t e) { return e == hipSuccess ? QL_OK : QL_ERR_HIP; }
 
-// LoRA intermediate t = bf16(s * x A^T) into the workspace (GEMM paths).
-qlinear_status run_lora_t(const LoraWs& lw, char* ws, const uint16_t* x, int64_t m, int64_t k,
-                          const uint16_t* lora_a, int32_t rank, float scale, uint16_t** t_out,
-                          hipStream_t s) {
-  if (ql::launch_lora_down(lw.plan, x, m, k, lora_a, rank, scale, ws, s) != hipSuccess) return QL_ERR_HIP;
-  *t_out = ql::lora_t_in_workspace(lw.plan, ws);
-  return QL_OK;
+// Scratch bytes (after the reserved region) of a forward call; SIZE_MAX when the shape is
+// beyond what the kernels can run.
+size_t forward_scratch(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank, bool prequant) {
+  if (format == QL_NVFP4) {
+    if (m <= kG16MaxM) {
+      const ql::G16Plan p = ql::plan_g16(m, n, k, rank);
+      return ql::g16_plan_ok(p, m) ? up(ql::g16_workspace(p, m)) : SIZE_MAX;
+    }
+    if (nvfp4_f16_path(k)) return up(ql::gemm_nvfp4_f16_workspace(m, n, k, rank));
+    return up(ql::lora_down_bytes(m, k, rank));
+  }
+  if (format == QL_FP8_BLOCK128) {
+    if (k >= ql::kFp8MaxK) return SIZE_MAX;
+    return (prequant ? 0 : fp8_act_bytes(m, k)) + up(ql::lora_down_bytes(m, k, rank));
+  }
+  return SIZE_MAX;
 }
 
 }  // namespace
@@ -92,6 +87,8 @@ const char* qlinear_status_string(qlinear_status s) {
   }
   return "unknown status";
 }
+
+int32_t* qlinear_status_word(void* ws) { return ql::ws_status(ws); }
 
 // ------------------------------------------------------------------ quantizers
 
@@ -137,20 +134,15 @@ qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
 // --------------------------------------------------------------------- forward
 
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank) {
-  if (m <= 0 || n <= 0 || k <= 0 || rank < 0) return 0;
-  if (format == QL_NVFP4) {
-    if (m <= kG16MaxM) return up(ql::g16_workspace(ql::plan_g16(m, n, k, rank), m));
-    if (k % 64 == 0) return up(ql::gemm_nvfp4_f16_workspace(m, n, k, rank));
-    return lora_ws(m, k, rank).total();
-  }
-  if (format == QL_FP8_BLOCK128) return fp8_act_bytes(m, k) + lora_ws(m, k, rank).total();
-  return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || rank < 0 || rank > QLINEAR_MAX_RANK) return 0;
+  const size_t s = forward_scratch(format, m, n, k, rank, false);
+  return s == SIZE_MAX ? 0 : ql::kWsReserved + s;
 }
 
 size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32_t rank) {
-  (void)n;
-  if (m <= 0 || k <= 0 || rank < 0) return 0;
-  return lora_ws(m, k, rank).total();
+  if (m <= 0 || n <= 0 || k <= 0 || rank < 0 || rank > QLINEAR_MAX_RANK) return 0;
+  const size_t s = forward_scratch(QL_FP8_BLOCK128, m, n, k, rank, true);
+  return s == SIZE_MAX ? 0 : ql::kWsReserved + s;
 }
 
 static qlinear_status check_forward_common(const qlinear_qweight* w, int64_t m,
@@ -166,6 +158,17 @@ static qlinear_status check_forward_common(const qlinear_qweight* w, int64_t m,
   return QL_OK;
 }
 
+// Workspace check shared by both forward entry points: present, large enough, aligned, and
+// the shape within what the kernels run.
+static qlinear_status check_forward_ws(const qlinear_qweight* w, int64_t m, int32_t r, bool prequant,
+                                       void* ws, size_t ws_bytes) {
+  const size_t s = forward_scratch(w->format, m, w->n, w->k, r, prequant);
+  if (s == SIZE_MAX) return QL_ERR_SHAPE;
+  if (!ws || ws_bytes < ql::kWsReserved + s) return QL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QL_ERR_ALIGN;
+  return QL_OK;
+}
+
 qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int64_t m,
                                const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
                                float lora_scale, void* y, int32_t out_dtype, void* ws,
@@ -175,12 +178,11 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
   if (!x) return QL_ERR_NULL;
   if (!aligned16(x)) return QL_ERR_ALIGN;
   const int32_t r = lora_rank(lora_a, lora_b, rank, lora_scale);
-  const size_t need = qlinear_forward_workspace(w->format, m, w->n, w->k, r);
-  if (need > 0 && (!ws || ws_bytes < need)) return QL_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(ws)) return QL_ERR_ALIGN;
+  st = check_forward_ws(w, m, r, false, ws, ws_bytes);
+  if (st != QL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int out_f32 = out_dtype == QL_OUT_F32;
-  char* wsb = (char*)ws;
+  char* scratch = ql::ws_scratch(ws);
 
   if (w->format == QL_NVFP4) {
     const uint8_t* codes = (const uint8_t*)w->codes;
@@ -188,33 +190,26 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
     if (m <= kG16MaxM) {
       const ql::G16Plan p = ql::plan_g16(m, w->n, w->k, r);
       return hip_status(ql::launch_g16(p, x, m, w->n, w->k, codes, scales, w->tensor_scale, lora_a,
-                                       lora_b, r, lora_scale, y, out_f32, wsb, s));
+                                       lora_b, r, lora_scale, y, out_f32, ws, s));
     }
-    if (w->k % 64 == 0)
+    if (nvfp4_f16_path(w->k))
       return hip_status(ql::launch_gemm_nvfp4_f16(x, m, w->n, w->k, codes, scales, w->tensor_scale,
-                                                  lora_a, lora_b, r, lora_scale, y, out_f32, wsb, s));
-    const LoraWs lw = lora_ws(m, w->k, r);
+                                                  lora_a, lora_b, r, lora_scale, y, out_f32, scratch, s));
     uint16_t* t = nullptr;
-    if (r > 0) {
-      st = run_lora_t(lw, wsb, x, m, w->k, lora_a, r, lora_scale, &t, s);
-      if (st != QL_OK) return st;
-    }
+    if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, scratch, &t, s) != hipSuccess)
+      return QL_ERR_HIP;
     return hip_status(ql::launch_gemm_nvfp4(x, m, w->n, w->k, codes, scales, w->tensor_scale, t,
                                             lora_b, r, y, out_f32, s));
   }
 
   // FP8: quantize activations per 1x128 segment, then the block-scaled GEMM.
-  if (w->format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
-  uint8_t* xq = (uint8_t*)wsb;
-  float* sx = (float*)(wsb + up((size_t)m * (size_t)w->k));
-  char* rest = wsb + fp8_act_bytes(m, w->k);
+  uint8_t* xq = (uint8_t*)scratch;
+  float* sx = (float*)(scratch + up((size_t)m * (size_t)w->k));
+  char* rest = scratch + fp8_act_bytes(m, w->k);
   if (ql::launch_fp8_act_quantize(x, m, w->k, xq, sx, s) != hipSuccess) return QL_ERR_HIP;
-  const LoraWs lw = lora_ws(m, w->k, r);
   uint16_t* t = nullptr;
-  if (r > 0) {
-    st = run_lora_t(lw, rest, x, m, w->k, lora_a, r, lora_scale, &t, s);
-    if (st != QL_OK) return st;
-  }
+  if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, rest, &t, s) != hipSuccess)
+    return QL_ERR_HIP;
   return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes,
                                         (const float*)w->scales, t, lora_b, r, y, out_f32, s));
 }
@@ -233,15 +228,12 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
   const int32_t r = lora_rank(lora_a, lora_b, rank, lora_scale);
   if (r > 0 && !x) return QL_ERR_NULL;
   if (x && !aligned16(x)) return QL_ERR_ALIGN;
-  const size_t need = qlinear_forward_prequant_workspace(m, w->n, w->k, r);
-  if (need > 0 && (!ws || ws_bytes < need)) return QL_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(ws)) return QL_ERR_ALIGN;
+  st = check_forward_ws(w, m, r, true, ws, ws_bytes);
+  if (st != QL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   uint16_t* t = nullptr;
-  if (r > 0) {
-    st = run_lora_t(lora_ws(m, w->k, r), (char*)ws, x, m, w->k, lora_a, r, lora_scale, &t, s);
-    if (st != QL_OK) return st;
-  }
+  if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, ql::ws_scratch(ws), &t, s) != hipSuccess)
+    return QL_ERR_HIP;
   return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes,
                                         (const float*)w->scales, t, lora_b, r, y,
                                         out_dtype == QL_OUT_F32, s));
@@ -249,65 +241,19 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
 
 // ------------------------------------------------------------------- requant
 
-size_t qlinear_requant_table_bytes(int32_t count) {
-  if (count <= 0 || count > 65536) return 0;
-  return ql::requant_table_bytes(count);
+size_t qlinear_requant_workspace(int32_t count) {
+  if (count <= 0 || count > QLINEAR_MAX_REQUANT_ITEMS) return 0;
+  return ql::requant_workspace(count);
 }
 
-qlinear_status qlinear_requant_prepare(const qlinear_requant_item* items, int32_t count,
-                                       int32_t format, void* table, size_t table_bytes,
-                                       qlinear_requant_plan* plan, void* stream) {
-  if (!items || !table || !plan) return QL_ERR_NULL;
-  if (count <= 0 || count > 65536) return QL_ERR_ARG;
+qlinear_status qlinear_requantize_all(const qlinear_requant_item* items, int32_t count,
+                                      int32_t format, void* ws, size_t ws_bytes, void* stream) {
+  if (!items) return QL_ERR_NULL;
+  if (count <= 0 || count > QLINEAR_MAX_REQUANT_ITEMS) return QL_ERR_ARG;
   if (format != QL_NVFP4 && format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
-  if (table_bytes < ql::requant_table_bytes(count)) return QL_ERR_WORKSPACE;
-  if (!aligned16(table)) return QL_ERR_ALIGN;
-  std::vector<char> host(ql::requant_table_bytes(count), 0);
-  ql::RequantHeader* h = (ql::RequantHeader*)host.data();
-  ql::RequantDesc* d = (ql::RequantDesc*)(host.data() + sizeof(ql::RequantHeader));
-  int64_t units = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    const qlinear_requant_item& it = items[i];
-    if (it.q.format != format) return QL_ERR_ARG;
-    if (!it.w) return QL_ERR_NULL;
-    qlinear_status st = check_qweight(&it.q);
-    if (st != QL_OK) return st;
-    if (!aligned16(it.w)) return QL_ERR_ALIGN;
-    d[i].w = it.w;
-    d[i].codes = it.q.codes;
-    d[i].scales = it.q.scales;
-    d[i].tensor_scale = it.q.tensor_scale;
-    d[i].n = it.q.n;
-    d[i].k = it.q.k;
-    d[i].unit_begin = units;
-    d[i].unit_count = ql::requant_units(format, it.q.n, it.q.k);
-    units += d[i].unit_count;
-  }
-  h->count = count;
-  h->format = format;
-  h->total_units = units;
-  hipStream_t s = (hipStream_t)stream;
-  if (hipMemcpyAsync(table, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
-    return QL_ERR_HIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return QL_ERR_HIP;
-  plan->count = count;
-  plan->format = format;
-  plan->total_units = units;
-  return QL_OK;
-}
-
-qlinear_status qlinear_requantize_all(const qlinear_requant_plan* plan, void* table,
-                                      int32_t* status_word, void* stream) {
-  if (!plan || !table) return QL_ERR_NULL;
-  if (plan->count <= 0 || plan->count > 65536 || plan->total_units <= 0) return QL_ERR_ARG;
-  if (plan->format != QL_NVFP4 && plan->format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
-  if (!aligned16(table) || (status_word && ((uintptr_t)status_word & 3))) return QL_ERR_ALIGN;
-  ql::RequantHeader h;
-  std::memset(&h, 0, sizeof(h));
-  h.count = plan->count;
-  h.format = plan->format;
-  h.total_units = plan->total_units;
-  return hip_status(ql::launch_requant(table, h, status_word, (hipStream_t)stream));
+  if (!ws || ws_bytes < ql::requant_workspace(count)) return QL_ERR_WORKSPACE;
+  if (!aligned16(items) || !aligned16(ws)) return QL_ERR_ALIGN;
+  return hip_status(ql::launch_requant(items, count, format, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -149,18 +149,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16 bytes per lane from global memory (uniform base + per-lane byte offset) straight
 // into LDS at m0 + 16 * lane (m0 uniform).  An LDS-DMA load needs one wait state after
-// the write of m0.
+// the write of m0, which is read when the load issues; the asm keeps the compiler's own
+// m0 value in a scratch register and puts it back, so m0 is not clobbered.  Issued as
+// inline assembly (not the compiler builtin) because the compiler would otherwise take
+// these LDS writes to alias every fragment read and wait for them before each one;
+// completion is awaited explicitly with vmcnt.
 __device__ __forceinline__ void lds_copy16(const uint8_t* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-               "s"(lds_base)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(off), "s"(base), "s"(lds_base)
+               : "memory");
 }
 
 // 4 bytes per lane from global memory straight into LDS at m0 + 4 * lane.
 __device__ __forceinline__ void lds_copy4(const uint8_t* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
-               "s"(lds_base)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(off), "s"(base), "s"(lds_base)
+               : "memory");
 }
 
 }  // namespace ql

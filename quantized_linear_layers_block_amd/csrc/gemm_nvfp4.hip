@@ -277,7 +277,9 @@ struct Nvfp4F16Args {
 // row's largest bf16 magnitude (bit pattern) in amax_part[split][row] and, with RT > 0,
 // accumulates x A^T over RT 16-row tiles of A with bf16 MFMAs (A rows past the rank
 // read as zero) into t_part[split][row][16 RT].  Workgroups of one split are adjacent
-// so that they share the same range of A in L2.
+// so that they share the same range of A in L2.  k % 16 == 0; split boundaries are
+// multiples of 32, and a last step that runs past k reads zeros for the 8-element units
+// beyond it.
 template <int RT, int MF>
 __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                        const uint16_t* __restrict__ lora_a, int32_t rank,
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
   // four 32-wide steps per batch, all of their loads issued before any is used (used one by
   // one they would cost a memory round trip each)
   int64_t kk = k0;
-  for (; kk + 96 < k1; kk += 128) {
+  for (; kk + 128 <= k1; kk += 128) {
     i32x4 xq[4][MF], aq[4][RA];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -350,11 +352,12 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
     for (int u = 0; u < 4; ++u) use(xq[u], aq[u]);
   }
   for (; kk < k1; kk += 32) {
+    const bool in = kk + 8 * g < k1;  // this lane's unit of 8 lies inside or past k1
     i32x4 xq[MF], aq[RA];
 #pragma unroll
-    for (int h = 0; h < MF; ++h) xq[h] = *(const i32x4*)(xr[h] + kk);
+    for (int h = 0; h < MF; ++h) xq[h] = in ? *(const i32x4*)(xr[h] + kk) : i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < RT; ++i) aq[i] = *(const i32x4*)(ar[i] + kk);
+    for (int i = 0; i < RT; ++i) aq[i] = in ? *(const i32x4*)(ar[i] + kk) : i32x4{0, 0, 0, 0};
     use(xq, aq);
   }
 #pragma unroll
@@ -380,6 +383,25 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
 // rank_pad.  The split maxima and the chunk are loaded together: one round trip to
 // memory before the conversion instead of one per step of a whole row.
 constexpr int64_t kNvChunk8 = 256;  // 16-byte units per wave
+
+// bf16(s * sum over the K splits of t_part[split][row][j]) for j < rank, 0 up to rank_pad.
+// Fixed order: eight interleaved partial sums (split sp goes to sum sp % 8), then those
+// eight in order; the loads of one round are independent so they overlap.
+__device__ __forceinline__ uint16_t lora_t_value(const float* __restrict__ t_part, int64_t m, int64_t splits,
+                                                 int32_t rank, int32_t rank_pad, float lora_scale, int64_t row,
+                                                 int j) {
+  float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc8[u] += t_part[((sp + u) * m + row) * rank_pad + j];
+  }
+  for (int u = 0; sp < splits; ++sp, ++u) acc8[u] += t_part[(sp * m + row) * rank_pad + j];
+  float sum = acc8[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) sum += acc8[u];
+  return (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
+}
 __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                         int64_t splits, const uint32_t* __restrict__ amax_part,
                                                         const float* __restrict__ t_part, int32_t rank,
@@ -426,21 +448,18 @@ __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restri
   }
   if (chunk != 0) return;
   if (lane == 0) rs[row] = __uint_as_float((uint32_t)(127 - e) << 23);
-  for (int j = lane; j < rank_pad; j += 64) {
-    // fixed order: eight interleaved partial sums (split sp goes to sum sp % 8), then those
-    // eight in order; the loads of one round are independent so they overlap
-    float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int64_t sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc8[u] += t_part[((sp + u) * m + row) * rank_pad + j];
-    }
-    for (int u = 0; sp < splits; ++sp, ++u) acc8[u] += t_part[(sp * m + row) * rank_pad + j];
-    float sum = acc8[0];
-#pragma unroll
-    for (int u = 1; u < 8; ++u) sum += acc8[u];
-    t[row * rank_pad + j] = (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
-  }
+  for (int j = lane; j < rank_pad; j += 64) t[row * rank_pad + j] = lora_t_value(t_part, m, splits, rank, rank_pad, lora_scale, row, j);
+}
+
+// t[row][j] alone (the GEMM paths that take bf16 activations): one row per wave.
+__global__ __launch_bounds__(256) void lora_t_finish_kernel(int64_t m, int64_t splits,
+                                                            const float* __restrict__ t_part, int32_t rank,
+                                                            int32_t rank_pad, float lora_scale,
+                                                            uint16_t* __restrict__ t) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  for (int j = threadIdx.x & 63; j < rank_pad; j += 64)
+    t[row * rank_pad + j] = lora_t_value(t_part, m, splits, rank, rank_pad, lora_scale, row, j);
 }
 
 template <int OUT_F32>
@@ -724,6 +743,35 @@ struct NvPrepWs {
   size_t bytes;
 };
 
+// Row statistics and LoRA partials (nv_stats_kernel) over nv_prep_splits(m, k) K splits.
+hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int32_t rank,
+                           uint32_t* amax_part, float* t_part, hipStream_t s) {
+  const int32_t rank_pad = nv_rank_pad(rank);
+  // Large m: 128 rows per workgroup, so each load of A serves two row fragments (the split
+  // count, and with it the workspace, is that of 64-row tiles either way).
+  const int mf = m >= kNvStatsWideRows ? 2 : 1;
+  const int64_t tiles = (m + 64 * mf - 1) / (64 * mf), sp = nv_prep_splits(m, k);
+  const int64_t kchunk = ((k + sp - 1) / sp + 31) / 32 * 32;
+  const unsigned sgrid = (unsigned)(tiles * sp);
+#define QL_NV_STATS(RT_)                                                                               \
+  case RT_ / 16:                                                                                      \
+    if (mf == 2)                                                                                      \
+      nv_stats_kernel<RT_ / 16, 2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, amax_part, t_part); \
+    else                                                                                              \
+      nv_stats_kernel<RT_ / 16, 1><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, amax_part, t_part); \
+    break;
+  switch (rank_pad / 16) {
+    QL_NV_STATS(0)
+    QL_NV_STATS(32)
+    QL_NV_STATS(64)
+    QL_NV_STATS(96)
+    QL_NV_STATS(128)
+#undef QL_NV_STATS
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t n, int64_t k, int32_t rank) {
   const int64_t sp = nv_prep_splits(m, k);
   const size_t rp = (size_t)nv_rank_pad(rank);
@@ -746,7 +794,48 @@ NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t n, int64_t k, int32_t rank) {
   w.bytes = off;
   return w;
 }
+
+// LoRA down-projection scratch: split maxima (unused here), split partials, t.
+struct LoraDownWs {
+  uint32_t* amax_part;
+  float* t_part;
+  uint16_t* t;
+  size_t bytes;
+};
+LoraDownWs lora_down_ws(void* scratch, int64_t m, int64_t k, int32_t rank) {
+  const int64_t sp = nv_prep_splits(m, k);
+  const size_t rp = (size_t)nv_rank_pad(rank);
+  char* p = (char*)scratch;
+  LoraDownWs w;
+  size_t off = 0;
+  w.t = (uint16_t*)(p + off);
+  off += up256((size_t)m * rp * 2);
+  w.amax_part = (uint32_t*)(p + off);
+  off += up256((size_t)sp * (size_t)m * 4);
+  w.t_part = (float*)(p + off);
+  off += up256((size_t)sp * (size_t)m * rp * 4);
+  w.bytes = off;
+  return w;
+}
 }  // namespace
+
+size_t lora_down_bytes(int64_t m, int64_t k, int32_t rank) {
+  if (m <= 0 || k <= 0 || rank <= 0) return 0;
+  return lora_down_ws(nullptr, m, k, rank).bytes;
+}
+
+hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
+                            int32_t rank, float lora_scale, void* scratch, uint16_t** t_out,
+                            hipStream_t s) {
+  if (m <= 0 || k <= 0 || k % 16 != 0 || rank <= 0 || rank > 128 || !scratch) return hipErrorInvalidValue;
+  const LoraDownWs w = lora_down_ws(scratch, m, k, rank);
+  hipError_t e = launch_nv_stats(x, m, k, lora_a, rank, w.amax_part, w.t_part, s);
+  if (e != hipSuccess) return e;
+  lora_t_finish_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(m, nv_prep_splits(m, k), w.t_part, rank,
+                                                               nv_rank_pad(rank), lora_scale, w.t);
+  *t_out = w.t;
+  return hipGetLastError();
+}
 
 size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank) {
   if (m <= 0 || n <= 0 || k <= 0 || k % kQK != 0) return 0;
@@ -760,32 +849,13 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
                                  int out_f32, void* ws, hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
   // Copy offsets are 32-bit within a 256-row tile.
-  if (k % kQK != 0 || k >= (int64_t(1) << 22) || !ws || rank < 0 || rank > 128)
+  if (k % kQK != 0 || k >= kNvF16MaxK || !ws || rank < 0 || rank > 128)
     return hipErrorInvalidValue;
   const int32_t rank_pad = nv_rank_pad(rank);
   const NvPrepWs w = nv_prep_ws(ws, m, n, k, rank);
-  // Large m: 128 rows per workgroup, so each load of A serves two row fragments (the split
-  // count, and with it the workspace, is that of 64-row tiles either way).
-  const int mf = m >= kNvStatsWideRows ? 2 : 1;
-  const int64_t tiles = (m + 64 * mf - 1) / (64 * mf), sp = nv_prep_splits(m, k);
-  const int64_t kchunk = ((k + sp - 1) / sp + 31) / 32 * 32;
-  const unsigned sgrid = (unsigned)(tiles * sp);
-#define QL_NV_STATS(RT_)                                                                               \
-  case RT_ / 16:                                                                                      \
-    if (mf == 2)                                                                                      \
-      nv_stats_kernel<RT_ / 16, 2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); \
-    else                                                                                              \
-      nv_stats_kernel<RT_ / 16, 1><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, w.amax_part, w.t_part); \
-    break;
-  switch (rank_pad / 16) {
-    QL_NV_STATS(0)
-    QL_NV_STATS(32)
-    QL_NV_STATS(64)
-    QL_NV_STATS(96)
-    QL_NV_STATS(128)
-#undef QL_NV_STATS
-    default: return hipErrorInvalidValue;
-  }
+  const int64_t sp = nv_prep_splits(m, k);
+  hipError_t e0 = launch_nv_stats(x, m, k, lora_a, rank, w.amax_part, w.t_part, s);
+  if (e0 != hipSuccess) return e0;
   const int64_t fin_units = m * ((k / 8 + kNvChunk8 - 1) / kNvChunk8);
   nv_finish_kernel<<<(unsigned)((fin_units + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank,
                                                                     rank_pad, lora_scale, w.x16, w.rs, w.t);

@@ -27,9 +27,15 @@
 //   weight items; each stores its partial of x A^T (device scope) and counts itself on a
 //   counter.  The last one adds the partials in a fixed order, publishes t = bf16(s . x A^T)
 //   once and raises a flag.  A row tile's finishing waves (their B rows were fetched at the
-//   start) wait for the flag (bounded; LoRA items are dispatched first, so they are running
-//   or done), add t B^T with one MFMA per 32 ranks, apply S and store y.  Counters and the
-//   flag are returned to zero by the call that used them.
+//   start) wait for the flag (bounded in time; LoRA items are dispatched first, so they are
+//   running or done), add t B^T with one MFMA per 32 ranks, apply S and store y.  A wait
+//   that gives up stores NaN for its tile and sets the timeout bit of the workspace's
+//   status word.
+// * Counters live in the workspace's reserved region, at a spacing that depends on the
+//   plan, and every call returns the ones it used to zero: the split counters by their
+//   tile's last arrival, and the LoRA counter and the t flag by the last of all LoRA items
+//   and finishing tiles (counted on a two-level "done" counter), after which no workgroup
+//   of the launch touches them.  A late flag can therefore never reach the next call.
 #include "../../include/qlinear.h"
 #include "common.hpp"
 #include "gemm_common.hpp"
@@ -76,7 +82,9 @@ struct G16Args {
   int xstride;        // LDS row stride of the activations (elements)
   int64_t kst;        // 128-wide K stages (33..64 tokens with K % 128 == 0), else 0
   int64_t sps;        // stages per K split
-  uint32_t* ctr;      // counters and flags, one per 128-byte line (g16_line_*)
+  uint32_t* ctr;      // counters and flags in the reserved region (g16_line_*)
+  int ctr_stride;     // words between two of them
+  int32_t* status;    // the workspace's status word
   uint32_t* t;        // [m][rank_pad / 2] bf16 pairs
   float* part_w;      // [splits][m][n_pad]
   float* part_l;      // [lgroups][m][tiles_l * 16]
@@ -87,30 +95,35 @@ struct G16Chunk {
   uint32_t s;
 };
 
-// Counters and flags, each on a 128-byte line of its own (atomics on one line serialise and
-// delay every other access to it): [0, tiles_w) split arrivals per row tile, the LoRA
-// counter, the t flag, 32 finishing groups, the finishing top counter.
-constexpr int kG16LineWords = 32;
-constexpr int kG16FinGroups = 32;
-__device__ __forceinline__ uint32_t* g16_ctr(const G16Args& a, int64_t line) { return a.ctr + line * kG16LineWords; }
+// Counters and flags, one per line of ctr_stride words (128 bytes when the region has room:
+// atomics on one line serialise and delay every other access to it): [0, tiles_w) split
+// arrivals per row tile, the LoRA counter, the t flag, 32 "done" groups, the done top counter.
+constexpr int kG16DoneGroups = 32;
+constexpr int64_t kG16ExtraLines = 3 + kG16DoneGroups;
+__device__ __forceinline__ uint32_t* g16_ctr(const G16Args& a, int64_t line) { return a.ctr + line * a.ctr_stride; }
 __device__ __forceinline__ int64_t g16_line_l(const G16Args& a) { return a.tiles_w; }
 __device__ __forceinline__ int64_t g16_line_t(const G16Args& a) { return a.tiles_w + 1; }
-__device__ __forceinline__ int64_t g16_line_fg(const G16Args& a, int j) { return a.tiles_w + 2 + j; }
-__device__ __forceinline__ int64_t g16_line_ft(const G16Args& a) { return a.tiles_w + 2 + kG16FinGroups; }
+__device__ __forceinline__ int64_t g16_line_dg(const G16Args& a, int j) { return a.tiles_w + 2 + j; }
+__device__ __forceinline__ int64_t g16_line_dt(const G16Args& a) { return a.tiles_w + 2 + kG16DoneGroups; }
 
-// One finishing row tile on a two-level counter (tile i counts in group i % 32); true for the
-// last one overall.  Every last arrival returns its counter to zero.
-__device__ __forceinline__ bool g16_fin(const G16Args& a, int64_t tile) {
-  const int j = (int)(tile % kG16FinGroups);
-  const int64_t gsize = (a.tiles_w - j + kG16FinGroups - 1) / kG16FinGroups;
-  const int ngroups = a.tiles_w < kG16FinGroups ? (int)a.tiles_w : kG16FinGroups;
-  uint32_t* cg = g16_ctr(a, g16_line_fg(a, j));
-  if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)gsize - 1) return false;
+// Thread 0 only, with LoRA.  Counts one of the launch's LoRA items (idx < items) or finishing
+// row tiles (idx = items + tile) as done with the LoRA counter, the t flag and t, on a
+// two-level counter (arrival idx counts in group idx % 32).  Every group's last arrival
+// returns its counter to zero; the last arrival overall also returns the LoRA counter and
+// the t flag to zero: every other user of them has finished with them by then.
+__device__ __forceinline__ void g16_done(const G16Args& a, int64_t idx) {
+  const int64_t total = a.tiles_l * a.lgroups + a.tiles_w;
+  const int j = (int)(idx % kG16DoneGroups);
+  const int64_t gsize = (total - j + kG16DoneGroups - 1) / kG16DoneGroups;
+  const int ngroups = total < kG16DoneGroups ? (int)total : kG16DoneGroups;
+  uint32_t* cg = g16_ctr(a, g16_line_dg(a, j));
+  if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)gsize - 1) return;
   st_dev_u32(cg, 0u);
-  uint32_t* ct = g16_ctr(a, g16_line_ft(a));
-  if (__hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)ngroups - 1) return false;
+  uint32_t* ct = g16_ctr(a, g16_line_dt(a));
+  if (__hip_atomic_fetch_add(ct, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)ngroups - 1) return;
   st_dev_u32(ct, 0u);
-  return true;
+  st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
+  st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
 }
 
 // Memory operations complete in order, and the compiler can only count the ones still in
@@ -433,7 +446,10 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
     const int64_t mi = 16 * wave + r;
     if (mi < a.m) st_dev4v(dev_rsrc(a.part_l), (uint32_t)(((cg * a.m + mi) * lrow + tile * 16 + 4 * g) * 4), v);
   }
-  if (!g16_arrive(g16_ctr(a, g16_line_l(a)), (uint32_t)(a.tiles_l * a.lgroups), flag)) return;
+  if (!g16_arrive(g16_ctr(a, g16_line_l(a)), (uint32_t)(a.tiles_l * a.lgroups), flag)) {
+    if (threadIdx.x == 0) g16_done(a, id);  // its arrival has returned: done with the counter
+    return;
+  }
 
   // last LoRA item: t = bf16(s . (partials added in group order)), published once.  A unit
   // is four ranks of one token; all of its partials are loaded before any is added.
@@ -463,7 +479,11 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
   }
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) st_dev_u32(g16_ctr(a, g16_line_t(a)), 1u);
+  if (threadIdx.x == 0) {
+    st_dev_u32(g16_ctr(a, g16_line_t(a)), 1u);
+    wait_stores();  // the flag has reached L2 before this item counts as done
+    g16_done(a, id);
+  }
 }
 
 
@@ -524,12 +544,17 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
 #pragma unroll
     for (int q = 0; q < MT; ++q) acc[rt][q] *= ts;
   if (a.rank > 0) {
-    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
-      int it = 0;
-      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
+    // bounded wait for t (one poller per workgroup; flag[1] is not the arrival flag, which
+    // other waves may still be reading)
+    const bool have_t = wait_flag_bounded(g16_ctr(a, g16_line_t(a)), flag + 1);
+    if (!have_t) {  // t never came: NaN outputs for this tile, reported in the status word
+      if (threadIdx.x == 0) __hip_atomic_fetch_or(a.status, (int32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int q = 0; q < MT; ++q) acc[rt][q] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
-    __syncthreads();
-    const int rc = a.rank_pad / 32;
+    const int rc = have_t ? a.rank_pad / 32 : 0;
 #pragma unroll
     for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
       if (c >= rc) break;
@@ -551,10 +576,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
       }
     }
     __syncthreads();  // every wave of this workgroup has read t
-    if (threadIdx.x == 0 && g16_fin(a, tile)) {
-      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
-      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
-    }
+    if (threadIdx.x == 0) g16_done(a, a.tiles_l * a.lgroups + tile);
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -844,7 +866,7 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
 template <int MT, int RT, bool ALIGNED, int XU>
 __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALIGNED ? (MT == 1 ? 5 : MT == 2 ? 4 : 2) : 1))) void g16_kernel(G16Args a) {
   extern __shared__ __align__(16) uint16_t xs[];
-  __shared__ int flag;
+  __shared__ int flag[2];  // [0]: arrival results, [1]: bounded-wait results
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
@@ -852,16 +874,16 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   const int64_t items_l = a.tiles_l * a.lgroups;
   int64_t id = blockIdx.x;
   if (id < items_l) {
-    g16_lora_item<MT, !ALIGNED>(a, xs, &flag, id);
+    g16_lora_item<MT, !ALIGNED>(a, xs, flag, id);
     return;
   }
 
   // -------------------------------------------------------------------- weight item
   if constexpr (MT == 4) {
     if (a.kst > 0)
-      g16_stream128_item(a, xs, &flag, id - items_l);
+      g16_stream128_item(a, xs, flag, id - items_l);
     else
-      g16_stream_item<RT, ALIGNED>(a, xs, &flag, id - items_l);
+      g16_stream_item<RT, ALIGNED>(a, xs, flag, id - items_l);
   } else {
   id -= items_l;
   const int64_t tile = id % a.tiles_w;
@@ -925,7 +947,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
   const int64_t nb = row0 + 16 * rt_e + 4 * g;
   if (a.splits > 1) {
     if (tile_wave && mi < a.m) st_dev4v(dev_rsrc(a.part_w), (uint32_t)(((split * a.m + mi) * a.n_pad + nb) * 4), v);
-    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, &flag)) return;
+    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
     if (tile_wave) {
       const auto rs = dev_rsrc(a.part_w);
       const int64_t mc = mi < a.m ? mi : a.m - 1;
@@ -948,12 +970,13 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
 
   v *= ts;
   if (a.rank > 0) {  // every wave passes the two barriers
-    if (threadIdx.x == 0) {  // bounded wait for t, one poller per workgroup
-      int it = 0;
-      while (ld_dev_u32(g16_ctr(a, g16_line_t(a))) == 0u && ++it < kGvSpinLimit) __builtin_amdgcn_s_sleep(4);
+    // bounded wait for t, one poller per workgroup (see g16_stream_finish)
+    const bool have_t = wait_flag_bounded(g16_ctr(a, g16_line_t(a)), flag + 1);
+    if (!have_t) {
+      if (threadIdx.x == 0) __hip_atomic_fetch_or(a.status, (int32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
-    __syncthreads();
-    if (tile_wave) {
+    if (tile_wave && have_t) {
       const int rc = a.rank_pad / 32;
 #pragma unroll
       for (int c = 0; c < QLINEAR_MAX_RANK / 32; ++c) {
@@ -969,10 +992,7 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
       }
     }
     __syncthreads();  // every tile wave of this workgroup has read t
-    if (threadIdx.x == 0 && g16_fin(a, tile)) {  // the last finishing tile returns the flags to zero
-      st_dev_u32(g16_ctr(a, g16_line_l(a)), 0u);
-      st_dev_u32(g16_ctr(a, g16_line_t(a)), 0u);
-    }
+    if (threadIdx.x == 0) g16_done(a, a.tiles_l * a.lgroups + tile);
   }
   if (!tile_wave) return;
   if (mi >= a.m || nb >= a.n) return;
@@ -984,6 +1004,16 @@ __global__ __launch_bounds__(kG16Threads) __attribute__((amdgpu_waves_per_eu(ALI
 
 static int64_t g16_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static size_t g16_align(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Counter spacing in the reserved region: a 128-byte line per counter when they fit, else
+// the widest power-of-two spacing that fits (0: they do not fit even one word apart).
+static int g16_ctr_stride(int64_t tiles_w) {
+  const int64_t lines = tiles_w + kG16ExtraLines;
+  const int64_t words = (int64_t)((kWsReserved - kWsCounterOff) / 4);
+  for (int st = 32; st >= 1; st /= 2)
+    if (lines * st <= words) return st;
+  return 0;
+}
 
 G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   G16Plan p;
@@ -1018,6 +1048,7 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
       p.cps = 0;
       p.xstride = 0;
       p.lds_bytes = (size_t)kS128Lds;
+      p.ctr_stride = g16_ctr_stride(p.tiles_w);
       return p;
     }
     // other K: 64-row workgroups running over 256-wide K chunks.  K is split only when
@@ -1032,6 +1063,7 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
     p.splits = (int)g16_cdiv(p.kchunks, p.cps);
     p.xstride = kG16Chunk + 8;
     p.lds_bytes = (size_t)2 * 64 * (size_t)p.xstride * 2;  // two chunks of 64 tokens
+    p.ctr_stride = g16_ctr_stride(p.tiles_w);
     return p;
   }
   p.mt = m <= 16 ? 1 : 2;
@@ -1059,19 +1091,23 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
   p.lds_bytes = (size_t)m * (size_t)p.xstride * 2 + kG16ZeroElems * 2;
   const size_t red_bytes = (size_t)kG16Waves * p.rt * p.mt * kWave * 16;  // the wave reduction reuses it
   if (p.lds_bytes < red_bytes) p.lds_bytes = red_bytes;
+  p.ctr_stride = g16_ctr_stride(p.tiles_w);
   return p;
 }
 
-static size_t g16_counter_bytes(const G16Plan& p) {
-  return g16_align((size_t)(p.tiles_w + 3 + kG16FinGroups) * kG16LineWords * 4);
+bool g16_plan_ok(const G16Plan& p, int64_t m) {
+  if (p.ctr_stride <= 0) return false;
+  if (p.mt < 4 && p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return false;  // one batch per wave
+  // partials are read through buffer descriptors with 32-bit byte offsets
+  return (double)p.splits * (double)m * (double)p.n_pad * 4.0 < 2147483648.0 &&
+         (double)p.lgroups * (double)m * (double)(p.tiles_l * 16) * 4.0 < 2147483648.0;
 }
 
 size_t g16_workspace(const G16Plan& p, int64_t m) {
-  const size_t counters = g16_counter_bytes(p);
   const size_t t = g16_align((size_t)m * (size_t)p.rank_pad * 2);
   const size_t pw = p.splits > 1 ? g16_align((size_t)p.splits * (size_t)m * (size_t)p.n_pad * 4) : 0;
   const size_t pl = g16_align((size_t)p.lgroups * (size_t)m * (size_t)(p.tiles_l * 16) * 4);
-  return counters + t + pw + pl;
+  return t + pw + pl;
 }
 
 hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n, int64_t k,
@@ -1104,9 +1140,11 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.xstride = p.xstride;
   a.kst = p.kst;
   a.sps = p.sps;
-  char* w = (char*)ws;
-  a.ctr = (uint32_t*)w;
-  size_t off = g16_counter_bytes(p);
+  a.ctr = ws_counters(ws);
+  a.ctr_stride = p.ctr_stride;
+  a.status = ws_status(ws);
+  char* w = ws_scratch(ws);
+  size_t off = 0;
   a.t = (uint32_t*)(w + off);
   off += g16_align((size_t)m * (size_t)p.rank_pad * 2);
   a.part_w = (float*)(w + off);
@@ -1114,11 +1152,7 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.part_l = (float*)(w + off);
   const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.tiles_w * p.splits);
   const bool aligned = (k % kG16Chunk) == 0;
-  if (p.mt < 4 && p.cps > (int64_t)kG16Waves * (kG16Pairs / p.rt)) return hipErrorInvalidValue;  // plan invariant
-  // partials are read through buffer descriptors with 32-bit byte offsets
-  if ((double)p.splits * (double)m * (double)p.n_pad * 4.0 >= 2147483648.0 ||
-      (double)p.lgroups * (double)m * (double)(p.tiles_l * 16) * 4.0 >= 2147483648.0)
-    return hipErrorInvalidValue;
+  if (!g16_plan_ok(p, m)) return hipErrorInvalidValue;  // the C ABI checks this first
   hipError_t e;
 #define QL_G16_LAUNCH(MT, RT, AL, XU)                                                          \
   e = hipFuncSetAttribute((const void*)g16_kernel<MT, RT, AL, XU>,                             \

@@ -8,6 +8,21 @@
 
 namespace ql {
 
+// ---- forward workspace layout, shared by every path
+// [0, kWsReserved): the status word (int32 at offset 0) and, from kWsCounterOff on, the
+// integer counters and flags through which the workgroups of one launch coordinate.  They
+// must be zero before the first call and every call returns the ones it used to zero, so
+// calls of any shape may share one workspace.  No path ever uses this region as scratch.
+// [kWsReserved, ...): per-call scratch, always written before it is read within a call.
+constexpr size_t kWsReserved = 128 * 1024;
+constexpr size_t kWsCounterOff = 256;
+constexpr uint32_t kStatusNonFinite = 1u;  // a weight input held Inf or NaN
+constexpr uint32_t kStatusTimeout = 2u;    // a bounded wait for another workgroup gave up
+constexpr uint32_t kStatusBadItem = 4u;    // a requantization item failed its checks
+inline int32_t* ws_status(void* ws) { return (int32_t*)ws; }
+inline uint32_t* ws_counters(void* ws) { return (uint32_t*)((char*)ws + kWsCounterOff); }
+inline char* ws_scratch(void* ws) { return (char*)ws + kWsReserved; }
+
 // ---- quantizers (quant.hip)
 constexpr int kAmaxParts = 1024;  // partial maxima written by the NVFP4 amax pass
 hipError_t launch_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
@@ -18,54 +33,18 @@ hipError_t launch_fp8_weight_quantize(const uint16_t* w, int64_t n, int64_t k, u
 hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
                                    float* sx, hipStream_t s);
 
-// ---- whole-policy requantization (requant.hip)
-struct RequantDesc {       // one tensor, as stored in the device table
-  const uint16_t* w;
-  void* codes;
-  void* scales;
-  float* tensor_scale;
-  int64_t n, k;
-  int64_t unit_begin;      // first work unit of this tensor in the global unit space
-  int64_t unit_count;
-};
-struct RequantHeader {
-  int32_t count;
-  int32_t format;
-  int64_t total_units;
-  int64_t pad[2];
-};
-// Table layout: header | descs[count] | amax[count] (uint32, per-tensor |w| maximum bits)
-size_t requant_table_bytes(int32_t count);
-hipError_t launch_requant(void* table, const RequantHeader& h, int32_t* status, hipStream_t s);
-int64_t requant_units(int32_t format, int64_t n, int64_t k);
+// ---- whole-policy requantization (quant.hip)
+// Workspace: status word | header | descriptors[count] | per-tensor maxima[count].  The
+// descriptors are rebuilt on the device from the caller's item array by every call.
+size_t requant_workspace(int32_t count);
+hipError_t launch_requant(const void* items, int32_t count, int32_t format, void* ws,
+                          hipStream_t s);
 
-// ---- NVFP4 few-token layer and LoRA down-projection (gemv.hip)
-struct SkinnyPlan {
-  int mt;                     // m tiles of 16 per workgroup (1, 2, 4)
-  int r;                      // row tiles of 16 per wave
-  int splits;                 // K splits
-  int64_t kchunks_per_split;  // 256-wide K chunks per split
-  int m_groups;               // groups of 16 mt tokens
-  int64_t rows_w;             // NVFP4 rows (n)
-  int64_t rows_w_pad;         // n rounded up to whole row groups
-  int64_t rows_l;             // LoRA rows (rank rounded up to 16), 0 if none
-  int64_t rows_total;         // row length of the LoRA partials
-  int64_t groups_w, groups_l; // row groups of 16 r rows
-  int rank_pad;               // row length of t (rank rounded up to 32)
-};
-SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int32_t rank);
-size_t skinny_workspace(const SkinnyPlan& p, int64_t m, int64_t k);
-// t = bf16(s x A^T) [m][rank_pad] into the workspace (plan from plan_skinny(m, 0, k, rank)).
-hipError_t launch_lora_down(const SkinnyPlan& p, const uint16_t* x, int64_t m, int64_t k,
-                            const uint16_t* lora_a, int32_t rank, float lora_scale, void* ws,
-                            hipStream_t s);
-uint16_t* lora_t_in_workspace(const SkinnyPlan& p, void* ws);
-
-// ---- NVFP4 layer for up to 64 tokens (gemv16.hip); workspace zero before first use
+// ---- NVFP4 layer for up to 64 tokens (gemv16.hip)
 struct G16Plan {
-  int mt;             // m tiles of 16 (1 or 2)
+  int mt;             // m tiles of 16 (1, 2 or 4)
   int rt;             // row tiles of 16 per workgroup (1 or 2)
-  int64_t tiles_w;    // weight tiles of 16 * rt rows
+  int64_t tiles_w;    // weight tiles of 16 * rt rows (64 rows for 33..64 tokens)
   int64_t kchunks;    // 256-wide K chunks
   int64_t tiles_l;    // LoRA row tiles of 16
   int64_t lgroups;    // LoRA chunk groups
@@ -78,13 +57,25 @@ struct G16Plan {
   int64_t kst = 0;    // 128-wide K stages of the 33..64-token stage path (0: not used)
   int64_t sps = 0;    // stages per K split on that path
   size_t lds_bytes;
+  int ctr_stride = 0; // words between two counters in the reserved region (0: does not fit)
 };
 G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank);
-size_t g16_workspace(const G16Plan& p, int64_t m);
+// false if the launch cannot run this shape (counters do not fit the reserved region,
+// partial offsets beyond 32 bits): the C ABI reports QL_ERR_SHAPE before launching.
+bool g16_plan_ok(const G16Plan& p, int64_t m);
+size_t g16_workspace(const G16Plan& p, int64_t m);  // scratch bytes after the reserved region
 hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                       const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                       const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
                       float lora_scale, void* y, int out_f32, void* ws, hipStream_t s);
+
+// ---- LoRA down-projection for the GEMM paths (gemm_nvfp4.hip)
+// t = bf16(s x A^T) as [m][rank_pad] (zero past the rank) in `scratch`; two kernels (split-K
+// partials, then their fixed-order sum), no inter-workgroup counters.  k % 16 == 0.
+size_t lora_down_bytes(int64_t m, int64_t k, int32_t rank);
+hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
+                            int32_t rank, float lora_scale, void* scratch, uint16_t** t_out,
+                            hipStream_t s);
 
 // ---- large-M GEMMs (gemm_nvfp4.hip, gemm_fp8.hip)
 // Generic K (k % 16 == 0): t = bf16(s x A^T) computed beforehand, or null.
@@ -92,14 +83,17 @@ hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              const uint16_t* t, const uint16_t* lora_b, int32_t rank, void* y,
                              int out_f32, hipStream_t s);
-// k % 64 == 0: f16 activations, row factors and the LoRA intermediate are formed in the
-// workspace (gemm_nvfp4_f16_workspace bytes) by a pre-pass.
+// k % 64 == 0 and k < kNvF16MaxK: f16 activations, row factors and the LoRA intermediate
+// are formed in `scratch` (gemm_nvfp4_f16_workspace bytes) by a pre-pass.
+constexpr int64_t kNvF16MaxK = int64_t(1) << 22;
 hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                  const uint8_t* codes, const uint8_t* scales,
                                  const float* tensor_scale, const uint16_t* lora_a,
                                  const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
-                                 int out_f32, void* ws, hipStream_t s);
+                                 int out_f32, void* scratch, hipStream_t s);
 size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
+// k % 128 == 0 and k < kFp8MaxK (copy offsets within a 256-row tile are 32-bit).
+constexpr int64_t kFp8MaxK = int64_t(1) << 24;
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_t n, int64_t k,
                            const uint8_t* wq, const float* sw, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,

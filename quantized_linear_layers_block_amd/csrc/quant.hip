@@ -18,6 +18,7 @@
 // move.  Maxima are taken on the integer |bf16| bit patterns, which order like the
 // values and are exact.  Element quotients w/d are formed exactly (see
 // exact_quotient) and converted by the hardware E2M1/E4M3 encoders.
+#include "../../include/qlinear.h"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -300,21 +301,112 @@ hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint
 }
 
 // ------------------------------------------------ whole-policy requantization
+//
+// Recalibration after every training step (mexc.co NeMo RL FP8 page, "Praktische
+// prestatiewinsten"): the per-tensor quantizer applied to every tensor of the policy,
+// grouped into a few launches over all tensors.  The caller's item array lives in device
+// memory; a one-workgroup prepare kernel checks every item, numbers the work units of all
+// tensors (NVFP4: 8192-element chunks, FP8: 128x128 tiles) and writes the descriptor table
+// into the workspace, so nothing crosses from the host per step.
 
-size_t requant_table_bytes(int32_t count) {
-  size_t b = sizeof(RequantHeader) + (size_t)count * sizeof(RequantDesc) + (size_t)count * 4;
+struct RequantDesc {       // one tensor, as the passes read it
+  const uint16_t* w;
+  void* codes;
+  void* scales;
+  float* tensor_scale;
+  int64_t n, k;
+  int64_t unit_begin;      // first work unit of this tensor in the global unit space
+  int64_t unit_count;      // 0 for an item that failed its checks
+};
+struct RequantHeader {
+  int32_t count;
+  int32_t format;
+  int64_t total_units;
+};
+// Workspace: status word at 0 | header at 16 | descriptors from 64 | maxima[count] (u32)
+constexpr size_t kRqHeaderOff = 16, kRqDescOff = 64;
+
+size_t requant_workspace(int32_t count) {
+  size_t b = kRqDescOff + (size_t)count * sizeof(RequantDesc) + (size_t)count * 4;
   return (b + 255) & ~(size_t)255;
 }
 
-int64_t requant_units(int32_t format, int64_t n, int64_t k) {
-  if (format == 1) return (n * k / 8 + kChunkVec - 1) / kChunkVec;  // NVFP4 chunks
-  return (n / 128) * (k / 128);                                     // FP8 tiles
+__device__ __forceinline__ int64_t requant_units_dev(int32_t format, int64_t n, int64_t k) {
+  if (format == QL_NVFP4) return (n * k / 8 + kChunkVec - 1) / kChunkVec;  // NVFP4 chunks
+  return (n / 128) * (k / 128);                                           // FP8 tiles
+}
+
+// The checks the host applies to a quantized weight (include/qlinear.h), on the device.
+__device__ __forceinline__ bool requant_item_ok(const qlinear_requant_item& it, int32_t format) {
+  const qlinear_qweight& q = it.q;
+  auto al = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (q.format != format || !it.w || !q.codes || !q.scales) return false;
+  if (q.n <= 0 || q.k <= 0 || q.n > QLINEAR_MAX_ELEMS / q.k) return false;
+  if (!al(it.w) || !al(q.codes) || !al(q.scales)) return false;
+  if (format == QL_NVFP4) return q.tensor_scale && al(q.tensor_scale) && q.k % 16 == 0;
+  return q.n % 128 == 0 && q.k % 128 == 0;
+}
+
+constexpr int kRqPrepThreads = 1024;
+__global__ __launch_bounds__(kRqPrepThreads) void requant_prepare_kernel(const qlinear_requant_item* __restrict__ items,
+                                                                         int32_t count, int32_t format, char* ws) {
+  __shared__ int64_t wsum[kRqPrepThreads / kWave];
+  RequantHeader* h = (RequantHeader*)(ws + kRqHeaderOff);
+  RequantDesc* d = (RequantDesc*)(ws + kRqDescOff);
+  int32_t* status = (int32_t*)ws;
+  // thread i numbers items [i * per, (i + 1) * per): local sum, block-wide exclusive scan
+  const int per = (count + kRqPrepThreads - 1) / kRqPrepThreads;
+  const int i0 = threadIdx.x * per, i1 = min(i0 + per, count);
+  int64_t local = 0;
+  bool bad = false;
+  for (int i = i0; i < i1; ++i) {
+    const qlinear_requant_item it = items[i];
+    const bool ok = requant_item_ok(it, format);
+    bad |= !ok;
+    local += ok ? requant_units_dev(format, it.q.n, it.q.k) : 0;
+  }
+  if (bad) atomicOr(status, (int32_t)kStatusBadItem);
+  // inclusive scan within the wave, then over the waves' totals
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int64_t v = local;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == kWave - 1) wsum[wave] = v;
+  __syncthreads();
+  int64_t before = 0, total = 0;
+  for (int w = 0; w < kRqPrepThreads / kWave; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  int64_t u = before + v - local;
+  for (int i = i0; i < i1; ++i) {
+    const qlinear_requant_item it = items[i];
+    const bool ok = requant_item_ok(it, format);
+    RequantDesc r;
+    r.w = it.w;
+    r.codes = it.q.codes;
+    r.scales = it.q.scales;
+    r.tensor_scale = it.q.tensor_scale;
+    r.n = it.q.n;
+    r.k = it.q.k;
+    r.unit_begin = u;
+    r.unit_count = ok ? requant_units_dev(format, it.q.n, it.q.k) : 0;
+    d[i] = r;
+    u += r.unit_count;
+  }
+  if (threadIdx.x == 0) {
+    h->count = count;
+    h->format = format;
+    h->total_units = total;
+  }
 }
 
 __device__ __forceinline__ int find_tensor(const RequantDesc* __restrict__ d, int count,
                                            int64_t unit) {
   int lo = 0, hi = count - 1;
-  while (lo < hi) {  // last tensor whose unit_begin <= unit
+  while (lo < hi) {  // last tensor whose unit_begin <= unit (the one holding it)
     const int mid = (lo + hi + 1) >> 1;
     if (d[mid].unit_begin <= unit) lo = mid; else hi = mid - 1;
   }
@@ -373,7 +465,7 @@ __global__ __launch_bounds__(kQThreads) void requant_encode_kernel(const Requant
     const int64_t chunk = u - d[t].unit_begin;
     if (chunk == 0 && threadIdx.x == 0) {
       *d[t].tensor_scale = ts.S;
-      if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+      if (amax_bits >= kBf16InfBits) atomicOr(status, (int32_t)kStatusNonFinite);
     }
     nvfp4_encode_chunk((const uint4*)d[t].w, d[t].n * d[t].k / 8, chunk, ts, rtab,
                        (uint32_t*)d[t].codes, (uint8_t*)d[t].scales);
@@ -395,21 +487,30 @@ __global__ __launch_bounds__(kQThreads) void requant_fp8_kernel(const RequantHea
   }
 }
 
-hipError_t launch_requant(void* table, const RequantHeader& h, int32_t* status, hipStream_t s) {
-  const RequantHeader* dh = (const RequantHeader*)table;
-  const RequantDesc* dd = (const RequantDesc*)((char*)table + sizeof(RequantHeader));
-  uint32_t* amax = (uint32_t*)((char*)table + sizeof(RequantHeader) + (size_t)h.count * sizeof(RequantDesc));
-  if (h.format == 1) {
-    requant_zero_kernel<<<(h.count + kQThreads - 1) / kQThreads, kQThreads, 0, s>>>(amax, h.count);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    requant_amax_kernel<<<stream_grid(h.total_units, 4096), kQThreads, 0, s>>>(dh, dd, amax);
+// Grids are fixed (the unit count is only known on the device); every kernel loops over
+// the units the header announces.
+constexpr int kRqAmaxGrid = 4096, kRqEncodeGrid = 4096, kRqFp8Grid = 8192;
+
+hipError_t launch_requant(const void* items, int32_t count, int32_t format, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  const RequantHeader* dh = (const RequantHeader*)(w + kRqHeaderOff);
+  const RequantDesc* dd = (const RequantDesc*)(w + kRqDescOff);
+  uint32_t* amax = (uint32_t*)(w + kRqDescOff + (size_t)count * sizeof(RequantDesc));
+  int32_t* status = (int32_t*)w;
+  requant_prepare_kernel<<<1, kRqPrepThreads, 0, s>>>((const qlinear_requant_item*)items, count, format, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (format == QL_NVFP4) {
+    requant_zero_kernel<<<(count + kQThreads - 1) / kQThreads, kQThreads, 0, s>>>(amax, count);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    requant_encode_kernel<<<stream_grid(h.total_units, 4096), kQThreads, 0, s>>>(dh, dd, amax, status);
+    requant_amax_kernel<<<kRqAmaxGrid, kQThreads, 0, s>>>(dh, dd, amax);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    requant_encode_kernel<<<kRqEncodeGrid, kQThreads, 0, s>>>(dh, dd, amax, status);
     return hipGetLastError();
   }
-  requant_fp8_kernel<<<stream_grid(h.total_units, 8192), kQThreads, 0, s>>>(dh, dd, status);
+  requant_fp8_kernel<<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
   return hipGetLastError();
 }
 

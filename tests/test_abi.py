@@ -30,24 +30,39 @@ def test_status_strings():
     assert b.status_string(b.QL_ERR_ALIGN) == "pointer not 16-byte aligned"
 
 
+RES = b.QLINEAR_WS_RESERVED_BYTES
+
+
 def test_workspace_queries():
     assert b.qlinear_quantize_workspace(b.QL_NVFP4, 256, 512) == 4096
     assert b.qlinear_quantize_workspace(b.QL_FP8_BLOCK128, 256, 512) == 0
-    assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 3584, 3584, 32) > 0
+    # every forward workspace starts with the reserved region (status word + counters)
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 3584, 3584, 32) > RES
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 3584, 3584, 0) >= RES
     # NVFP4 prefill (k % 64 == 0) holds f16 activations (m*k*2 bytes), m row factors, the
     # LoRA intermediate (m * rank rounded up to 32, bf16) and the pre-pass partials:
     # per K split, m row maxima and m * rank_pad float32 LoRA sums (16 splits here)
     m, k = 4096, 5120
-    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 0) == m * k * 2 + m * 4 + 16 * m * 4
-    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 40) == (
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 0) == RES + m * k * 2 + m * 4 + 16 * m * 4
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, m, 27648, k, 40) == RES + (
         m * k * 2 + m * 4 + m * 64 * 2 + 16 * m * 4 + 16 * m * 64 * 4)
-    # other k take the kernel that reads bf16 activations directly
-    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 256, 5136, 0) == 0
+    # other k take the kernel that reads bf16 activations directly: only the reserved region
+    # without LoRA, plus the LoRA down-projection's t and split partials with it
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 256, 5136, 0) == RES
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 4096, 256, 5136, 32) > RES + 4096 * 32 * 2
     # FP8 forward holds the quantized activations (m*k bytes + scales)
-    assert b.qlinear_forward_workspace(b.QL_FP8_BLOCK128, 8192, 4096, 14336, 0) >= 8192 * 14336
+    assert b.qlinear_forward_workspace(b.QL_FP8_BLOCK128, 8192, 4096, 14336, 0) >= RES + 8192 * 14336
+    assert b.qlinear_forward_prequant_workspace(8192, 4096, 14336, 0) == RES
     assert b.qlinear_forward_workspace(b.QL_NVFP4, 0, 16, 16, 0) == 0
-    assert b.qlinear_requant_table_bytes(448) > 448 * 56
-    assert b.qlinear_requant_table_bytes(0) == 0
+    # shapes the kernels cannot run have no workspace: FP8 k >= 2^24
+    assert b.qlinear_forward_workspace(b.QL_FP8_BLOCK128, 8, 128, 1 << 24, 0) == 0
+    assert b.qlinear_requant_workspace(448) >= 448 * (64 + 4)
+    assert b.qlinear_requant_workspace(0) == 0
+    assert b.qlinear_requant_workspace(65537) == 0
+
+
+def test_status_word_is_first_int32():
+    assert b.LIB.qlinear_status_word(0x20000) == 0x20000
 
 
 FAKE = 0x10000  # an aligned, never-dereferenced address
@@ -89,20 +104,39 @@ def test_forward_argument_errors():
     assert pq == b.QL_ERR_FORMAT
 
 
+def test_forward_shape_limits_before_launch():
+    """Limits of the kernels are argument errors reported before anything is enqueued."""
+    L = b.LIB
+    qf = b.QWeight(b.QL_FP8_BLOCK128, 0, 128, 1 << 24, FAKE, FAKE, None)
+    assert L.qlinear_forward(ctypes.byref(qf), FAKE, 8, None, None, 0, 0.0, FAKE, b.QL_OUT_BF16,
+                             FAKE, 1 << 40, None) == b.QL_ERR_SHAPE
+    pq = L.qlinear_forward_fp8_prequant(ctypes.byref(qf), FAKE, FAKE, 8, None, None, None, 0, 0.0, FAKE,
+                                        b.QL_OUT_BF16, FAKE, 1 << 40, None)
+    assert pq == b.QL_ERR_SHAPE
+    # a few-token NVFP4 call whose counters cannot fit the reserved region
+    qn = b.QWeight(b.QL_NVFP4, 0, 1 << 24, 16, FAKE, FAKE, FAKE)
+    assert L.qlinear_forward(ctypes.byref(qn), FAKE, 1, None, None, 0, 0.0, FAKE, b.QL_OUT_BF16,
+                             FAKE, 1 << 40, None) == b.QL_ERR_SHAPE
+    assert b.qlinear_forward_workspace(b.QL_NVFP4, 1, 1 << 24, 16, 0) == 0
+
+
 def test_requant_argument_errors():
     L = b.LIB
-    items = (b.RequantItem * 2)()
-    items[0].w = FAKE
-    items[0].q = b.QWeight(b.QL_NVFP4, 0, 128, 256, FAKE, FAKE, FAKE)
-    items[1].w = FAKE
-    items[1].q = b.QWeight(b.QL_FP8_BLOCK128, 0, 128, 256, FAKE, FAKE, None)
-    plan = b.RequantPlan()
-    nb = b.qlinear_requant_table_bytes(2)
-    assert L.qlinear_requant_prepare(items, 2, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_ARG
-    assert L.qlinear_requant_prepare(items, 0, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_ARG
-    assert L.qlinear_requant_prepare(items, 1, b.QL_NVFP4, FAKE, 8, ctypes.byref(plan), None) == b.QL_ERR_WORKSPACE
-    assert L.qlinear_requant_prepare(items, 1, 9, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_FORMAT
-    items[0].q = b.QWeight(b.QL_NVFP4, 0, 128, 250, FAKE, FAKE, FAKE)
-    assert L.qlinear_requant_prepare(items, 1, b.QL_NVFP4, FAKE, nb, ctypes.byref(plan), None) == b.QL_ERR_SHAPE
-    assert L.qlinear_requantize_all(ctypes.byref(plan), FAKE, None, None) == b.QL_ERR_ARG  # empty plan
-    assert L.qlinear_requantize_all(None, FAKE, None, None) == b.QL_ERR_NULL
+    nb = b.qlinear_requant_workspace(2)
+    ra = lambda items=FAKE, count=2, fmt=b.QL_NVFP4, ws=FAKE, wsb=nb: L.qlinear_requantize_all(
+        items, count, fmt, ws, wsb, None)
+    assert ra(items=None) == b.QL_ERR_NULL
+    assert ra(count=0) == b.QL_ERR_ARG
+    assert ra(count=65537) == b.QL_ERR_ARG
+    assert ra(fmt=9) == b.QL_ERR_FORMAT
+    assert ra(ws=None) == b.QL_ERR_WORKSPACE
+    assert ra(wsb=nb - 1) == b.QL_ERR_WORKSPACE
+    assert ra(items=FAKE + 8) == b.QL_ERR_ALIGN
+    assert ra(ws=FAKE + 8) == b.QL_ERR_ALIGN
+
+
+def test_requant_item_layout():
+    """The item array is read on the device: its layout is the header's struct."""
+    assert ctypes.sizeof(b.RequantItem) == 56
+    assert b.RequantItem.q.offset == 8
+    assert b.QWeight.tensor_scale.offset == 40

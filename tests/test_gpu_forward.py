@@ -20,6 +20,15 @@ ql = pytest.importorskip("quantized_linear_layers_block_amd")
 TOL = 2e-3
 
 
+def _sample(n, count, seed):
+    """Seeded random indices in [0, n) plus the first and last: every lane position of a
+    16-row MFMA fragment gets sampled, unlike a fixed stride that shares a factor with 16."""
+    if count >= n:
+        return np.arange(n)
+    pick = np.random.default_rng(seed).choice(n, size=count, replace=False)
+    return np.unique(np.concatenate([pick, [0, n - 1]]))
+
+
 def _both_outputs(qw, x, a=None, b=None, s=0.0):
     y32 = ql.forward(qw, x, a, b, s, out_dtype=torch.float32)
     y16 = ql.forward(qw, x, a, b, s, out_dtype=torch.bfloat16)
@@ -65,7 +74,7 @@ def test_nvfp4_decode_config2_full_size(shape_idx, m):
     w = synth.config2_weight(shape_idx)
     x = synth.config2_x(shape_idx, m)
     a, b = synth.config2_lora(shape_idx)
-    rows_n = np.unique(np.concatenate([np.arange(0, n, max(1, n // 509)), [n - 1]]))
+    rows_n = _sample(n, 512, 1000 * shape_idx + m)
     _nvfp4_case(w, x, a, b, synth.CFG2["lora_scale"], rows_n=rows_n)
 
 
@@ -88,7 +97,11 @@ def test_nvfp4_skinny_ragged(m, n, k, r):
 
 
 @pytest.mark.parametrize("m,n,k,r", [(65, 130, 272, 8), (300, 512, 1040, 40), (256, 256, 512, 0), (257, 1024, 4096, 64),
-                                       (1100, 512, 2048, 48)])
+                                       (1100, 512, 2048, 48),
+                                       # 272 tiles: 256 whole tiles, then 16 tail tiles split along K
+                                       (4100, 4096, 256, 16),
+                                       # 256 tiles, all whole (no split tail)
+                                       (4096, 4096, 128, 0)])
 def test_nvfp4_gemm_ragged(m, n, k, r):
     g = np.random.default_rng(m * 1000 + n + k)
     w = synth.normal_bf16((n, k), 0.02, g, 0.01, 15.0)
@@ -106,12 +119,12 @@ def test_nvfp4_prefill_config3_full_size_sampled(shape_idx):
     x = synth.config3_x(shape_idx)
     a, b = synth.config3_lora(shape_idx)
     m = x.shape[0]
-    rows_m = np.unique(np.concatenate([np.arange(0, m, m // 128), [m - 1]]))
-    rows_n = np.unique(np.concatenate([np.arange(0, n, max(1, n // 257)), [n - 1]]))
+    rows_m = _sample(m, 128, 30 + shape_idx)
+    rows_n = _sample(n, 256, 40 + shape_idx)
     _nvfp4_case(w, x, a, b, synth.CFG3["lora_scale"], rows_m=rows_m, rows_n=rows_n)
 
 
-@pytest.mark.parametrize("li", [1, 3, 6])  # k 5120->1024, o 8192->5120, down 27648->5120
+@pytest.mark.parametrize("li", range(7))  # q, k, v, o, gate, up, down
 def test_nvfp4_policy_decode_m256_full_size_sampled(li):
     # one linear of the whole-policy decode step at its real size: 256 tokens, LoRA r32
     name, k, n = synth.CFG5_LINEARS[li]
@@ -122,8 +135,8 @@ def test_nvfp4_policy_decode_m256_full_size_sampled(li):
     x = synth.normal_bf16((c["M"], k), 1.0, g)
     a = synth.normal_bf16((c["rank"], k), 0.01, g)
     b = synth.normal_bf16((n, c["rank"]), 0.01, g)
-    rows_m = np.unique(np.concatenate([np.arange(0, c["M"], 3), [c["M"] - 1]]))
-    rows_n = np.unique(np.concatenate([np.arange(0, n, max(1, n // 257)), [n - 1]]))
+    rows_m = _sample(c["M"], 96, 50 + li)
+    rows_n = _sample(n, 256, 60 + li)
     _nvfp4_case(w, x, a, b, c["lora_scale"], rows_m=rows_m, rows_n=rows_n)
 
 
@@ -200,13 +213,15 @@ def test_fp8_small(m, n, k, r):
     _fp8_case(w, x, a, b, 2.0 if r else 0.0, prequant=True)
 
 
+@pytest.mark.parametrize("prequant", [True, False])
 @pytest.mark.parametrize("shape_idx", [0, 1])
-def test_fp8_config4_full_size_sampled(shape_idx):
+def test_fp8_config4_full_size_sampled(shape_idx, prequant):
+    # the GEMM on activations quantized beforehand, and the forward that quantizes them
     k, n = synth.CFG4_SHAPES[shape_idx]
-    print(f"forward config4 K={k} N={n}", flush=True)
+    print(f"forward config4 K={k} N={n} prequant={prequant}", flush=True)
     w = synth.config4_weight(shape_idx)
     x = synth.config4_x(shape_idx)
     m = x.shape[0]
-    rows_m = np.unique(np.concatenate([np.arange(0, m, m // 128), [m - 1]]))
-    rows_n = np.unique(np.concatenate([np.arange(0, n, max(1, n // 131)), [n - 1]]))
-    _fp8_case(w, x, rows_m=rows_m, rows_n=rows_n, prequant=True)
+    rows_m = _sample(m, 128, 70 + shape_idx)
+    rows_n = _sample(n, 192, 80 + shape_idx)
+    _fp8_case(w, x, rows_m=rows_m, rows_n=rows_n, prequant=prequant)

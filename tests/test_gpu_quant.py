@@ -93,12 +93,18 @@ def test_nvfp4_nonfinite_sets_status():
 
 
 @pytest.mark.parametrize("shape_idx", [0, 1, 2, 3])
-def test_nvfp4_decode_weights_full_size_sampled_rows(shape_idx):
+def test_nvfp4_decode_weights_full_size(shape_idx):
     k, n = synth.CFG2_SHAPES[shape_idx]
-    print(f"nvfp4 config2 weight {n}x{k}", flush=True)
-    w = synth.config2_weight(shape_idx)
-    rows = np.unique(np.concatenate([np.arange(0, n, max(1, n // 97)), [n - 1]]))
-    _check_nvfp4(w, rows)
+    print(f"nvfp4 config2 weight {n}x{k} (every byte)", flush=True)
+    _check_nvfp4(synth.config2_weight(shape_idx))
+
+
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_nvfp4_prefill_weights_full_size(shape_idx):
+    # the 32B-class MLP weights of the prefill workload, every code and scale byte
+    k, n = synth.CFG3_SHAPES[shape_idx]
+    print(f"nvfp4 config3 weight {n}x{k} (every byte)", flush=True)
+    _check_nvfp4(synth.config3_weight(shape_idx))
 
 
 def test_nvfp4_determinism():
@@ -135,9 +141,24 @@ def test_fp8_weight_round_trip_tile():
     _check_fp8_weight(codecs.f32_to_bf16_bits_rne(w))
 
 
-def test_fp8_weight_full_size_slab():
-    w = synth.config4_weight(1)[:1024]       # 1024 x 14336 slab of the 4096 x 14336 weight
-    _check_fp8_weight(w)
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_fp8_weight_full_size(shape_idx):
+    # both weights of the FP8 recipe's MLP workload, every code and scale
+    k, n = synth.CFG4_SHAPES[shape_idx]
+    print(f"fp8 config4 weight {n}x{k} (every byte)", flush=True)
+    _check_fp8_weight(synth.config4_weight(shape_idx))
+
+
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_fp8_act_full_size(shape_idx):
+    k, _ = synth.CFG4_SHAPES[shape_idx]
+    print(f"fp8 config4 activations 8192x{k} (every byte)", flush=True)
+    x = synth.config4_x(shape_idx)
+    xq, sx = ql.quantize_act_fp8(to_dev(x))
+    torch.cuda.synchronize()
+    rq, rs = ofp8.quantize_act(x)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), rq)
 
 
 @pytest.mark.parametrize("m,k", [(1, 128), (7, 512), (300, 4096)])

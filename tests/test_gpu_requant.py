@@ -1,6 +1,8 @@
 """GPU parity of the whole-policy requantization (recalibration after every training
 step, mexc.co NeMo RL FP8 page, "Praktische prestatiewinsten"): every tensor's codes,
 scales and tensor scale must equal the oracle's per-tensor quantizer bit for bit."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -78,7 +80,29 @@ def test_requant_nonfinite_sets_status():
     dev = [to_dev(t) for t in ts]
     qs = [ql.NVFP4Weight.empty(*t.shape) for t in ts]
     table = ql.RequantTable(list(zip(dev, qs)), ql.QL_NVFP4)
-    status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    table.requantize_all(status)
+    table.requantize_all()
     torch.cuda.synchronize()
-    assert status.item() & 1
+    assert table.status() & ql.binding.QLINEAR_STATUS_NONFINITE
+
+
+def test_requant_bad_item_is_skipped_and_reported():
+    # items are checked on the device: a misaligned or misshaped one is skipped, its outputs
+    # untouched, the others requantized as usual, and the status word says so
+    ts = _tensors(5, [(128, 256), (64, 512), (256, 128)])
+    dev = [to_dev(t) for t in ts]
+    qs = [ql.NVFP4Weight.empty(*t.shape) for t in ts]
+    pairs = list(zip(dev, qs))
+    img = bytearray(ql.binding.requant_items_bytes([(w, q.qweight()) for w, q in pairs]))
+    item = ql.binding.RequantItem.from_buffer(img, ctypes.sizeof(ql.binding.RequantItem))  # item 1
+    item.q.k = 500                       # not a multiple of 16
+    items = torch.frombuffer(img, dtype=torch.uint8).to(DEV)
+    ws = torch.zeros(ql.binding.qlinear_requant_workspace(3), dtype=torch.uint8, device=DEV)
+    qs[1].codes.fill_(0x5A)
+    ql.binding.qlinear_requantize_all(items, 3, ql.QL_NVFP4, ws)
+    torch.cuda.synchronize()
+    assert ql.workspace_status(ws) == ql.binding.QLINEAR_STATUS_BAD_ITEM
+    assert int(torch.count_nonzero(qs[1].codes != 0x5A).item()) == 0
+    for i in (0, 2):
+        c, sc, S = onv.quantize(ts[i])
+        assert np.array_equal(qs[i].codes.cpu().numpy(), c) and np.array_equal(qs[i].scales.cpu().numpy(), sc)
+        assert qs[i].tensor_scale.item() == float(S)
