@@ -206,6 +206,24 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
                                             int32_t out_dtype, void* ws, size_t ws_bytes,
                                             void* stream);
 
+/* Allocation-free variant of qlinear_forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, checks, kernels and results as qlinear_forward, without
+ * ws/ws_bytes: the library's own device array of QLINEAR_NOALLOC_MAX_BYTES per GPU (held
+ * until the process ends) serves as the workspace.  Calls whose
+ * qlinear_forward_workspace(...) exceeds that size return QL_ERR_WORKSPACE and enqueue
+ * nothing (decode-size calls fit; large prefill and FP8 GEMMs do not).  The first call on
+ * each device sets the array up synchronously and must not be made under stream capture
+ * (QL_ERR_ARG); later calls allocate nothing and may be captured.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (different streams without
+ * ordering, several host threads) race and give wrong results.  The array's status word
+ * is not exposed: a timed-out wait shows as NaN outputs. */
+#define QLINEAR_NOALLOC_MAX_BYTES (((size_t)32) << 20)
+qlinear_status qlinear_forward_noalloc(const qlinear_qweight* w, const uint16_t* x, int64_t m,
+                                       const uint16_t* lora_a, const uint16_t* lora_b,
+                                       int32_t rank, float lora_scale, void* y,
+                                       int32_t out_dtype, void* stream);
+
 /* Workspace sizes (0 for invalid arguments and for shapes the kernels cannot run). */
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank);
 size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);

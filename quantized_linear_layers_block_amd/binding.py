@@ -31,10 +31,12 @@ EXPORTS = [
     "qlinear_requant_workspace",
     "qlinear_requantize_all",
     "qlinear_status_word",
+    "qlinear_forward_noalloc",
 ]
 
 QLINEAR_STATUS_NONFINITE, QLINEAR_STATUS_TIMEOUT, QLINEAR_STATUS_BAD_ITEM = 1, 2, 4
 QLINEAR_WS_RESERVED_BYTES = 131072
+QLINEAR_NOALLOC_MAX_BYTES = 32 << 20
 
 
 class QlinearError(RuntimeError):
@@ -74,6 +76,7 @@ def _load():
         "qlinear_requant_workspace": ([i32], sz),
         "qlinear_requantize_all": ([vp, i32, i32, vp, sz, vp], i32),
         "qlinear_status_word": ([vp], vp),
+        "qlinear_forward_noalloc": ([ctypes.POINTER(QWeight), vp, i64, vp, vp, i32, f32, vp, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -155,6 +158,15 @@ def qlinear_forward(qw, x, y, out_dtype, ws=None, lora_a=None, lora_b=None, rank
     _check(LIB.qlinear_forward(ctypes.byref(qw), _ptr(x), m, _ptr(lora_a), _ptr(lora_b), rank,
                                float(lora_scale), _ptr(y), out_dtype, _ptr(ws), wsb, _stream(stream)),
            "qlinear_forward")
+
+
+def qlinear_forward_noalloc(qw, x, y, out_dtype, lora_a=None, lora_b=None, rank=0, lora_scale=0.0,
+                            stream=None):
+    """qlinear_forward on the library's own device array instead of a workspace."""
+    m = x.shape[0]
+    _check(LIB.qlinear_forward_noalloc(ctypes.byref(qw), _ptr(x), m, _ptr(lora_a), _ptr(lora_b), rank,
+                                       float(lora_scale), _ptr(y), out_dtype, _stream(stream)),
+           "qlinear_forward_noalloc")
 
 
 def qlinear_forward_fp8_prequant(qw, xq, sx, y, out_dtype, ws=None, x=None, lora_a=None, lora_b=None,

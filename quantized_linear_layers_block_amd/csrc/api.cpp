@@ -169,10 +169,13 @@ static qlinear_status check_forward_ws(const qlinear_qweight* w, int64_t m, int3
   return QL_OK;
 }
 
-qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int64_t m,
-                               const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
-                               float lora_scale, void* y, int32_t out_dtype, void* ws,
-                               size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The body of qlinear_forward, also behind the allocation-free variant (noalloc.hip).
+qlinear_status ql::forward_impl(const qlinear_qweight* w, const uint16_t* x, int64_t m,
+                                const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
+                                float lora_scale, void* y, int32_t out_dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
   qlinear_status st = check_forward_common(w, m, lora_a, lora_b, rank, y, out_dtype);
   if (st != QL_OK) return st;
   if (!x) return QL_ERR_NULL;
@@ -212,6 +215,15 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
     return QL_ERR_HIP;
   return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes,
                                         (const float*)w->scales, t, lora_b, r, y, out_f32, s));
+}
+
+extern "C" {
+
+qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int64_t m,
+                               const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
+                               float lora_scale, void* y, int32_t out_dtype, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return ql::forward_impl(w, x, m, lora_a, lora_b, rank, lora_scale, y, out_dtype, ws, ws_bytes, stream);
 }
 
 qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint8_t* xq,

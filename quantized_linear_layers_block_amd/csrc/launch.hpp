@@ -6,7 +6,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/qlinear.h"
+
 namespace ql {
+
+// qlinear_forward's checks and dispatch (api.cpp), shared with the allocation-free variant.
+qlinear_status forward_impl(const qlinear_qweight* w, const uint16_t* x, int64_t m,
+                            const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,
+                            float lora_scale, void* y, int32_t out_dtype, void* ws, size_t ws_bytes,
+                            void* stream);
 
 // ---- forward workspace layout, shared by every path
 // [0, kWsReserved): the status word (int32 at offset 0) and, from kWsCounterOff on, the
