@@ -138,3 +138,36 @@ def test_rel_err_inf():
     r = np.array([[1.0, -4.0], [2.0, 0.0]])
     assert gemm.rel_err_inf(r, r) == 0
     assert gemm.rel_err_inf(r + 0.04, r) == pytest.approx(0.01)
+
+
+# ------------------------------------------------ unquantized reference (error report)
+
+@pytest.mark.parametrize("m,n,k,r", [(2, 3, 16, 2), (1, 4, 32, 0)])
+def test_bf16_reference_matches_exact_arithmetic(m, n, k, r):
+    # forward_bf16_reference is only used to report the quantization error; it is pinned
+    # here against the layer's definition in exact rational arithmetic on the bf16 values
+    w = rnd(11, (n, k), 0.05)
+    x = rnd(12, (m, k), 1.0)
+    a = rnd(13, (r, k), 0.01) if r else None
+    b = rnd(14, (n, r), 0.01) if r else None
+    y = gemm.forward_bf16_reference(x, w, a, b, 2.0 if r else 0.0)
+    W, X = frac(w), frac(x)
+    A = frac(a) if r else None
+    B = frac(b) if r else None
+    for i in range(m):
+        for j in range(n):
+            want = sum(X[i][kk] * W[j][kk] for kk in range(k))
+            if r:
+                t = [sum(X[i][kk] * A[q][kk] for kk in range(k)) for q in range(r)]
+                want += 2 * sum(t[q] * B[j][q] for q in range(r))
+            assert abs(Fraction(float(y[i, j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+
+
+def test_bf16_reference_one_hot_returns_a_weight_column():
+    w = rnd(15, (6, 32), 0.05)
+    x = np.zeros((1, 32), np.uint16)
+    x[0, 7] = bf16(1.0)
+    y = gemm.forward_bf16_reference(x, w)
+    assert np.array_equal(y[0], codecs.bf16_bits_to_f32(w)[:, 7].astype(np.float64))
+    # and a transposed weight (rows and columns swapped) would not give it
+    assert not np.array_equal(y[0], codecs.bf16_bits_to_f32(w)[7 % 6, :6].astype(np.float64))
