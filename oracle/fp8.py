@@ -75,3 +75,63 @@ def dequantize_act(codes, scales):
     v = e4m3_decode(codes)
     s = np.repeat(np.asarray(scales, np.float64), 128, axis=1)
     return v * s
+
+
+# ------------------------------------------------------------ power-of-two scales
+#
+# Source: the same page, closing section: advanced users can switch the recipe to
+# power-of-two scale factors.  Readings: the block scale becomes the smallest power of
+# two 2^e that still keeps the block within E4M3's range, i.e. the smallest integer e
+# with amax <= 448 * 2^e (e = 0 for an all-zero block), clamped to [-127, 127], the
+# range of an E8M0 scale byte, which stores e + 127.  Elements are coded exactly as
+# above, sign | E4M3(fl32(|w| / 2^e)) -- a division by a power of two, exact here.
+# Blocks are the same 128 x 128 weight tiles and 1 x 128 activation segments.
+
+E8M0_BIAS = 127
+
+
+def pow2_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e, for amax >= 0 (0 for amax == 0), clamped
+    to [-127, 127].  frexp splits amax = f * 2^E exactly with f in [0.5, 1); since
+    448 = 0.875 * 2^9, the answer is E - 9 when f <= 0.875 and E - 8 otherwise."""
+    a = np.asarray(amax, np.float64)
+    f, E = np.frexp(a)
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.where(a == 0, 0, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def e8m0_decode(b):
+    """E8M0 scale bytes -> float64 2^(b - 127) (0xFF, NaN in the format, is never written)."""
+    return np.ldexp(1.0, np.asarray(b).astype(np.int64) - E8M0_BIAS)
+
+
+def _quantize_blocks_pow2(w_bits, bn, bk):
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    if w_bits.ndim != 2:
+        raise ValueError("expected a 2-D tensor")
+    n, k = w_bits.shape
+    if n % bn or k % bk:
+        raise ValueError(f"shape {w_bits.shape} is not a multiple of the {bn}x{bk} block")
+    w = bf16_bits_to_f32(w_bits)
+    if not np.isfinite(w).all():
+        raise ValueError("non-finite values have no FP8 encoding")
+    wb = w.reshape(n // bn, bn, k // bk, bk)
+    mag = np.abs(wb)
+    e = pow2_exponent(mag.max(axis=(1, 3)))                  # [N/bn, K/bk]
+    s = np.ldexp(F32(1.0), e).astype(F32)
+    with np.errstate(under="ignore"):
+        q = (mag / s[:, None, :, None]).astype(F32)
+    code = e4m3_encode_magnitude(q)
+    code = code | (np.signbit(wb).astype(np.uint8) << 7)
+    return code.reshape(n, k).astype(np.uint8), (e + E8M0_BIAS).astype(np.uint8)
+
+
+def quantize_weight_pow2(w_bits):
+    """W bf16 bits [N, K] -> (codes uint8 [N, K], E8M0 scale bytes uint8 [N/128, K/128])."""
+    return _quantize_blocks_pow2(w_bits, 128, 128)
+
+
+def quantize_act_pow2(x_bits):
+    """x bf16 bits [M, K] -> (codes uint8 [M, K], E8M0 scale bytes uint8 [M, K/128])."""
+    return _quantize_blocks_pow2(x_bits, 1, 128)

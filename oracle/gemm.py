@@ -63,6 +63,18 @@ def forward_fp8_from_bf16(x_bits, wq, sw, a_bits=None, b_bits=None, lora_scale=0
     return forward_fp8(xq, sx, wq, sw, x_bits, a_bits, b_bits, lora_scale)
 
 
+def forward_fp8_pow2(xq, ex, wq, ew, x_bits=None, a_bits=None, b_bits=None, lora_scale=0.0):
+    """The FP8 layer with power-of-two block scales given as E8M0 bytes (ex [M, K/128],
+    ew [N/128, K/128]): forward_fp8 with the scales 2^(byte - 127)."""
+    return forward_fp8(xq, _fp8.e8m0_decode(ex), wq, _fp8.e8m0_decode(ew), x_bits, a_bits, b_bits, lora_scale)
+
+
+def forward_fp8_pow2_from_bf16(x_bits, wq, ew, a_bits=None, b_bits=None, lora_scale=0.0):
+    """The power-of-two FP8 layer on bf16 activations (quantized per 1x128 segment)."""
+    xq, ex = _fp8.quantize_act_pow2(x_bits)
+    return forward_fp8_pow2(xq, ex, wq, ew, x_bits, a_bits, b_bits, lora_scale)
+
+
 def forward_bf16_reference(x_bits, w_bits, a_bits=None, b_bits=None, lora_scale=0.0):
     """The unquantized layer (x W^T + LoRA) in float64, for reporting quantization error only."""
     y = _f64(x_bits) @ _f64(w_bits).T
