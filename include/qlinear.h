@@ -66,7 +66,7 @@ typedef enum {
   QL_ERR_ARG = 7        /* another invalid argument (rank, count, ...)              */
 } qlinear_status;
 
-typedef enum { QL_NVFP4 = 1, QL_FP8_BLOCK128 = 2 } qlinear_format;
+typedef enum { QL_NVFP4 = 1, QL_FP8_BLOCK128 = 2, QL_FP8_POW2 = 3 } qlinear_format;
 typedef enum { QL_OUT_BF16 = 1, QL_OUT_F32 = 2 } qlinear_out;
 
 /* A quantized weight W [n, k] (host struct holding device pointers).
@@ -75,8 +75,13 @@ typedef enum { QL_OUT_BF16 = 1, QL_OUT_F32 = 2 } qlinear_out;
  *                    tensor_scale f32[1]  the FP32 tensor scale S
  *                    requires k % 16 == 0
  *   QL_FP8_BLOCK128: codes  u8 [n][k]     E4M3
- *                    scales f32 [n/128][k/128]  dequantization multipliers
- *                    tensor_scale NULL;   requires n % 128 == 0 and k % 128 == 0  */
+ *                    scales f32 [n/128][k/128]  dequantization multipliers amax/448
+ *                    tensor_scale NULL;   requires n % 128 == 0 and k % 128 == 0
+ *   QL_FP8_POW2:     the FP8 recipe with its power-of-two scale option (mexc.co NeMo RL
+ *                    FP8 page, closing section): as QL_FP8_BLOCK128, but
+ *                    scales u8 [n/128][k/128]  E8M0 bytes e + 127 of the scale 2^e, e the
+ *                    smallest integer with amax <= 448 * 2^e (0 for a zero block),
+ *                    clamped to [-127, 127]; activations get the same 1x128 rule.  */
 typedef struct {
   int32_t format;
   int32_t reserved;
@@ -148,6 +153,14 @@ qlinear_status qlinear_quantize_fp8_block(const uint16_t* w, int64_t n, int64_t 
 qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
                                         uint8_t* xq, float* sx, void* stream);
 
+/* The power-of-two variants of the two FP8 quantizers above (QL_FP8_POW2): scales are
+ * E8M0 bytes, u8 [n/128][k/128] for weights and u8 [m][k/128] for activations; codes are
+ * sign | E4M3(fl32(|v| / 2^e)).  Errors as their float-scale counterparts. */
+qlinear_status qlinear_quantize_fp8_pow2(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                         uint8_t* scales, int32_t* status_word, void* stream);
+qlinear_status qlinear_quantize_act_fp8_pow2(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
+                                             uint8_t* sx, void* stream);
+
 /* Size in bytes of the workspace qlinear_quantize_nvfp4 needs (0 for FP8). */
 size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
 
@@ -169,7 +182,9 @@ size_t qlinear_quantize_workspace(int32_t format, int64_t n, int64_t k);
  * scaled by a power of two that puts its largest magnitude in [2^14, 2^15) (exact but
  * for magnitudes below about 2^-29 of the row maximum), and f16 MFMA is used.
  * FP8: x is quantized per 1x128 segment into the workspace, then an FP8 MFMA GEMM
- * rescales each 128-deep partial sum by sx * sw.
+ * rescales each 128-deep partial sum by sx * sw.  QL_FP8_POW2: the same with power-of-two
+ * scales, which the scaled MFMA applies itself (E8M0 operand scales), so partial sums
+ * accumulate directly.
  * The LoRA intermediate s*t is rounded to bf16 before the up-projection.
  *
  * Workspace: qlinear_forward_workspace(format, m, n, k, rank) bytes, 16-byte aligned,
@@ -195,12 +210,13 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
 
 /* FP8 layer on activations already quantized by qlinear_quantize_act_fp8 (the FP8 GEMM
  * of the recipe, same page and section, without the activation step): xq u8 [m][k],
- * sx f32 [m][k/128].  x (bf16 [m][k]) is read only for the LoRA term and may be NULL
- * when there is none.  Workspace: qlinear_forward_prequant_workspace(m, n, k, rank)
- * bytes, with the same layout and rules as qlinear_forward's.  Errors as
- * qlinear_forward, plus QL_ERR_FORMAT if w is not QL_FP8_BLOCK128. */
+ * sx f32 [m][k/128] (QL_FP8_BLOCK128) or E8M0 u8 [m][k/128] from
+ * qlinear_quantize_act_fp8_pow2 (QL_FP8_POW2).  x (bf16 [m][k]) is read only for the LoRA
+ * term and may be NULL when there is none.  Workspace:
+ * qlinear_forward_prequant_workspace(m, n, k, rank) bytes, with the same layout and rules
+ * as qlinear_forward's.  Errors as qlinear_forward, plus QL_ERR_FORMAT if w is not FP8. */
 qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint8_t* xq,
-                                            const float* sx, int64_t m, const uint16_t* x,
+                                            const void* sx, int64_t m, const uint16_t* x,
                                             const uint16_t* lora_a, const uint16_t* lora_b,
                                             int32_t rank, float lora_scale, void* y,
                                             int32_t out_dtype, void* ws, size_t ws_bytes,
@@ -248,6 +264,44 @@ size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32
 qlinear_status qlinear_requantize_all(const qlinear_requant_item* items, int32_t count,
                                       int32_t format, void* ws, size_t ws_bytes, void* stream);
 size_t qlinear_requant_workspace(int32_t count);
+
+/* The training step's update fused with the requantization that follows it (same page and
+ * section: the weights change every step, the scales are recalibrated after each).
+ * deltas: DEVICE array of `count` pointers to dense bf16 updates, deltas[i] [n_i][k_i]
+ * (16-byte aligned).  Each weight is replaced in place, through items[i].w, by
+ * bf16_RNE(fl32(W) + fl32(delta)) and requantized in `format` exactly as
+ * qlinear_requantize_all would requantize the new weights -- but the update pass also
+ * takes the maxima (NVFP4) or does the whole FP8 tile, so only one more pass (the NVFP4
+ * encode) reads the new weights.  Workspace, status word and errors as
+ * qlinear_requantize_all; an item whose delta is NULL or misaligned is skipped (weight
+ * untouched) and sets QLINEAR_STATUS_BAD_ITEM. */
+qlinear_status qlinear_update_requantize_all(const qlinear_requant_item* items,
+                                             const uint16_t* const* deltas, int32_t count,
+                                             int32_t format, void* ws, size_t ws_bytes,
+                                             void* stream);
+
+/* ------------------------------------------------------------ FP8 KV cache */
+
+/* FP8 KV-cache codec (mexc.co NeMo RL FP8 page, "Praktische prestatiewinsten": FP8
+ * extended to the KV cache).  Each (token, head) vector of head_dim elements gets one
+ * float32 scale s = amax/448 and E4M3 codes sign | E4M3(fl32(|v| / s)) -- the recipe's
+ * 1 x 128 activation rule applied per vector.
+ * Store: kv bf16 [tokens][heads][head_dim] -> cache_codes u8 [cache_slots][heads][head_dim]
+ * and cache_scales f32 [cache_slots][heads] at rows slots[t] (int64, device, distinct).
+ * Load: rows slots[t] of the cache -> out bf16 [tokens][heads][head_dim], each element
+ * bf16_RNE(fl32(E4M3(code) * s)).
+ * head_dim must be a power of two in [16, 512].  A slot outside [0, cache_slots) is skipped
+ * (a load writes zeros for it) and sets QLINEAR_STATUS_BAD_ITEM in *status_word (if not
+ * NULL).  Errors: QL_ERR_NULL, QL_ERR_SHAPE (tokens < 0, heads <= 0, head_dim,
+ * cache_slots <= 0, sizes beyond QLINEAR_MAX_ELEMS), QL_ERR_ALIGN.  tokens == 0 launches
+ * nothing. */
+qlinear_status qlinear_kv_store_fp8(const uint16_t* kv, int64_t tokens, int32_t heads, int32_t head_dim,
+                                    const int64_t* slots, uint8_t* cache_codes, float* cache_scales,
+                                    int64_t cache_slots, int32_t* status_word, void* stream);
+qlinear_status qlinear_kv_load_fp8(const uint8_t* cache_codes, const float* cache_scales,
+                                   int64_t cache_slots, const int64_t* slots, int64_t tokens,
+                                   int32_t heads, int32_t head_dim, uint16_t* out,
+                                   int32_t* status_word, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,11 +14,12 @@ from dataclasses import dataclass
 import torch
 
 from . import binding
-from .binding import (QL_FP8_BLOCK128, QL_NVFP4, QL_OUT_BF16, QL_OUT_F32, QlinearError,  # noqa: F401
-                      make_qweight)
+from .binding import (QL_FP8_BLOCK128, QL_FP8_POW2, QL_NVFP4, QL_OUT_BF16, QL_OUT_F32,  # noqa: F401
+                      QlinearError, make_qweight)
 
 __all__ = ["NVFP4Weight", "FP8Weight", "quantize_nvfp4", "quantize_fp8_block", "quantize_act_fp8",
-           "forward", "forward_fp8_prequant", "RequantTable", "QlinearError", "binding", "workspace_status"]
+           "forward", "forward_fp8_prequant", "RequantTable", "QlinearError", "binding", "workspace_status",
+           "quantize_fp8_pow2", "kv_store_fp8", "kv_load_fp8"]
 
 
 def _dev(t):
@@ -48,17 +49,20 @@ class NVFP4Weight:
 @dataclass
 class FP8Weight:
     codes: torch.Tensor   # uint8 [n, k] (E4M3)
-    scales: torch.Tensor  # float32 [n/128, k/128]
+    scales: torch.Tensor  # float32 [n/128, k/128], or uint8 E8M0 bytes with pow2
     n: int
     k: int
+    pow2: bool = False    # power-of-two block scales (QL_FP8_POW2)
 
     def qweight(self):
-        return make_qweight(QL_FP8_BLOCK128, self.n, self.k, self.codes, self.scales, None)
+        return make_qweight(QL_FP8_POW2 if self.pow2 else QL_FP8_BLOCK128, self.n, self.k, self.codes,
+                            self.scales, None)
 
     @staticmethod
-    def empty(n, k, device="cuda"):
+    def empty(n, k, device="cuda", pow2=False):
         return FP8Weight(torch.empty((n, k), dtype=torch.uint8, device=device),
-                         torch.empty((n // 128, k // 128), dtype=torch.float32, device=device), n, k)
+                         torch.empty((n // 128, k // 128), dtype=torch.uint8 if pow2 else torch.float32,
+                                     device=device), n, k, pow2)
 
 
 def _u16(t):
@@ -94,17 +98,27 @@ def quantize_fp8_block(w, out=None, status_word=None):
     return q
 
 
-def quantize_act_fp8(x):
+def quantize_fp8_pow2(w, out=None, status_word=None):
+    _dev(_u16(w))
+    n, k = w.shape
+    q = out if out is not None else FP8Weight.empty(n, k, w.device, pow2=True)
+    binding.qlinear_quantize_fp8_pow2(w, q.codes, q.scales, status_word)
+    return q
+
+
+def quantize_act_fp8(x, pow2=False):
     _dev(_u16(x))
     m, k = x.shape
     xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    sx = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
-    binding.qlinear_quantize_act_fp8(x, xq, sx)
+    sx = torch.empty((m, k // 128), dtype=torch.uint8 if pow2 else torch.float32, device=x.device)
+    (binding.qlinear_quantize_act_fp8_pow2 if pow2 else binding.qlinear_quantize_act_fp8)(x, xq, sx)
     return xq, sx
 
 
 def _fmt(qw):
-    return QL_NVFP4 if isinstance(qw, NVFP4Weight) else QL_FP8_BLOCK128
+    if isinstance(qw, NVFP4Weight):
+        return QL_NVFP4
+    return QL_FP8_POW2 if qw.pow2 else QL_FP8_BLOCK128
 
 
 def forward(qw, x, lora_a=None, lora_b=None, lora_scale=0.0, out_dtype=torch.bfloat16, out=None, ws=None):
@@ -150,6 +164,30 @@ class RequantTable:
     def requantize_all(self):
         binding.qlinear_requantize_all(self.items, len(self.pairs), self.fmt, self.ws)
 
+    def set_updates(self, deltas):
+        """Device pointer array of one dense bf16 update per tensor (kept alive here)."""
+        self.deltas = list(deltas)
+        ptrs = torch.tensor([d.data_ptr() for d in self.deltas], dtype=torch.int64)
+        self.delta_ptrs = ptrs.to(self.ws.device)
+
+    def update_requantize_all(self):
+        """W <- bf16(W + delta) for every tensor, fused with the requantization."""
+        binding.qlinear_update_requantize_all(self.items, self.delta_ptrs, len(self.pairs), self.fmt, self.ws)
+
     def status(self):
         """The workspace's status word (QLINEAR_STATUS_* bits); synchronises."""
         return int(self.ws[:4].view(torch.int32).item())
+
+
+def kv_store_fp8(kv, slots, cache_codes, cache_scales, status_word=None):
+    """Store bf16 kv [T, H, D] into FP8 cache rows slots[t] (codes u8 [S, H, D], scales f32 [S, H])."""
+    binding.qlinear_kv_store_fp8(_dev(_u16(kv)), slots, cache_codes, cache_scales, status_word)
+
+
+def kv_load_fp8(cache_codes, cache_scales, slots, heads=None, status_word=None):
+    """Load cache rows `slots` back to bf16 [T, H, D]."""
+    t = slots.shape[0]
+    out = torch.empty((t, cache_codes.shape[1], cache_codes.shape[2]), dtype=torch.bfloat16,
+                      device=cache_codes.device)
+    binding.qlinear_kv_load_fp8(cache_codes, cache_scales, slots, out, status_word)
+    return out

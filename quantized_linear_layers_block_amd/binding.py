@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqlinear.so")
 
 QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_FORMAT, QL_ERR_WORKSPACE, QL_ERR_HIP, QL_ERR_ARG = range(8)
-QL_NVFP4, QL_FP8_BLOCK128 = 1, 2
+QL_NVFP4, QL_FP8_BLOCK128, QL_FP8_POW2 = 1, 2, 3
 QL_OUT_BF16, QL_OUT_F32 = 1, 2
 
 # every symbol include/qlinear.h declares
@@ -32,6 +32,11 @@ EXPORTS = [
     "qlinear_requantize_all",
     "qlinear_status_word",
     "qlinear_forward_noalloc",
+    "qlinear_quantize_fp8_pow2",
+    "qlinear_quantize_act_fp8_pow2",
+    "qlinear_update_requantize_all",
+    "qlinear_kv_store_fp8",
+    "qlinear_kv_load_fp8",
 ]
 
 QLINEAR_STATUS_NONFINITE, QLINEAR_STATUS_TIMEOUT, QLINEAR_STATUS_BAD_ITEM = 1, 2, 4
@@ -77,6 +82,11 @@ def _load():
         "qlinear_requantize_all": ([vp, i32, i32, vp, sz, vp], i32),
         "qlinear_status_word": ([vp], vp),
         "qlinear_forward_noalloc": ([ctypes.POINTER(QWeight), vp, i64, vp, vp, i32, f32, vp, i32, vp], i32),
+        "qlinear_quantize_fp8_pow2": ([vp, i64, i64, vp, vp, vp, vp], i32),
+        "qlinear_quantize_act_fp8_pow2": ([vp, i64, i64, vp, vp, vp], i32),
+        "qlinear_update_requantize_all": ([vp, vp, i32, i32, vp, sz, vp], i32),
+        "qlinear_kv_store_fp8": ([vp, i64, i32, i32, vp, vp, vp, i64, vp, vp], i32),
+        "qlinear_kv_load_fp8": ([vp, vp, i64, vp, i64, i32, i32, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -127,6 +137,20 @@ def qlinear_quantize_fp8_block(w, codes, scales, status_word=None, stream=None):
     n, k = w.shape
     _check(LIB.qlinear_quantize_fp8_block(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(status_word),
                                           _stream(stream)), "qlinear_quantize_fp8_block")
+
+
+def qlinear_quantize_fp8_pow2(w, codes, scales, status_word=None, stream=None):
+    """w bf16 [n,k] -> codes u8 [n,k], E8M0 scale bytes u8 [n/128, k/128]."""
+    n, k = w.shape
+    _check(LIB.qlinear_quantize_fp8_pow2(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(status_word),
+                                         _stream(stream)), "qlinear_quantize_fp8_pow2")
+
+
+def qlinear_quantize_act_fp8_pow2(x, xq, sx, stream=None):
+    """x bf16 [m,k] -> xq u8 [m,k], E8M0 scale bytes u8 [m, k/128]."""
+    m, k = x.shape
+    _check(LIB.qlinear_quantize_act_fp8_pow2(_ptr(x), m, k, _ptr(xq), _ptr(sx), _stream(stream)),
+           "qlinear_quantize_act_fp8_pow2")
 
 
 def qlinear_quantize_act_fp8(x, xq, sx, stream=None):
@@ -198,6 +222,31 @@ def qlinear_requantize_all(items_dev, count, fmt, ws, stream=None):
     """items_dev: device tensor holding `count` qlinear_requant_item entries."""
     _check(LIB.qlinear_requantize_all(_ptr(items_dev), count, fmt, _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream)), "qlinear_requantize_all")
+
+
+def qlinear_update_requantize_all(items_dev, deltas_dev, count, fmt, ws, stream=None):
+    """deltas_dev: device tensor holding `count` pointers (int64) to the bf16 updates."""
+    _check(LIB.qlinear_update_requantize_all(_ptr(items_dev), _ptr(deltas_dev), count, fmt, _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)),
+           "qlinear_update_requantize_all")
+
+
+# -------------------------------------------------------------------- KV cache
+
+def qlinear_kv_store_fp8(kv, slots, cache_codes, cache_scales, status_word=None, stream=None):
+    """kv bf16 [T, H, D] -> cache rows slots[t] of codes u8 [S, H, D] and scales f32 [S, H]."""
+    t, h, d = kv.shape
+    _check(LIB.qlinear_kv_store_fp8(_ptr(kv), t, h, d, _ptr(slots), _ptr(cache_codes), _ptr(cache_scales),
+                                    cache_codes.shape[0], _ptr(status_word), _stream(stream)),
+           "qlinear_kv_store_fp8")
+
+
+def qlinear_kv_load_fp8(cache_codes, cache_scales, slots, out, status_word=None, stream=None):
+    """cache rows slots[t] -> out bf16 [T, H, D]."""
+    t, h, d = out.shape
+    _check(LIB.qlinear_kv_load_fp8(_ptr(cache_codes), _ptr(cache_scales), cache_codes.shape[0], _ptr(slots), t,
+                                   h, d, _ptr(out), _ptr(status_word), _stream(stream)),
+           "qlinear_kv_load_fp8")
 
 
 def qlinear_status_word(ws):

@@ -24,9 +24,11 @@ bool elems_ok(int64_t n, int64_t k) {
   return n > 0 && k > 0 && n <= QLINEAR_MAX_ELEMS / k;
 }
 
+bool is_fp8(int32_t format) { return format == QL_FP8_BLOCK128 || format == QL_FP8_POW2; }
+
 qlinear_status check_qweight(const qlinear_qweight* w) {
   if (!w) return QL_ERR_NULL;
-  if (w->format != QL_NVFP4 && w->format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
+  if (w->format != QL_NVFP4 && !is_fp8(w->format)) return QL_ERR_FORMAT;
   if (!w->codes || !w->scales) return QL_ERR_NULL;
   if (!elems_ok(w->n, w->k)) return QL_ERR_SHAPE;
   if (w->format == QL_NVFP4) {
@@ -45,7 +47,11 @@ int32_t lora_rank(const uint16_t* a, const uint16_t* b, int32_t rank, float scal
   return (rank > 0 && a && b && scale != 0.0f) ? rank : 0;
 }
 
-size_t fp8_act_bytes(int64_t m, int64_t k) { return up((size_t)m * (size_t)k) + up((size_t)m * (size_t)(k / 128) * 4); }
+// FP8 activation codes and their scales (float32, or E8M0 bytes with power-of-two scales).
+size_t fp8_act_bytes(int32_t format, int64_t m, int64_t k) {
+  const size_t sb = format == QL_FP8_POW2 ? 1 : 4;
+  return up((size_t)m * (size_t)k) + up((size_t)m * (size_t)(k / 128) * sb);
+}
 
 // The NVFP4 path for m > 64: the f16 pre-pass GEMM when K allows it, else the generic one.
 bool nvfp4_f16_path(int64_t k) { return k % 64 == 0 && k < ql::kNvF16MaxK; }
@@ -63,9 +69,9 @@ size_t forward_scratch(int32_t format, int64_t m, int64_t n, int64_t k, int32_t 
     if (nvfp4_f16_path(k)) return up(ql::gemm_nvfp4_f16_workspace(m, n, k, rank));
     return up(ql::lora_down_bytes(m, k, rank));
   }
-  if (format == QL_FP8_BLOCK128) {
+  if (is_fp8(format)) {
     if (k >= ql::kFp8MaxK) return SIZE_MAX;
-    return (prequant ? 0 : fp8_act_bytes(m, k)) + up(ql::lora_down_bytes(m, k, rank));
+    return (prequant ? 0 : fp8_act_bytes(format, m, k)) + up(ql::lora_down_bytes(m, k, rank));
   }
   return SIZE_MAX;
 }
@@ -119,7 +125,18 @@ qlinear_status qlinear_quantize_fp8_block(const uint16_t* w, int64_t n, int64_t 
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) ||
       (status_word && ((uintptr_t)status_word & 3)))
     return QL_ERR_ALIGN;
-  return hip_status(ql::launch_fp8_weight_quantize(w, n, k, codes, scales, status_word,
+  return hip_status(ql::launch_fp8_weight_quantize(w, n, k, codes, scales, false, status_word,
+                                                   (hipStream_t)stream));
+}
+
+qlinear_status qlinear_quantize_fp8_pow2(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                         uint8_t* scales, int32_t* status_word, void* stream) {
+  if (!w || !codes || !scales) return QL_ERR_NULL;
+  if (!elems_ok(n, k) || n % 128 || k % 128) return QL_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) ||
+      (status_word && ((uintptr_t)status_word & 3)))
+    return QL_ERR_ALIGN;
+  return hip_status(ql::launch_fp8_weight_quantize(w, n, k, codes, scales, true, status_word,
                                                    (hipStream_t)stream));
 }
 
@@ -128,7 +145,15 @@ qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
   if (!x || !xq || !sx) return QL_ERR_NULL;
   if (!elems_ok(m, k) || k % 128) return QL_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return QL_ERR_ALIGN;
-  return hip_status(ql::launch_fp8_act_quantize(x, m, k, xq, sx, (hipStream_t)stream));
+  return hip_status(ql::launch_fp8_act_quantize(x, m, k, xq, sx, false, (hipStream_t)stream));
+}
+
+qlinear_status qlinear_quantize_act_fp8_pow2(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
+                                             uint8_t* sx, void* stream) {
+  if (!x || !xq || !sx) return QL_ERR_NULL;
+  if (!elems_ok(m, k) || k % 128) return QL_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return QL_ERR_ALIGN;
+  return hip_status(ql::launch_fp8_act_quantize(x, m, k, xq, sx, true, (hipStream_t)stream));
 }
 
 // --------------------------------------------------------------------- forward
@@ -206,15 +231,16 @@ qlinear_status ql::forward_impl(const qlinear_qweight* w, const uint16_t* x, int
   }
 
   // FP8: quantize activations per 1x128 segment, then the block-scaled GEMM.
+  const bool pow2 = w->format == QL_FP8_POW2;
   uint8_t* xq = (uint8_t*)scratch;
-  float* sx = (float*)(scratch + up((size_t)m * (size_t)w->k));
-  char* rest = scratch + fp8_act_bytes(m, w->k);
-  if (ql::launch_fp8_act_quantize(x, m, w->k, xq, sx, s) != hipSuccess) return QL_ERR_HIP;
+  void* sx = scratch + up((size_t)m * (size_t)w->k);
+  char* rest = scratch + fp8_act_bytes(w->format, m, w->k);
+  if (ql::launch_fp8_act_quantize(x, m, w->k, xq, sx, pow2, s) != hipSuccess) return QL_ERR_HIP;
   uint16_t* t = nullptr;
   if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, rest, &t, s) != hipSuccess)
     return QL_ERR_HIP;
-  return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes,
-                                        (const float*)w->scales, t, lora_b, r, y, out_f32, s));
+  return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes, w->scales, pow2, t,
+                                        lora_b, r, y, out_f32, s));
 }
 
 extern "C" {
@@ -227,14 +253,14 @@ qlinear_status qlinear_forward(const qlinear_qweight* w, const uint16_t* x, int6
 }
 
 qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint8_t* xq,
-                                            const float* sx, int64_t m, const uint16_t* x,
+                                            const void* sx, int64_t m, const uint16_t* x,
                                             const uint16_t* lora_a, const uint16_t* lora_b,
                                             int32_t rank, float lora_scale, void* y,
                                             int32_t out_dtype, void* ws, size_t ws_bytes,
                                             void* stream) {
   qlinear_status st = check_forward_common(w, m, lora_a, lora_b, rank, y, out_dtype);
   if (st != QL_OK) return st;
-  if (w->format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
+  if (!is_fp8(w->format)) return QL_ERR_FORMAT;
   if (!xq || !sx) return QL_ERR_NULL;
   if (!aligned16(xq) || !aligned16(sx)) return QL_ERR_ALIGN;
   const int32_t r = lora_rank(lora_a, lora_b, rank, lora_scale);
@@ -246,9 +272,8 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
   uint16_t* t = nullptr;
   if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, ql::ws_scratch(ws), &t, s) != hipSuccess)
     return QL_ERR_HIP;
-  return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes,
-                                        (const float*)w->scales, t, lora_b, r, y,
-                                        out_dtype == QL_OUT_F32, s));
+  return hip_status(ql::launch_gemm_fp8(xq, sx, m, w->n, w->k, (const uint8_t*)w->codes, w->scales,
+                                        w->format == QL_FP8_POW2, t, lora_b, r, y, out_dtype == QL_OUT_F32, s));
 }
 
 // ------------------------------------------------------------------- requant
@@ -258,14 +283,66 @@ size_t qlinear_requant_workspace(int32_t count) {
   return ql::requant_workspace(count);
 }
 
-qlinear_status qlinear_requantize_all(const qlinear_requant_item* items, int32_t count,
-                                      int32_t format, void* ws, size_t ws_bytes, void* stream) {
+static qlinear_status requant_common(const qlinear_requant_item* items, const uint16_t* const* deltas,
+                                     int32_t count, int32_t format, void* ws, size_t ws_bytes, void* stream) {
   if (!items) return QL_ERR_NULL;
   if (count <= 0 || count > QLINEAR_MAX_REQUANT_ITEMS) return QL_ERR_ARG;
-  if (format != QL_NVFP4 && format != QL_FP8_BLOCK128) return QL_ERR_FORMAT;
+  if (format != QL_NVFP4 && !is_fp8(format)) return QL_ERR_FORMAT;
   if (!ws || ws_bytes < ql::requant_workspace(count)) return QL_ERR_WORKSPACE;
-  if (!aligned16(items) || !aligned16(ws)) return QL_ERR_ALIGN;
-  return hip_status(ql::launch_requant(items, count, format, ws, (hipStream_t)stream));
+  if (!aligned16(items) || !aligned16(ws) || (deltas && ((uintptr_t)deltas & 7))) return QL_ERR_ALIGN;
+  return hip_status(ql::launch_requant(items, deltas, count, format, ws, (hipStream_t)stream));
+}
+
+qlinear_status qlinear_requantize_all(const qlinear_requant_item* items, int32_t count,
+                                      int32_t format, void* ws, size_t ws_bytes, void* stream) {
+  return requant_common(items, nullptr, count, format, ws, ws_bytes, stream);
+}
+
+qlinear_status qlinear_update_requantize_all(const qlinear_requant_item* items,
+                                             const uint16_t* const* deltas, int32_t count,
+                                             int32_t format, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  if (!deltas) return QL_ERR_NULL;
+  return requant_common(items, deltas, count, format, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ KV cache
+
+static qlinear_status check_kv(int64_t tokens, int32_t heads, int32_t head_dim, int64_t cache_slots,
+                               const int32_t* status_word) {
+  if (tokens < 0 || heads <= 0 || cache_slots <= 0) return QL_ERR_SHAPE;
+  if (head_dim < 16 || head_dim > 512 || (head_dim & (head_dim - 1))) return QL_ERR_SHAPE;
+  const int64_t vec = (int64_t)heads * head_dim;
+  if ((tokens > 0 && !elems_ok(tokens, vec)) || !elems_ok(cache_slots, vec)) return QL_ERR_SHAPE;
+  if (status_word && ((uintptr_t)status_word & 3)) return QL_ERR_ALIGN;
+  return QL_OK;
+}
+
+qlinear_status qlinear_kv_store_fp8(const uint16_t* kv, int64_t tokens, int32_t heads, int32_t head_dim,
+                                    const int64_t* slots, uint8_t* cache_codes, float* cache_scales,
+                                    int64_t cache_slots, int32_t* status_word, void* stream) {
+  if (!kv || !slots || !cache_codes || !cache_scales) return QL_ERR_NULL;
+  qlinear_status st = check_kv(tokens, heads, head_dim, cache_slots, status_word);
+  if (st != QL_OK) return st;
+  if (!aligned16(kv) || !aligned16(cache_codes) || !aligned16(cache_scales) || ((uintptr_t)slots & 7))
+    return QL_ERR_ALIGN;
+  if (tokens == 0) return QL_OK;
+  return hip_status(ql::launch_kv_store(kv, tokens, heads, head_dim, slots, cache_codes, cache_scales, cache_slots,
+                                        status_word, (hipStream_t)stream));
+}
+
+qlinear_status qlinear_kv_load_fp8(const uint8_t* cache_codes, const float* cache_scales,
+                                   int64_t cache_slots, const int64_t* slots, int64_t tokens,
+                                   int32_t heads, int32_t head_dim, uint16_t* out,
+                                   int32_t* status_word, void* stream) {
+  if (!cache_codes || !cache_scales || !slots || !out) return QL_ERR_NULL;
+  qlinear_status st = check_kv(tokens, heads, head_dim, cache_slots, status_word);
+  if (st != QL_OK) return st;
+  if (!aligned16(out) || !aligned16(cache_codes) || !aligned16(cache_scales) || ((uintptr_t)slots & 7))
+    return QL_ERR_ALIGN;
+  if (tokens == 0) return QL_OK;
+  return hip_status(ql::launch_kv_load(cache_codes, cache_scales, cache_slots, slots, tokens, heads, head_dim, out,
+                                       status_word, (hipStream_t)stream));
 }
 
 }  // extern "C"

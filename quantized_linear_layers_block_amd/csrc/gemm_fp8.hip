@@ -10,6 +10,12 @@
 // operand (columns m): a lane's four accumulators then share one m and one 128-row
 // weight block, i.e. one scale per lane per K block.
 //
+// With the page's power-of-two option (closing section) the block scales are E8M0 bytes,
+// which is the operand-scale format of gfx950's scaled FP8 MFMA: each lane hands the MFMA
+// the scale of the 32 K values it supplies (its weight block's, its token's), the MFMA
+// applies both, and accumulates straight into the float32 accumulator -- no fold, no
+// per-block vector work.
+//
 // Tiling: 256 (n) x 256 (m) per workgroup of eight waves (2 along n x 4 along m), 128 x 64
 // per wave (8 x 4 MFMA tiles, 128 float32 accumulators per lane), K step 128.  Operand tiles (32 KB each) are double-buffered in
 // LDS (128 KB) with a 16-byte XOR swizzle so that the 16 lanes reading one column of
@@ -31,9 +37,9 @@ constexpr size_t kFp8Lds = 8 * kStagePerWave;    // >= the two operand stages (1
 
 struct Fp8GemmArgs {
   const uint8_t* xq;
-  const float* sx;
+  const void* sx;          // float32 [m][k/128], or E8M0 bytes (POW2)
   const uint8_t* wq;
-  const float* sw;
+  const void* sw;          // float32 [n/128][k/128], or E8M0 bytes (POW2)
   int64_t m, n, k;
   const uint16_t* t;       // bf16 [m][rank_pad] (lora_scale already applied) or null
   const uint16_t* lora_b;  // bf16 [n][rank]
@@ -50,7 +56,7 @@ __device__ __forceinline__ i32x8 frag_fp8(const uint8_t* tile, int row, int g) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int OUT_F32>
+template <int OUT_F32, bool POW2>
 __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
   constexpr int kStage = 2 * kTile * kRowBytes;
@@ -100,17 +106,65 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
     const int64_t row = 64 * wm + 16 * j + r;
     osx[j] = (uint32_t)((row < m_last ? row : m_last) * kblocks);
   }
-  const float* sxbase = a.sx + m0 * kblocks;
   const int64_t nblk = (n0 + 128 * wn) / 128;  // the wave's 128-row weight block
   const bool nblk_ok = nblk * 128 < a.n;
-  const float* swp = a.sw + (nblk_ok ? nblk : 0) * kblocks;
-  const float swmask = nblk_ok ? 1.0f : 0.0f;
 
   f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  if constexpr (POW2) {
+    // Scale bytes of the next K block are loaded during this one: the wave's weight block
+    // (A operand, the same for every lane) and the lane's four m rows (B operand).
+    const uint8_t* sxb = (const uint8_t*)a.sx + m0 * kblocks;
+    const uint8_t* swb = (const uint8_t*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma(0, 0, q);
+    int sa = swb[0], sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sb[j] = sxb[osx[j]];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    i32x8 bf[4], af, afn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = frag_fp8(smem + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
+    af = frag_fp8(smem, 128 * wn + r, g);
+    for (int64_t kb = 0; kb < kblocks; ++kb) {
+      const int buf = (int)(kb & 1);
+      const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;
+      const int san = swb[kn];
+      int sbn[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sbn[j] = sxb[osx[j] + kn];
+      const uint8_t* As = smem + buf * kStage;
+      const uint8_t* An = smem + (buf ^ 1) * kStage;
+      // Same schedule as the fold path below, with each MFMA accumulating in place.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i == 7) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, sa, 0, sb[j]);
+          if (j == 0) afn = i < 7 ? frag_fp8(As, 128 * wn + 16 * (i + 1) + r, g) : frag_fp8(An, 128 * wn + r, g);
+          if (i < 4 && (j == 1 || j == 2)) dma(kn, buf ^ 1, 2 * i + (j - 1));
+          if (i == 7) bf[j] = frag_fp8(An + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        af = afn;
+      }
+      sa = san;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sb[j] = sbn[j];
+    }
+  } else {
+  const float* sxbase = (const float*)a.sx + m0 * kblocks;
+  const float* swp = (const float*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
+  const float swmask = nblk_ok ? 1.0f : 0.0f;
 
   float sxn[4];
 #pragma unroll
@@ -180,6 +234,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
+  }
 
   // Epilogue: lane holds m = m0 + 64 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
   if (a.rank_pad > 0)
@@ -218,8 +273,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   }
 }
 
-hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_t n, int64_t k,
-                           const uint8_t* wq, const float* sw, const uint16_t* t,
+hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t n, int64_t k,
+                           const uint8_t* wq, const void* sw, bool pow2, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,
                            hipStream_t s) {
   // Copy offsets are 32-bit within a 256-row tile; k is a multiple of the 128 block.
@@ -243,15 +298,19 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_
   const size_t lds = kFp8Lds;
   static_assert(kFp8Lds >= 4 * kTile * kRowBytes, "staging must cover the operand buffers");
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-  if (out_f32) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    gemm_fp8_kernel<1><<<grid, kGThreads, lds, s>>>(a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    gemm_fp8_kernel<0><<<grid, kGThreads, lds, s>>>(a);
+#define QL_FP8_LAUNCH(OF, P2)                                                                             \
+  {                                                                                                       \
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<OF, P2>,                               \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);             \
+    if (e != hipSuccess) return e;                                                                        \
+    gemm_fp8_kernel<OF, P2><<<grid, kGThreads, lds, s>>>(a);                                               \
   }
+  if (out_f32) {
+    if (pow2) QL_FP8_LAUNCH(1, true) else QL_FP8_LAUNCH(1, false)
+  } else {
+    if (pow2) QL_FP8_LAUNCH(0, true) else QL_FP8_LAUNCH(0, false)
+  }
+#undef QL_FP8_LAUNCH
   return hipGetLastError();
 }
 

@@ -36,17 +36,25 @@ constexpr int kAmaxParts = 1024;  // partial maxima written by the NVFP4 amax pa
 hipError_t launch_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
                                  uint8_t* scales, float* tensor_scale, int32_t* status,
                                  uint32_t* partials, hipStream_t s);
+// FP8 scales: float32 amax/448, or with pow2 the E8M0 byte of the power-of-two scale.
 hipError_t launch_fp8_weight_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
-                                      float* scales, int32_t* status, hipStream_t s);
+                                      void* scales, bool pow2, int32_t* status, hipStream_t s);
 hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
-                                   float* sx, hipStream_t s);
+                                   void* sx, bool pow2, hipStream_t s);
 
 // ---- whole-policy requantization (quant.hip)
 // Workspace: status word | header | descriptors[count] | per-tensor maxima[count].  The
-// descriptors are rebuilt on the device from the caller's item array by every call.
+// descriptors are rebuilt on the device from the caller's item array by every call.  With
+// deltas (a device array of count update pointers) each weight is first updated in place.
 size_t requant_workspace(int32_t count);
-hipError_t launch_requant(const void* items, int32_t count, int32_t format, void* ws,
-                          hipStream_t s);
+hipError_t launch_requant(const void* items, const uint16_t* const* deltas, int32_t count,
+                          int32_t format, void* ws, hipStream_t s);
+
+// ---- FP8 KV-cache codec (kv.hip); head_dim a power of two in [16, 512]
+hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int head_dim, const int64_t* slots,
+                           uint8_t* codes, float* scales, int64_t cache_slots, int32_t* status, hipStream_t s);
+hipError_t launch_kv_load(const uint8_t* codes, const float* scales, int64_t cache_slots, const int64_t* slots,
+                          int64_t tokens, int heads, int head_dim, uint16_t* out, int32_t* status, hipStream_t s);
 
 // ---- NVFP4 layer for up to 64 tokens (gemv16.hip)
 struct G16Plan {
@@ -102,8 +110,9 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
 size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
 // k % 128 == 0 and k < kFp8MaxK (copy offsets within a 256-row tile are 32-bit).
 constexpr int64_t kFp8MaxK = int64_t(1) << 24;
-hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, int64_t n, int64_t k,
-                           const uint8_t* wq, const float* sw, const uint16_t* t,
+// pow2: sx, sw are E8M0 bytes applied by the scaled MFMA; else float32, folded per K block.
+hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t n, int64_t k,
+                           const uint8_t* wq, const void* sw, bool pow2, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,
                            hipStream_t s);
 

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_encode_kernel(
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *tensor_scale = ts.S;
-    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, (int32_t)kStatusNonFinite);
   }
   // Back to front: the tail of the tensor, read last by the maximum pass, is the part
   // most likely still held in the memory-side cache.
@@ -169,14 +169,71 @@ hipError_t launch_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- FP8 block scale
+
+// Block scale from the block's |bf16| maximum (bit pattern): the float32 multiplier
+// amax/448 of the recipe (POW2 false), or the power-of-two option (the mexc.co page's
+// closing section): 2^e with e the smallest integer such that amax <= 448 * 2^e, clamped
+// to [-127, 127], 0 for an all-zero block (POW2 true).  With amax = (1 + M/128) 2^(E-127)
+// (bf16 exponent field E > 0, mantissa M) and 448 = 1.75 * 2^8, e = E - 135 when
+// 1 + M/128 <= 1.75 (M <= 96) and E - 134 otherwise; every bf16 subnormal gives e below
+// -127.  r is the exact double reciprocal the element quotients use; `stored` is what the
+// scale array holds (float32 bits, or the E8M0 byte e + 127).
+struct Fp8Scale {
+  double r;
+  uint32_t stored;
+};
+template <bool POW2>
+__device__ __forceinline__ Fp8Scale fp8_block_scale(uint32_t amax_bits) {
+  Fp8Scale o;
+  if (!POW2) {
+    const float sc = __uint_as_float(amax_bits << 16) / 448.0f;
+    o.r = sc > 0.0f ? 1.0 / (double)sc : 0.0;
+    o.stored = __float_as_uint(sc);
+  } else {
+    const int E = (int)(amax_bits >> 7) & 0xFF, M = (int)(amax_bits & 0x7F);
+    int e = amax_bits == 0 ? 0 : (E == 0 ? -127 : (M <= 96 ? E - 135 : E - 134));
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    o.r = __longlong_as_double((long long)(1023 - e) << 52);  // 2^-e
+    o.stored = (uint32_t)(e + 127);
+  }
+  return o;
+}
+
+// Eight bf16 values (one 16-byte unit) -> eight E4M3 codes (sign | E4M3(fl32(|v| / s))).
+__device__ __forceinline__ uint2 fp8_encode8(const uint4& v, double r) {
+  float q[8];
+  q[0] = exact_quotient(bf16_lo(v.x), r);
+  q[1] = exact_quotient(bf16_hi(v.x), r);
+  q[2] = exact_quotient(bf16_lo(v.y), r);
+  q[3] = exact_quotient(bf16_hi(v.y), r);
+  q[4] = exact_quotient(bf16_lo(v.z), r);
+  q[5] = exact_quotient(bf16_hi(v.z), r);
+  q[6] = exact_quotient(bf16_lo(v.w), r);
+  q[7] = exact_quotient(bf16_hi(v.w), r);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t], -448.0f, 448.0f);
+  uint2 c;
+  c.x = e4m3_pack4(q[0], q[1], q[2], q[3]);
+  c.y = e4m3_pack4(q[4], q[5], q[6], q[7]);
+  return c;
+}
+
+// A training step's update applied to eight bf16 weights: bf16_RNE(fl32(w) + fl32(d)).
+__device__ __forceinline__ uint4 bf16_add8(const uint4& w, const uint4& d) {
+  auto add2 = [](uint32_t a, uint32_t b) { return pack_bf16x2_rne(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b)); };
+  return make_uint4(add2(w.x, d.x), add2(w.y, d.y), add2(w.z, d.z), add2(w.w, d.w));
+}
+
 // ---------------------------------------------------------------- FP8 weights
 
 // One 128x128 tile per workgroup.  Wave v, lane l holds rows 32v + 4j + l/16 (j = 0..7),
-// elements [8 (l%16), 8 (l%16) + 8) of the tile's 128 columns.
-__device__ __forceinline__ void fp8_tile(const uint16_t* __restrict__ w, int64_t k, int64_t tr,
-                                         int64_t tc, uint8_t* __restrict__ codes,
-                                         float* __restrict__ scales, int32_t* status,
-                                         uint32_t* red) {
+// elements [8 (l%16), 8 (l%16) + 8) of the tile's 128 columns.  With UPDATE the tile is
+// first updated (W <- W + delta, written back) and the new values are quantized.
+template <bool POW2, bool UPDATE>
+__device__ __forceinline__ void fp8_tile(const uint16_t* __restrict__ w, const uint16_t* __restrict__ delta,
+                                         int64_t k, int64_t tr, int64_t tc, uint8_t* __restrict__ codes,
+                                         void* __restrict__ scales, int32_t* status, uint32_t* red) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int piece = lane & 15;
@@ -188,6 +245,16 @@ __device__ __forceinline__ void fp8_tile(const uint16_t* __restrict__ w, int64_t
     off[j] = row * k + tc * 128 + piece * 8;
     v[j] = *(const uint4*)(w + off[j]);
   }
+  if (UPDATE) {
+    uint4 d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = *(const uint4*)(delta + off[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = bf16_add8(v[j], d[j]);
+      *(uint4*)(const_cast<uint16_t*>(w) + off[j]) = v[j];
+    }
+  }
   u16x2 m = {0, 0};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -197,45 +264,35 @@ __device__ __forceinline__ void fp8_tile(const uint16_t* __restrict__ w, int64_t
     m = max_u16x2(m, abs_bits2(v[j].w));
   }
   const uint32_t amax_bits = max_block<kQThreads>(hmax_u16x2(m), red);
-  const float sc = __uint_as_float(amax_bits << 16) / 448.0f;
-  const double r = sc > 0.0f ? 1.0 / (double)sc : 0.0;
+  const Fp8Scale sc = fp8_block_scale<POW2>(amax_bits);
   if (threadIdx.x == 0) {
-    scales[tr * (k / 128) + tc] = sc;
-    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, 1);
+    if (POW2)
+      ((uint8_t*)scales)[tr * (k / 128) + tc] = (uint8_t)sc.stored;
+    else
+      ((uint32_t*)scales)[tr * (k / 128) + tc] = sc.stored;
+    if (amax_bits >= kBf16InfBits && status != nullptr) atomicOr(status, (int32_t)kStatusNonFinite);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float q[8];
-    q[0] = exact_quotient(bf16_lo(v[j].x), r);
-    q[1] = exact_quotient(bf16_hi(v[j].x), r);
-    q[2] = exact_quotient(bf16_lo(v[j].y), r);
-    q[3] = exact_quotient(bf16_hi(v[j].y), r);
-    q[4] = exact_quotient(bf16_lo(v[j].z), r);
-    q[5] = exact_quotient(bf16_hi(v[j].z), r);
-    q[6] = exact_quotient(bf16_lo(v[j].w), r);
-    q[7] = exact_quotient(bf16_hi(v[j].w), r);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t], -448.0f, 448.0f);
-    uint2 c;
-    c.x = e4m3_pack4(q[0], q[1], q[2], q[3]);
-    c.y = e4m3_pack4(q[4], q[5], q[6], q[7]);
-    *(uint2*)(codes + off[j]) = c;
-  }
+  for (int j = 0; j < 8; ++j) *(uint2*)(codes + off[j]) = fp8_encode8(v[j], sc.r);
 }
 
+template <bool POW2>
 __global__ __launch_bounds__(kQThreads) void fp8_weight_kernel(const uint16_t* __restrict__ w,
                                                                int64_t k,
                                                                uint8_t* __restrict__ codes,
-                                                               float* __restrict__ scales,
+                                                               void* __restrict__ scales,
                                                                int32_t* status) {
   __shared__ uint32_t red[kQThreads / kWave];
-  fp8_tile(w, k, blockIdx.y, blockIdx.x, codes, scales, status, red);
+  fp8_tile<POW2, false>(w, nullptr, k, blockIdx.y, blockIdx.x, codes, scales, status, red);
 }
 
 hipError_t launch_fp8_weight_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
-                                      float* scales, int32_t* status, hipStream_t s) {
+                                      void* scales, bool pow2, int32_t* status, hipStream_t s) {
   dim3 grid((unsigned)(k / 128), (unsigned)(n / 128));
-  fp8_weight_kernel<<<grid, kQThreads, 0, s>>>(w, k, codes, scales, status);
+  if (pow2)
+    fp8_weight_kernel<true><<<grid, kQThreads, 0, s>>>(w, k, codes, scales, status);
+  else
+    fp8_weight_kernel<false><<<grid, kQThreads, 0, s>>>(w, k, codes, scales, status);
   return hipGetLastError();
 }
 
@@ -245,10 +302,11 @@ constexpr int kActSegPerIter = 2;  // segments per 16-lane group per iteration
 
 // Segment = 1x128 of a token row.  16 lanes per segment (8 elements each); a DPP row
 // is exactly one segment, so the segment maximum is four DPP moves.
+template <bool POW2>
 __global__ __launch_bounds__(kQThreads) void fp8_act_kernel(const uint16_t* __restrict__ x,
                                                             int64_t nseg,
                                                             uint8_t* __restrict__ xq,
-                                                            float* __restrict__ sx) {
+                                                            void* __restrict__ sx) {
   const int piece = threadIdx.x & 15;
   const int64_t groups = (nseg + (kQThreads / 16) * kActSegPerIter - 1) /
                          ((kQThreads / 16) * kActSegPerIter);
@@ -267,36 +325,30 @@ __global__ __launch_bounds__(kQThreads) void fp8_act_kernel(const uint16_t* __re
       m = max_u16x2(m, abs_bits2(v[j].z));
       m = max_u16x2(m, abs_bits2(v[j].w));
       const uint32_t amax_bits = max_row16(hmax_u16x2(m));
-      const float sc = __uint_as_float(amax_bits << 16) / 448.0f;
-      const double r = sc > 0.0f ? 1.0 / (double)sc : 0.0;
-      float q[8];
-      q[0] = exact_quotient(bf16_lo(v[j].x), r);
-      q[1] = exact_quotient(bf16_hi(v[j].x), r);
-      q[2] = exact_quotient(bf16_lo(v[j].y), r);
-      q[3] = exact_quotient(bf16_hi(v[j].y), r);
-      q[4] = exact_quotient(bf16_lo(v[j].z), r);
-      q[5] = exact_quotient(bf16_hi(v[j].z), r);
-      q[6] = exact_quotient(bf16_lo(v[j].w), r);
-      q[7] = exact_quotient(bf16_hi(v[j].w), r);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t], -448.0f, 448.0f);
-      uint2 c;
-      c.x = e4m3_pack4(q[0], q[1], q[2], q[3]);
-      c.y = e4m3_pack4(q[4], q[5], q[6], q[7]);
+      const Fp8Scale sc = fp8_block_scale<POW2>(amax_bits);
+      const uint2 c = fp8_encode8(v[j], sc.r);
       if (seg[j] < nseg) {
         *(uint2*)(xq + seg[j] * 128 + piece * 8) = c;
-        if (piece == 0) sx[seg[j]] = sc;
+        if (piece == 0) {
+          if (POW2)
+            ((uint8_t*)sx)[seg[j]] = (uint8_t)sc.stored;
+          else
+            ((uint32_t*)sx)[seg[j]] = sc.stored;
+        }
       }
     }
   }
 }
 
 hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq,
-                                   float* sx, hipStream_t s) {
+                                   void* sx, bool pow2, hipStream_t s) {
   const int64_t nseg = m * (k / 128);
   const int64_t per_block = (kQThreads / 16) * kActSegPerIter;
   const int64_t groups = (nseg + per_block - 1) / per_block;
-  fp8_act_kernel<<<stream_grid(groups, 4096), kQThreads, 0, s>>>(x, nseg, xq, sx);
+  if (pow2)
+    fp8_act_kernel<true><<<stream_grid(groups, 4096), kQThreads, 0, s>>>(x, nseg, xq, sx);
+  else
+    fp8_act_kernel<false><<<stream_grid(groups, 4096), kQThreads, 0, s>>>(x, nseg, xq, sx);
   return hipGetLastError();
 }
 
@@ -308,9 +360,15 @@ hipError_t launch_fp8_act_quantize(const uint16_t* x, int64_t m, int64_t k, uint
 // memory; a one-workgroup prepare kernel checks every item, numbers the work units of all
 // tensors (NVFP4: 8192-element chunks, FP8: 128x128 tiles) and writes the descriptor table
 // into the workspace, so nothing crosses from the host per step.
+//
+// With a device array of dense bf16 updates (one per tensor), the step's update is fused
+// in: W <- bf16(fl32(W) + fl32(delta)) is applied, written back and its maximum taken in
+// the same pass (NVFP4: the maximum pass; FP8: the one pass over each tile), so the
+// requantization itself adds only the encode pass over the new weights.
 
 struct RequantDesc {       // one tensor, as the passes read it
   const uint16_t* w;
+  const uint16_t* delta;   // the step's update (fused variant), else null
   void* codes;
   void* scales;
   float* tensor_scale;
@@ -333,22 +391,25 @@ size_t requant_workspace(int32_t count) {
 
 __device__ __forceinline__ int64_t requant_units_dev(int32_t format, int64_t n, int64_t k) {
   if (format == QL_NVFP4) return (n * k / 8 + kChunkVec - 1) / kChunkVec;  // NVFP4 chunks
-  return (n / 128) * (k / 128);                                           // FP8 tiles
+  return (n / 128) * (k / 128);                                           // FP8 tiles (both kinds)
 }
 
 // The checks the host applies to a quantized weight (include/qlinear.h), on the device.
-__device__ __forceinline__ bool requant_item_ok(const qlinear_requant_item& it, int32_t format) {
+__device__ __forceinline__ bool requant_item_ok(const qlinear_requant_item& it, int32_t format,
+                                                const uint16_t* const* deltas, int i) {
   const qlinear_qweight& q = it.q;
   auto al = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  if (deltas && (!deltas[i] || !al(deltas[i]))) return false;
   if (q.format != format || !it.w || !q.codes || !q.scales) return false;
   if (q.n <= 0 || q.k <= 0 || q.n > QLINEAR_MAX_ELEMS / q.k) return false;
   if (!al(it.w) || !al(q.codes) || !al(q.scales)) return false;
   if (format == QL_NVFP4) return q.tensor_scale && al(q.tensor_scale) && q.k % 16 == 0;
-  return q.n % 128 == 0 && q.k % 128 == 0;
+  return q.n % 128 == 0 && q.k % 128 == 0;  // both FP8 kinds
 }
 
 constexpr int kRqPrepThreads = 1024;
 __global__ __launch_bounds__(kRqPrepThreads) void requant_prepare_kernel(const qlinear_requant_item* __restrict__ items,
+                                                                         const uint16_t* const* __restrict__ deltas,
                                                                          int32_t count, int32_t format, char* ws) {
   __shared__ int64_t wsum[kRqPrepThreads / kWave];
   RequantHeader* h = (RequantHeader*)(ws + kRqHeaderOff);
@@ -361,7 +422,7 @@ __global__ __launch_bounds__(kRqPrepThreads) void requant_prepare_kernel(const q
   bool bad = false;
   for (int i = i0; i < i1; ++i) {
     const qlinear_requant_item it = items[i];
-    const bool ok = requant_item_ok(it, format);
+    const bool ok = requant_item_ok(it, format, deltas, i);
     bad |= !ok;
     local += ok ? requant_units_dev(format, it.q.n, it.q.k) : 0;
   }
@@ -383,9 +444,10 @@ __global__ __launch_bounds__(kRqPrepThreads) void requant_prepare_kernel(const q
   int64_t u = before + v - local;
   for (int i = i0; i < i1; ++i) {
     const qlinear_requant_item it = items[i];
-    const bool ok = requant_item_ok(it, format);
+    const bool ok = requant_item_ok(it, format, deltas, i);
     RequantDesc r;
     r.w = it.w;
+    r.delta = deltas ? deltas[i] : nullptr;
     r.codes = it.q.codes;
     r.scales = it.q.scales;
     r.tensor_scale = it.q.tensor_scale;
@@ -418,8 +480,33 @@ __global__ __launch_bounds__(kQThreads) void requant_zero_kernel(uint32_t* amax,
     amax[i] = 0;
 }
 
+// UPDATE: one chunk of W <- W + delta written back, and the maximum of the new values.
+__device__ __forceinline__ u16x2 nvfp4_chunk_update_max(uint4* __restrict__ w, const uint4* __restrict__ d,
+                                                        int64_t nvec, int64_t chunk, u16x2 m) {
+  const int64_t base = chunk * kChunkVec + threadIdx.x;
+  uint4 v[kQUnroll], dv[kQUnroll];
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kQThreads;
+    v[j] = i < nvec ? w[i] : make_uint4(0, 0, 0, 0);
+    dv[j] = i < nvec ? d[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kQUnroll; ++j) {
+    const int64_t i = base + (int64_t)j * kQThreads;
+    v[j] = bf16_add8(v[j], dv[j]);
+    if (i < nvec) w[i] = v[j];
+    m = max_u16x2(m, abs_bits2(v[j].x));
+    m = max_u16x2(m, abs_bits2(v[j].y));
+    m = max_u16x2(m, abs_bits2(v[j].z));
+    m = max_u16x2(m, abs_bits2(v[j].w));
+  }
+  return m;
+}
+
 // Each workgroup takes a contiguous range of units (so that most of its units belong
 // to one tensor) and publishes one integer atomicMax per tensor it touched.
+template <bool UPDATE>
 __global__ __launch_bounds__(kQThreads) void requant_amax_kernel(const RequantHeader* __restrict__ h,
                                                                  const RequantDesc* __restrict__ d,
                                                                  uint32_t* __restrict__ amax) {
@@ -436,7 +523,12 @@ __global__ __launch_bounds__(kQThreads) void requant_amax_kernel(const RequantHe
     const int64_t stop = tend < u1 ? tend : u1;
     const int64_t nvec = d[t].n * d[t].k / 8;
     u16x2 m = {0, 0};
-    for (; u < stop; ++u) m = nvfp4_chunk_max((const uint4*)d[t].w, nvec, u - d[t].unit_begin, m);
+    if (UPDATE)
+      for (; u < stop; ++u)
+        m = nvfp4_chunk_update_max((uint4*)const_cast<uint16_t*>(d[t].w), (const uint4*)d[t].delta, nvec,
+                                   u - d[t].unit_begin, m);
+    else
+      for (; u < stop; ++u) m = nvfp4_chunk_max((const uint4*)d[t].w, nvec, u - d[t].unit_begin, m);
     const uint32_t v = max_block<kQThreads>(hmax_u16x2(m), red);
     if (threadIdx.x == 0) atomicMax(amax + t, v);
   }
@@ -472,6 +564,7 @@ __global__ __launch_bounds__(kQThreads) void requant_encode_kernel(const Requant
   }
 }
 
+template <bool POW2, bool UPDATE>
 __global__ __launch_bounds__(kQThreads) void requant_fp8_kernel(const RequantHeader* __restrict__ h,
                                                                 const RequantDesc* __restrict__ d,
                                                                 int32_t* status) {
@@ -482,8 +575,8 @@ __global__ __launch_bounds__(kQThreads) void requant_fp8_kernel(const RequantHea
     const int t = find_tensor(d, count, u);
     const int64_t tile = u - d[t].unit_begin;
     const int64_t tiles_k = d[t].k / 128;
-    fp8_tile(d[t].w, d[t].k, tile / tiles_k, tile % tiles_k, (uint8_t*)d[t].codes,
-             (float*)d[t].scales, status, red);
+    fp8_tile<POW2, UPDATE>(d[t].w, d[t].delta, d[t].k, tile / tiles_k, tile % tiles_k, (uint8_t*)d[t].codes,
+                           d[t].scales, status, red);
   }
 }
 
@@ -491,26 +584,38 @@ __global__ __launch_bounds__(kQThreads) void requant_fp8_kernel(const RequantHea
 // the units the header announces.
 constexpr int kRqAmaxGrid = 4096, kRqEncodeGrid = 4096, kRqFp8Grid = 8192;
 
-hipError_t launch_requant(const void* items, int32_t count, int32_t format, void* ws, hipStream_t s) {
+hipError_t launch_requant(const void* items, const uint16_t* const* deltas, int32_t count, int32_t format,
+                          void* ws, hipStream_t s) {
   char* w = (char*)ws;
   const RequantHeader* dh = (const RequantHeader*)(w + kRqHeaderOff);
   const RequantDesc* dd = (const RequantDesc*)(w + kRqDescOff);
   uint32_t* amax = (uint32_t*)(w + kRqDescOff + (size_t)count * sizeof(RequantDesc));
   int32_t* status = (int32_t*)w;
-  requant_prepare_kernel<<<1, kRqPrepThreads, 0, s>>>((const qlinear_requant_item*)items, count, format, w);
+  requant_prepare_kernel<<<1, kRqPrepThreads, 0, s>>>((const qlinear_requant_item*)items, deltas, count, format, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (format == QL_NVFP4) {
     requant_zero_kernel<<<(count + kQThreads - 1) / kQThreads, kQThreads, 0, s>>>(amax, count);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    requant_amax_kernel<<<kRqAmaxGrid, kQThreads, 0, s>>>(dh, dd, amax);
+    if (deltas)
+      requant_amax_kernel<true><<<kRqAmaxGrid, kQThreads, 0, s>>>(dh, dd, amax);
+    else
+      requant_amax_kernel<false><<<kRqAmaxGrid, kQThreads, 0, s>>>(dh, dd, amax);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     requant_encode_kernel<<<kRqEncodeGrid, kQThreads, 0, s>>>(dh, dd, amax, status);
     return hipGetLastError();
   }
-  requant_fp8_kernel<<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
+  const bool pow2 = format == QL_FP8_POW2;
+  if (pow2 && deltas)
+    requant_fp8_kernel<true, true><<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
+  else if (pow2)
+    requant_fp8_kernel<true, false><<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
+  else if (deltas)
+    requant_fp8_kernel<false, true><<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
+  else
+    requant_fp8_kernel<false, false><<<kRqFp8Grid, kQThreads, 0, s>>>(dh, dd, status);
   return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ def test_forward_argument_errors():
     assert f(qw, la=FAKE, lb=FAKE, r=8, s=2.0, ws=None) == b.QL_ERR_WORKSPACE
     assert f(qw, la=FAKE, lb=FAKE, r=8, s=2.0, wsb=16) == b.QL_ERR_WORKSPACE
     assert f(qw, x=FAKE + 8) == b.QL_ERR_ALIGN
-    assert f(b.QWeight(3, 0, 256, 512, FAKE, FAKE, FAKE)) == b.QL_ERR_FORMAT
+    assert f(b.QWeight(9, 0, 256, 512, FAKE, FAKE, FAKE)) == b.QL_ERR_FORMAT
     assert f(b.QWeight(b.QL_NVFP4, 0, 256, 500, FAKE, FAKE, FAKE)) == b.QL_ERR_SHAPE
     assert f(b.QWeight(b.QL_NVFP4, 0, 256, 512, FAKE, FAKE, None)) == b.QL_ERR_NULL
     assert f(b.QWeight(b.QL_FP8_BLOCK128, 0, 200, 512, FAKE, FAKE, None)) == b.QL_ERR_SHAPE
@@ -140,3 +140,36 @@ def test_requant_item_layout():
     assert ctypes.sizeof(b.RequantItem) == 56
     assert b.RequantItem.q.offset == 8
     assert b.QWeight.tensor_scale.offset == 40
+
+
+def test_new_entry_argument_errors():
+    L = b.LIB
+    # power-of-two FP8 quantizers share the FP8 shape rules
+    assert L.qlinear_quantize_fp8_pow2(FAKE, 100, 128, FAKE, FAKE, None, None) == b.QL_ERR_SHAPE
+    assert L.qlinear_quantize_fp8_pow2(FAKE, 128, 128, None, FAKE, None, None) == b.QL_ERR_NULL
+    assert L.qlinear_quantize_act_fp8_pow2(FAKE, 3, 100, FAKE, FAKE, None) == b.QL_ERR_SHAPE
+    # the FP8 prequant GEMM takes both FP8 kinds but no NVFP4 weight
+    qn = b.QWeight(b.QL_NVFP4, 0, 128, 128, FAKE, FAKE, FAKE)
+    assert L.qlinear_forward_fp8_prequant(ctypes.byref(qn), FAKE, FAKE, 4, None, None, None, 0, 0.0, FAKE,
+                                          b.QL_OUT_BF16, FAKE, 1 << 30, None) == b.QL_ERR_FORMAT
+    qp = b.QWeight(b.QL_FP8_POW2, 0, 200, 128, FAKE, FAKE, None)
+    assert L.qlinear_forward(ctypes.byref(qp), FAKE, 4, None, None, 0, 0.0, FAKE, b.QL_OUT_BF16,
+                             FAKE, 1 << 30, None) == b.QL_ERR_SHAPE
+    # fused update: the update array is required
+    nb = b.qlinear_requant_workspace(1)
+    assert L.qlinear_update_requantize_all(FAKE, None, 1, b.QL_NVFP4, FAKE, nb, None) == b.QL_ERR_NULL
+    assert L.qlinear_update_requantize_all(FAKE, FAKE + 4, 1, b.QL_NVFP4, FAKE, nb, None) == b.QL_ERR_ALIGN
+    assert L.qlinear_update_requantize_all(FAKE, FAKE, 0, b.QL_NVFP4, FAKE, nb, None) == b.QL_ERR_ARG
+    # KV cache: head_dim a power of two in [16, 512], positive heads and slots
+    st = lambda t=4, h=8, d=128, s=16, kv=FAKE, slots=FAKE: L.qlinear_kv_store_fp8(kv, t, h, d, slots, FAKE, FAKE, s,
+                                                                                   None, None)
+    assert st(d=96) == b.QL_ERR_SHAPE
+    assert st(d=1024) == b.QL_ERR_SHAPE
+    assert st(h=0) == b.QL_ERR_SHAPE
+    assert st(s=0) == b.QL_ERR_SHAPE
+    assert st(t=-1) == b.QL_ERR_SHAPE
+    assert st(kv=None) == b.QL_ERR_NULL
+    assert st(slots=FAKE + 4) == b.QL_ERR_ALIGN
+    assert st(t=0) == b.QL_OK          # nothing to store: nothing launched
+    ld = L.qlinear_kv_load_fp8(FAKE, FAKE, 16, FAKE, 4, 8, 100, FAKE, None, None)
+    assert ld == b.QL_ERR_SHAPE
