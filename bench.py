@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--rows", default="all")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle quantizers on every whole tensor of configs 1-4 (minutes)")
     ap.add_argument("--steps-only", action="store_true",
                     help="time the decode step only (no per-call launches, no copy ceiling): every layer "
                          "call is launched equally often, as hardware-counter runs need")
@@ -297,13 +299,13 @@ def main():
 
     log(f"decode step: {ms_per_step:.3f} ms, {value:.1f} GB/s")
     rows = set(args.rows.split(",")) if args.rows not in ("all", "none") else (
-        {"a1", "a2", "a3", "a5", "a6", "a8", "a9"} if args.rows == "all" else set())
+        {"a1", "a2", "a3", "a5", "a6", "a6p", "a8", "a8u", "a9", "kv", "ceil"} if args.rows == "all" else set())
     if rows:
         result["rows"] = run_rows(rows, torch, ql, dev)
 
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.cpu_full)
     print(json.dumps(result), flush=True)
 
 
@@ -320,6 +322,30 @@ def _events_ms(torch, fn, reps):
         t.stop(e0)
     torch.cuda.synchronize()
     return t.total_ms() / reps
+
+
+def _timed(torch, fns, iters=100, repeats=5, warmup=10):
+    """The rows' timing protocol: `warmup` untimed calls, then `repeats` blocks of
+    iters / repeats back-to-back calls (fns[0], fns[1], ... in turn over rotated buffers),
+    HIP events on the current stream around each block.  Returns the median block mean
+    (ms) with the block spread."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    per = max(1, iters // repeats)
+    means, j = [], 0
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per):
+            fns[j % len(fns)]()
+            j += 1
+        e1.record()
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / per)
+    means.sort()
+    return means[len(means) // 2], {"timing": f"warm-up {warmup}, {repeats} x {per} calls, median of block means",
+                                    "block_ms_min": round(means[0], 4), "block_ms_max": round(means[-1], 4)}
 
 
 def _graph_ms(torch, fns, reps=None):
@@ -359,6 +385,40 @@ def _row(kind, work, ms, peak, unit_work):
             "peak_TFLOP/s": peak / 1e12, "frac": round(rate / peak, 4), "flop": work}
 
 
+def mfma_ceiling(torch, dev):
+    """Measured MFMA ceilings (libqlinear_ceiling.so: eight independent MFMA chains per wave,
+    no memory traffic) for the bf16, f16 and block-scaled FP8 shapes, with the shader clock
+    the workgroups ran at (s_memtime / s_memrealtime ticks x 100 MHz, median over workgroups)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_linear_layers_block_amd", "libqlinear_ceiling.so"))
+    lib.qlc_mfma_loop.restype = ctypes.c_int
+    lib.qlc_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.qlc_mfma_flop.restype = ctypes.c_int64
+    lib.qlc_chains.restype = ctypes.c_int32
+    blocks, iters = 2048, 2048
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    times = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    out = {}
+    for kind, name, peak in ((0, "bf16_16x16x32", BF16_PEAK), (2, "f16_16x16x32", BF16_PEAK),
+                             (3, "bf16_32x32x16", BF16_PEAK), (4, "f16_32x32x16", BF16_PEAK),
+                             (1, "fp8_scaled_16x16x128", FP8_PEAK), (5, "fp8_scaled_32x32x64", FP8_PEAK)):
+        st = torch.cuda.current_stream().cuda_stream
+
+        def run():
+            rc = lib.qlc_mfma_loop(kind, blocks, iters, sink.data_ptr(), times.data_ptr(), st)
+            if rc != 0:
+                raise RuntimeError(f"qlc_mfma_loop: {rc}")
+        ms, info = _timed(torch, [run], iters=10, repeats=5, warmup=2)
+        t = times.view(blocks, 4).cpu().numpy().astype("float64")
+        ratio = sorted(((t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2])).tolist())
+        flop = float(blocks) * 4 * iters * lib.qlc_chains() * lib.qlc_mfma_flop(kind)
+        r = _row("mfma", flop, ms, peak, "flop")
+        r.update({"clock_GHz": round(ratio[len(ratio) // 2] * 0.1, 3), "blocks": blocks, **info})
+        out[name] = r
+    return out
+
+
 def run_rows(rows, torch, ql, dev):
     import synth
     from synth import gpu as sg
@@ -366,6 +426,19 @@ def run_rows(rows, torch, ql, dev):
     bf = torch.bfloat16
 
     log(f"rows {sorted(rows)}")
+    ceil = None
+    if rows & {"ceil", "a5", "a6", "a6p", "a9"}:
+        ceil = mfma_ceiling(torch, dev)
+        out["ceiling_mfma"] = ceil
+        log("MFMA ceiling done")
+
+    def with_ceiling(r, name):
+        if ceil is not None:
+            c = ceil[name]
+            r.update({"frac_of_measured_ceiling": round(r["TFLOP/s"] / c["TFLOP/s"], 4),
+                      "mfma_loop_clock_GHz": c["clock_GHz"]})
+        return r
+
     if "a1" in rows:   # NVFP4 weight quantizer on the decode weights (2.5625 B/param)
         res = []
         for si, (k, n) in enumerate(DECODE_SHAPES):
@@ -385,7 +458,7 @@ def run_rows(rows, torch, ql, dev):
         out["a1_quantize_nvfp4"] = res
         log("a1 done")
 
-    if "a2" in rows or "a3" in rows or "a6" in rows:
+    if rows & {"a2", "a3", "a6", "a6p"}:
         c4 = []
         for si, (k, n) in enumerate(synth.CFG4_SHAPES):
             w = sg.normal_bf16((n, k), 0.02, sg.gen(sg.seed_of(4, si, 1)), device=dev)
@@ -418,25 +491,33 @@ def run_rows(rows, torch, ql, dev):
                 res.append(r)
                 del xs_
             out["a3_quantize_fp8_act"] = res
-        if "a6" in rows:
+        for name, pow2 in (("a6", False), ("a6p", True)):
+            if name not in rows:
+                continue
             res = []
+            fmt = ql.QL_FP8_POW2 if pow2 else ql.QL_FP8_BLOCK128
             for k, n, w, x in c4:
                 m = x.shape[0]
-                q = ql.quantize_fp8_block(w)
-                xq, sx = ql.quantize_act_fp8(x)
+                q0 = ql.quantize_fp8_pow2(w) if pow2 else ql.quantize_fp8_block(w)
+                qs = [q0] + [ql.FP8Weight(q0.codes.clone(), q0.scales.clone(), n, k, pow2)
+                             for _ in range(_copies_for(n * k) - 1)]
+                xq, sx = ql.quantize_act_fp8(x, pow2=pow2)
                 y = torch.empty((m, n), dtype=bf, device=dev)
-                ws = torch.zeros(ql.binding.qlinear_forward_workspace(ql.QL_FP8_BLOCK128, m, n, k, 0) + 16,
+                ws = torch.zeros(ql.binding.qlinear_forward_workspace(fmt, m, n, k, 0) + 16,
                                  dtype=torch.uint8, device=dev)
                 wsp = torch.zeros(ql.binding.qlinear_forward_prequant_workspace(m, n, k, 0), dtype=torch.uint8,
                                   device=dev)
-                ms = _events_ms(torch, lambda: ql.forward_fp8_prequant(q, xq, sx, out=y, ws=wsp), 10)
-                r = _row("mfma", 2.0 * m * n * k, ms, FP8_PEAK, "flop")
-                ms_e2e = _events_ms(torch, lambda: ql.forward(q, x, out=y, ws=ws), 10)
-                r.update({"M": m, "K": k, "N": n, "e2e_us_with_act_quant": round(ms_e2e * 1e3, 2),
+                ms, info = _timed(torch, [(lambda q=q: ql.forward_fp8_prequant(q, xq, sx, out=y, ws=wsp)) for q in qs])
+                r = with_ceiling(_row("mfma", 2.0 * m * n * k, ms, FP8_PEAK, "flop"), "fp8_scaled_16x16x128")
+                ms_e2e, _ = _timed(torch, [(lambda q=q: ql.forward(q, x, out=y, ws=ws)) for q in qs])
+                r.update({"M": m, "K": k, "N": n, "scales": "E8M0 power of two" if pow2 else "float32",
+                          "weight_copies_rotated": len(qs), **info,
+                          "e2e_us_with_act_quant": round(ms_e2e * 1e3, 2),
                           "e2e_TFLOP/s": round(2.0 * m * n * k / (ms_e2e * 1e-3) / 1e12, 1)})
                 res.append(r)
-            out["a6_gemm_fp8_block"] = res
-            log("a6 done")
+                del qs
+            out["a6_gemm_fp8_block" if not pow2 else "next1_gemm_fp8_pow2"] = res
+            log(f"{name} done")
         del c4
 
     if "a5" in rows:   # NVFP4 prefill with LoRA r64
@@ -448,27 +529,67 @@ def run_rows(rows, torch, ql, dev):
             x = sg.normal_bf16((m, k), 1.0, sg.gen(sg.seed_of(3, si, 2)), c["x_out"], c["x_mult"], dev)
             a = sg.normal_bf16((r_, k), 0.01, sg.gen(sg.seed_of(3, si, 3)), device=dev)
             b = sg.normal_bf16((n, r_), 0.01, sg.gen(sg.seed_of(3, si, 4)), device=dev)
-            q = ql.quantize_nvfp4(w)
+            q0 = ql.quantize_nvfp4(w)
             del w
+            qs = [q0] + [ql.NVFP4Weight(q0.codes.clone(), q0.scales.clone(), q0.tensor_scale.clone(), n, k)
+                         for _ in range(_copies_for(n * k * 0.5625) - 1)]
             y = torch.empty((m, n), dtype=bf, device=dev)
             ws = torch.zeros(ql.binding.qlinear_forward_workspace(ql.QL_NVFP4, m, n, k, r_) + 16,
                              dtype=torch.uint8, device=dev)
-            ms = _events_ms(torch, lambda: ql.forward(q, x, a, b, c["lora_scale"], out=y, ws=ws), 10)
+            ms, info = _timed(torch, [(lambda q=q: ql.forward(q, x, a, b, c["lora_scale"], out=y, ws=ws)) for q in qs])
             flop = 2.0 * m * n * k + 2.0 * m * r_ * (k + n)
-            rr = _row("mfma", flop, ms, BF16_PEAK, "flop")
-            rr.update({"M": m, "K": k, "N": n, "rank": r_})
+            rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
+            rr.update({"M": m, "K": k, "N": n, "rank": r_, "weight_copies_rotated": len(qs), **info})
             res.append(rr)
+            del qs
         out["a5_gemm_nvfp4_prefill"] = res
         log("a5 done")
 
-    if "a8" in rows or "a9" in rows:
-        out.update(_policy(rows, torch, ql, dev))
+    if "kv" in rows:
+        out["next4_kv_fp8"] = _kv_rows(torch, ql, dev)
+        log("kv done")
+
+    if rows & {"a8", "a8u", "a9"}:
+        out.update(_policy(rows, torch, ql, dev, with_ceiling))
     return out
 
 
-def _policy(rows, torch, ql, dev):
-    """64 decoder layers of 32B-class linears: requantize after a rank-64 update, then
-    one decode step at 256 tokens through all 448 linears with LoRA r32."""
+def _kv_rows(torch, ql, dev):
+    """FP8 KV-cache codec at the 32B-class attention geometry (8 KV heads x 128): a store of
+    32768 new tokens (e.g. 8 prompts of 4096) into random slots of a 262144-slot cache, and a
+    load (gather) of 32768 cached tokens.  Algorithmic bytes per token: H D (2 + 1) + 4 H + 8."""
+    from synth import gpu as sg
+    heads, hd, slots_total, t = 8, 128, 262144, 32768
+    codes = torch.zeros((slots_total, heads, hd), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((slots_total, heads), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    g = sg.gen(sg.seed_of(6, 0, 2))
+    nsets = 4
+    kvs = [sg.normal_bf16((t, heads, hd), 1.0, g, device=dev) for _ in range(nsets)]
+    slots = [torch.randperm(slots_total, generator=g, device=dev)[:t].contiguous() for _ in range(nsets)]
+    outs = [torch.empty((t, heads, hd), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    by = t * (heads * hd * 3 + 4 * heads + 8)
+    res = []
+    ms, info = _timed(torch, [(lambda i=i: ql.binding.qlinear_kv_store_fp8(kvs[i], slots[i], codes, scales, status))
+                              for i in range(nsets)])
+    r = _row("hbm", by, ms, HBM_PEAK, "B")
+    r.update({"op": "store", "tokens": t, "heads": heads, "head_dim": hd, "cache_slots": slots_total, **info})
+    res.append(r)
+    ms, info = _timed(torch, [(lambda i=i: ql.binding.qlinear_kv_load_fp8(codes, scales, slots[i], outs[i], status))
+                              for i in range(nsets)])
+    r = _row("hbm", by, ms, HBM_PEAK, "B")
+    r.update({"op": "load", "tokens": t, "heads": heads, "head_dim": hd, "cache_slots": slots_total, **info})
+    res.append(r)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("kv codec reported a bad slot")
+    return res
+
+
+def _policy(rows, torch, ql, dev, with_ceiling):
+    """64 decoder layers of 32B-class linears: requantize after a rank-64 update, the fused
+    apply-update + requantize, then one decode step at 256 tokens through all 448 linears
+    with LoRA r32."""
     import synth
     from synth import gpu as sg
     c = synth.CFG5
@@ -492,14 +613,44 @@ def _policy(rows, torch, ql, dev):
         sg.rank_update_(w, c["delta_rank"], c["delta_std"], sg.gen(sg.seed_of(5, i % 7, 7, i // 7, 1)))
     torch.cuda.synchronize()
     delta_s = time.time() - t0
-    ms = _events_ms(torch, table.requantize_all, 3)
+    ms, info = _timed(torch, [table.requantize_all], iters=20, repeats=5, warmup=2)
     alg = params * 2.5625 + 4 * len(ws_list)
     r = _row("hbm", alg, ms, HBM_PEAK, "B")
     r.update({"tensors": len(ws_list), "params": params, "two_pass_bytes": params * 4.5625,
               "two_pass_GB/s": round(params * 4.5625 / (ms * 1e-3) / 1e9, 1),
-              "delta_update_s_harness": round(delta_s, 3), "gen_s": round(gen_s, 1)})
+              "delta_update_s_harness": round(delta_s, 3), "gen_s": round(gen_s, 1), **info})
     out["a8_requantize_all"] = r
+    if int(table.status()) != 0:
+        raise RuntimeError("requantize_all reported a non-finite weight")
     log("a8 done")
+    if "a8u" in rows:
+        # the same update given as dense bf16 deltas (one per tensor), applied inside the
+        # requantization: W <- bf16(W + delta) with the tensor amax as a by-product, then the
+        # encode pass.  Algorithmic bytes per parameter: 2 + 2 read, 2 written (the update),
+        # then 2 read + 0.5625 written (the encode) = 8.5625; 2.5625 of it beyond the update.
+        deltas = []
+        for i, w in enumerate(ws_list):
+            n, k = w.shape
+            g = sg.gen(sg.seed_of(5, i % 7, 8, i // 7, 1))
+            a_ = torch.randn((c["delta_rank"], k), generator=g, device=dev, dtype=torch.float32)
+            b_ = torch.randn((n, c["delta_rank"]), generator=g, device=dev, dtype=torch.float32)
+            deltas.append((b_ @ a_).mul_(c["delta_std"] / c["delta_rank"] ** 0.5).to(torch.bfloat16))
+            del a_, b_
+        table.set_updates(deltas)
+        torch.cuda.synchronize()
+        ms, info = _timed(torch, [table.update_requantize_all], iters=20, repeats=5, warmup=2)
+        alg_u = params * 8.5625 + 4 * len(ws_list)
+        r = _row("hbm", alg_u, ms, HBM_PEAK, "B")
+        r.update({"tensors": len(ws_list), "params": params, "B_per_param": 8.5625,
+                  "B_per_param_beyond_update": 2.5625,
+                  "separate_update_then_requant_B_per_param": 6 + 4.5625, **info})
+        out["next3_update_requantize_all"] = r
+        if int(table.status()) != 0:
+            raise RuntimeError("update_requantize_all reported a non-finite weight")
+        table.set_updates([])
+        del deltas
+        torch.cuda.empty_cache()
+        log("a8u done")
     del ws_list
     if "a9" in rows:
         m, r_ = c["M"], c["rank"]
@@ -521,19 +672,23 @@ def _policy(rows, torch, ql, dev):
                 a, b = loras[i]
                 ql.forward(q, xs[li], a, b, c["lora_scale"], out=ys[li], ws=wss[li])
 
-        ms = _events_ms(torch, decode_step, 3)
+        ms, info = _timed(torch, [decode_step], iters=20, repeats=5, warmup=2)
         flop = sum(2.0 * m * (n * k + r_ * (k + n)) for (_, k, n) in synth.CFG5_LINEARS) * c["layers"]
-        rr = _row("mfma", flop, ms, BF16_PEAK, "flop")
-        rr.update({"M": m, "linears": len(qs), "requant_over_decode": round(out["a8_requantize_all"]["us"] / (ms * 1e3), 3)})
+        rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
+        rr.update({"M": m, "linears": len(qs), **info,
+                   "requant_over_decode": round(out["a8_requantize_all"]["us"] / (ms * 1e3), 3)})
         out["a9_policy_decode_step"] = rr
     return out
 
 
-def cpu_baseline(budget_s):
+def cpu_baseline(budget_s, full=False):
     """The oracle (unchanged) on a bounded sample of the decode workload: the two
     3584-deep shapes with N in {3584, 512} at every M, layer calls repeated until the
     time budget is used.  Weights are quantized by the oracle outside the timing, as
-    the GPU's are."""
+    the GPU's are.  `extended` adds the oracle quantizers on whole tensors (single
+    thread), the other configurations' layers on sampled tokens x columns with the
+    full-size time extrapolated (and labelled so), and the quantization error of each
+    format against the unquantized bf16 layer (reported, not gated)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -561,7 +716,122 @@ def cpu_baseline(budget_s):
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{calls} layer calls of (K,N) in {{(3584,3584),(3584,512)}} x M in {{1,8,64}}, "
                       f"LoRA r32, float64 oracle on NVFP4 codes, {dt:.1f} s",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "nproc": _nproc(),
+            "extended": _cpu_extended(full)}
+
+
+def _nproc():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def _cpu_extended(full):
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import synth
+    from oracle import fp8 as ofp8, gemm as ogemm, nvfp4 as onv
+
+    ext = {}
+    # ---- quantizers on whole tensors, one thread (numpy elementwise code)
+    qt = []
+
+    def q_time(name, fn, bits, params):
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            fn(bits)
+            dt = time.perf_counter() - t0
+        qt.append({"quantizer": name, "shape": list(bits.shape), "s": round(dt, 3),
+                   "Mparam/s": round(params / dt / 1e6, 2)})
+
+    nv_shapes = [DECODE_SHAPES[0]] if not full else list(DECODE_SHAPES)
+    for si, (k, n) in enumerate(DECODE_SHAPES):
+        if (k, n) in nv_shapes:
+            q_time("nvfp4 (config 2)", onv.quantize, synth.config2_weight(si), n * k)
+    c4_shapes = list(enumerate(synth.CFG4_SHAPES))[:1] if not full else list(enumerate(synth.CFG4_SHAPES))
+    for si, (k, n) in c4_shapes:
+        w = synth.config4_weight(si)
+        q_time("fp8 128x128 weight (config 4)", ofp8.quantize_weight, w, n * k)
+        if full:
+            q_time("fp8 power-of-two weight (config 4)", ofp8.quantize_weight_pow2, w, n * k)
+        x = synth.config4_x(si)
+        q_time("fp8 1x128 activation (config 4)", ofp8.quantize_act, x, x.size)
+        del w, x
+    if full:
+        for si, (k, n) in enumerate(synth.CFG3_SHAPES):
+            q_time("nvfp4 (config 3)", onv.quantize, synth.config3_weight(si), n * k)
+        q_time("nvfp4 (config 1)", onv.quantize, synth.config1()["w"], 256 * 512)
+    ext["quantizers_one_thread"] = qt
+
+    # ---- other configurations' layers on sampled tokens x output columns (BLAS threads as
+    # the headline sample); weights of the sampled rows drawn from the same distribution and
+    # quantized with their own tensor scale (timing only); full size extrapolated linearly
+    g = np.random.default_rng([9, 9, 9])
+    gs = []
+
+    def g_time(cfg, k, n, m_full, n_full, m_s, n_s, fn, count=1):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        gs.append({"config": cfg, "K": k, "N": n_full, "M": m_full, "sample_tokens": m_s, "sample_columns": n_s,
+                   "s": round(dt, 3), "layers": count,
+                   "extrapolated_full_s": round(dt * (m_full / m_s) * (n_full / n_s) * count, 1),
+                   "extrapolated": True})
+
+    c3 = synth.CFG3
+    for (k, n) in synth.CFG3_SHAPES:
+        w = synth.normal_bf16((512, k), c3["w_std"], g, c3["w_out"], c3["w_mult"])
+        codes, scales, S = onv.quantize(w)
+        x = synth.normal_bf16((16, k), 1.0, g, c3["x_out"], c3["x_mult"])
+        a = synth.normal_bf16((c3["rank"], k), 0.01, g)
+        b = synth.normal_bf16((512, c3["rank"]), 0.01, g)
+        g_time(3, k, n, c3["M"], n, 16, 512,
+               lambda: ogemm.forward_nvfp4(x, codes, scales, S, a, b, c3["lora_scale"]))
+    for (k, n) in synth.CFG4_SHAPES:
+        w = synth.normal_bf16((512, k), 0.02, g)
+        wq, sw = ofp8.quantize_weight(w)
+        x = synth.student_t_bf16((16, k), 3, g)
+        g_time(4, k, n, synth.CFG4["M"], n, 16, 512, lambda: ogemm.forward_fp8_from_bf16(x, wq, sw))
+    c5 = synth.CFG5
+    for (name, k, n) in synth.CFG5_LINEARS:
+        w = synth.normal_bf16((256, k), c5["w_std"], g, c5["w_out"], c5["w_mult"])
+        codes, scales, S = onv.quantize(w)
+        x = synth.normal_bf16((4, k), 1.0, g)
+        a = synth.normal_bf16((c5["rank"], k), 0.01, g)
+        b = synth.normal_bf16((256, c5["rank"]), 0.01, g)
+        g_time(f"5 ({name})", k, n, c5["M"], n, 4, 256,
+               lambda: ogemm.forward_nvfp4(x, codes, scales, S, a, b, c5["lora_scale"]), count=c5["layers"])
+    ext["layers_sampled"] = gs
+    ext["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+    # ---- quantization error against the unquantized bf16 layer (float64), not gated
+    qe = []
+    k, n = DECODE_SHAPES[0]
+    w = synth.config2_weight(0)
+    codes, scales, S = onv.quantize(w)
+    a, b = synth.config2_lora(0)
+    for m in (1, 8):
+        x = synth.config2_x(0, m)
+        ref = ogemm.forward_bf16_reference(x, w, a, b, LORA_S)
+        y = ogemm.forward_nvfp4(x, codes, scales, S, a, b, LORA_S)
+        qe.append({"format": "nvfp4", "config": 2, "M": m, "K": k, "N": n, "rank": RANK,
+                   "rel_err_inf": round(ogemm.rel_err_inf(y, ref), 5),
+                   "rel_err_fro": round(float(np.linalg.norm(y - ref) / np.linalg.norm(ref)), 5)})
+    k4, _ = synth.CFG4_SHAPES[0]
+    w = synth.normal_bf16((256, k4), 0.02, g)
+    x = synth.student_t_bf16((64, k4), 3, g)
+    ref = ogemm.forward_bf16_reference(x, w)
+    wq, sw = ofp8.quantize_weight(w)
+    wq2, ew = ofp8.quantize_weight_pow2(w)
+    for fmt, y in (("fp8 128x128 / 1x128", ogemm.forward_fp8_from_bf16(x, wq, sw)),
+                   ("fp8 power-of-two scales", ogemm.forward_fp8_pow2_from_bf16(x, wq2, ew))):
+        qe.append({"format": fmt, "config": "4 (64 tokens x 256 columns, Student-t(3) activations)", "K": k4,
+                   "rel_err_inf": round(ogemm.rel_err_inf(y, ref), 5),
+                   "rel_err_fro": round(float(np.linalg.norm(y - ref) / np.linalg.norm(ref)), 5)})
+    ext["quant_error_vs_bf16"] = qe
+    return ext
 
 
 if __name__ == "__main__":
