@@ -45,11 +45,43 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27860981, "fetch_bytes": 26567615, "write_bytes": 1293365,
+DECODE_TRAFFIC = {"bytes_per_launch": 27870985, "fetch_bytes": 26577128, "write_bytes": 1293856,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "0cd737143e3cc52fc5925b4e6ab26e7fa8776e45a06af2af3f92d7fe78f06454"}
+                  "sources_sha256": "196070371184e7890481574a0ae54f7840296f58789316cac0f5fb713e85d080"}
+
+# Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
+# duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over
+#   bench.py --rows <row> --row-iters 3 --steps-only --steps 3 --warmup 1 --no-cpu-baseline
+# (mean over both shapes of the row).  Reported only while the kernel sources are the ones
+# measured (hash), like the traffic above.
+COUNTER_CLOCKS = {
+    "a5": {"GHz": 1.90, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+                                    "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
+           "sources_sha256": "6241ee12eab3d724c7ed304daea81de8201316c8c9737112d2f1a34b19a929b2"},
+    "a6": {"GHz": 1.99, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+                                    "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
+           "sources_sha256": "007ef314ff16ad4f379c865274458fcaed212bde9d6b79f3c160addf54ba1f38"},
+    "a6p": {"GHz": 2.08, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
+            "sources_sha256": "007ef314ff16ad4f379c865274458fcaed212bde9d6b79f3c160addf54ba1f38"},
+}
+
+
+def _sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_clock(row):
+    """The counter-measured clock of a row's kernel, or None once its sources changed."""
+    c = COUNTER_CLOCKS.get(row)
+    return c["GHz"] if c and _sources_sha(c["sources"]) == c["sources_sha256"] else None
 
 
 def decode_traffic():
@@ -86,6 +118,13 @@ def parse():
     ap.add_argument("--steps-only", action="store_true",
                     help="time the decode step only (no per-call launches, no copy ceiling): every layer "
                          "call is launched equally often, as hardware-counter runs need")
+    ap.add_argument("--row-iters", type=int, default=0, metavar="N",
+                    help="time each row with N calls after one warm-up call (counter runs); "
+                         "default: warm-up 10, 5 x 20 calls")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="only print per-kernel means of rocprofv3 counter CSVs under DIR ... (markdown)")
+    ap.add_argument("--summarize-stats", nargs="+", metavar="DIR",
+                    help="only print the rocprofv3 --stats kernel summaries under DIR ... (markdown)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -143,6 +182,14 @@ class Timer:
 
 def main():
     args = parse()
+    global ROW_ITERS
+    ROW_ITERS = args.row_iters
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
         return
@@ -324,11 +371,16 @@ def _events_ms(torch, fn, reps):
     return t.total_ms() / reps
 
 
+ROW_ITERS = 0  # --row-iters: calls per row in counter runs (0: the protocol below)
+
+
 def _timed(torch, fns, iters=100, repeats=5, warmup=10):
     """The rows' timing protocol: `warmup` untimed calls, then `repeats` blocks of
     iters / repeats back-to-back calls (fns[0], fns[1], ... in turn over rotated buffers),
     HIP events on the current stream around each block.  Returns the median block mean
     (ms) with the block spread."""
+    if ROW_ITERS > 0:
+        iters, repeats, warmup = ROW_ITERS, 1, 1
     for i in range(warmup):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
@@ -433,10 +485,13 @@ def run_rows(rows, torch, ql, dev):
         log("MFMA ceiling done")
 
     def with_ceiling(r, name):
+        # against the fastest measured MFMA shape of the row's precision class
         if ceil is not None:
-            c = ceil[name]
+            cls = [v for k, v in ceil.items() if k.startswith("fp8")] if name.startswith("fp8") else \
+                  [v for k, v in ceil.items() if not k.startswith("fp8")]
+            c = max(cls, key=lambda v: v["TFLOP/s"])
             r.update({"frac_of_measured_ceiling": round(r["TFLOP/s"] / c["TFLOP/s"], 4),
-                      "mfma_loop_clock_GHz": c["clock_GHz"]})
+                      "measured_ceiling_TFLOP/s": c["TFLOP/s"], "mfma_loop_clock_GHz": c["clock_GHz"]})
         return r
 
     if "a1" in rows:   # NVFP4 weight quantizer on the decode weights (2.5625 B/param)
@@ -511,6 +566,7 @@ def run_rows(rows, torch, ql, dev):
                 r = with_ceiling(_row("mfma", 2.0 * m * n * k, ms, FP8_PEAK, "flop"), "fp8_scaled_16x16x128")
                 ms_e2e, _ = _timed(torch, [(lambda q=q: ql.forward(q, x, out=y, ws=ws)) for q in qs])
                 r.update({"M": m, "K": k, "N": n, "scales": "E8M0 power of two" if pow2 else "float32",
+                          "counter_clock_GHz": counter_clock(name),
                           "weight_copies_rotated": len(qs), **info,
                           "e2e_us_with_act_quant": round(ms_e2e * 1e3, 2),
                           "e2e_TFLOP/s": round(2.0 * m * n * k / (ms_e2e * 1e-3) / 1e12, 1)})
@@ -539,7 +595,8 @@ def run_rows(rows, torch, ql, dev):
             ms, info = _timed(torch, [(lambda q=q: ql.forward(q, x, a, b, c["lora_scale"], out=y, ws=ws)) for q in qs])
             flop = 2.0 * m * n * k + 2.0 * m * r_ * (k + n)
             rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
-            rr.update({"M": m, "K": k, "N": n, "rank": r_, "weight_copies_rotated": len(qs), **info})
+            rr.update({"M": m, "K": k, "N": n, "rank": r_, "weight_copies_rotated": len(qs),
+                       "counter_clock_GHz": counter_clock("a5"), **info})
             res.append(rr)
             del qs
         out["a5_gemm_nvfp4_prefill"] = res
@@ -679,6 +736,44 @@ def _policy(rows, torch, ql, dev, with_ceiling):
                    "requant_over_decode": round(out["a8_requantize_all"]["us"] / (ms * 1e3), 3)})
         out["a9_policy_decode_step"] = rr
     return out
+
+
+def summarize_counters(dirs):
+    """Per-kernel mean per dispatch of every counter in the rocprofv3 counter CSVs under
+    `dirs` (one directory per counter pass), as a markdown table."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(lambda: defaultdict(set))
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    kn = row["Kernel_Name"].split("(")[0].replace("void ", "")
+                    vals[kn][row["Counter_Name"]] += float(row["Counter_Value"])
+                    disp[kn][row["Counter_Name"]].add(row.get("Dispatch_Id") or row.get("Correlation_Id"))
+    print("| kernel | dispatches | counter | mean per dispatch |\n|---|---|---|---|")
+    for kn in sorted(vals):
+        for c in sorted(vals[kn]):
+            nd = max(1, len(disp[kn][c]))
+            print(f"| `{kn}` | {nd} | {c} | {vals[kn][c] / nd:.6g} |")
+
+
+def summarize_stats(dirs):
+    """The rocprofv3 --stats kernel tables under `dirs`, as markdown."""
+    import csv
+    import glob
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            with open(f) as fh:
+                rows = list(csv.DictReader(fh))
+            print(f"{os.path.relpath(f, d)}\n\n| kernel | calls | total ms | average us | min us | max us |\n|---|---|---|---|---|---|")
+            for r in rows:
+                kn = r["Name"].split("(")[0].replace("void ", "")
+                print(f"| `{kn}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+            print()
 
 
 def cpu_baseline(budget_s, full=False):
