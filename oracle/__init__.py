@@ -23,10 +23,12 @@ What it computes (each module cites the passage it follows):
   that requantization.
 * ``kvcache`` -- the FP8 KV-cache codec: E4M3 codes with one float32 scale per cached
   (token, head) vector, scattered to and gathered from cache slots.
+* ``backward`` -- the layer's backward pass with the NVFP4 base frozen: dX through the
+  dequantized weight and the adapter, and the adapter's gradients dA, dB, in float64.
 
 Quantizer arithmetic is IEEE float32 with round-to-nearest-even, because that is
 where the codes are decided and the GPU decides them in float32 too; every
 GEMM and every dequantized value is float64.
 """
 
-from . import codecs, nvfp4, fp8, gemm, requant, update, kvcache  # noqa: F401
+from . import codecs, nvfp4, fp8, gemm, requant, update, kvcache, backward  # noqa: F401
