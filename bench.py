@@ -346,7 +346,7 @@ def main():
 
     log(f"decode step: {ms_per_step:.3f} ms, {value:.1f} GB/s")
     rows = set(args.rows.split(",")) if args.rows not in ("all", "none") else (
-        {"a1", "a2", "a3", "a5", "a6", "a6p", "a8", "a8u", "a9", "kv", "ceil"} if args.rows == "all" else set())
+        {"a1", "a2", "a3", "a5", "a6", "a6p", "a8", "a8u", "a9", "kv", "bwd", "ceil"} if args.rows == "all" else set())
     if rows:
         result["rows"] = run_rows(rows, torch, ql, dev)
 
@@ -479,7 +479,7 @@ def run_rows(rows, torch, ql, dev):
 
     log(f"rows {sorted(rows)}")
     ceil = None
-    if rows & {"ceil", "a5", "a6", "a6p", "a9"}:
+    if rows & {"ceil", "a5", "a6", "a6p", "a9", "bwd"}:
         ceil = mfma_ceiling(torch, dev)
         out["ceiling_mfma"] = ceil
         log("MFMA ceiling done")
@@ -601,6 +601,37 @@ def run_rows(rows, torch, ql, dev):
             del qs
         out["a5_gemm_nvfp4_prefill"] = res
         log("a5 done")
+
+    if "bwd" in rows:   # backward of the NVFP4 + LoRA layer at the prefill shapes
+        res = []
+        c = synth.CFG3
+        for si, (k, n) in enumerate(synth.CFG3_SHAPES):
+            m, r_ = c["M"], c["rank"]
+            w = sg.normal_bf16((n, k), c["w_std"], sg.gen(sg.seed_of(3, si, 1)), c["w_out"], c["w_mult"], dev)
+            x = sg.normal_bf16((m, k), 1.0, sg.gen(sg.seed_of(3, si, 2)), c["x_out"], c["x_mult"], dev)
+            dy = sg.normal_bf16((m, n), 1.0, sg.gen(sg.seed_of(3, si, 9)), device=dev)
+            a = sg.normal_bf16((r_, k), 0.01, sg.gen(sg.seed_of(3, si, 3)), device=dev)
+            b = sg.normal_bf16((n, r_), 0.01, sg.gen(sg.seed_of(3, si, 4)), device=dev)
+            q0 = ql.quantize_nvfp4(w)
+            del w
+            qs = [q0] + [ql.NVFP4Weight(q0.codes.clone(), q0.scales.clone(), q0.tensor_scale.clone(), n, k)
+                         for _ in range(_copies_for(n * k * 0.5625) - 1)]
+            dx = torch.empty((m, k), dtype=bf, device=dev)
+            da = torch.empty((r_, k), dtype=torch.float32, device=dev)
+            db = torch.empty((n, r_), dtype=torch.float32, device=dev)
+            ws = torch.zeros(ql.binding.qlinear_backward_workspace(ql.QL_NVFP4, m, n, k, r_), dtype=torch.uint8,
+                             device=dev)
+            fns = [(lambda q=q: ql.binding.qlinear_backward(q.qweight(), x, dy, dx, ql.QL_OUT_BF16, da, db, ws, a, b,
+                                                            r_, c["lora_scale"])) for q in qs]
+            ms, info = _timed(torch, fns)
+            flop = 2.0 * m * n * k + 2.0 * m * r_ * (2 * n + 3 * k)
+            rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
+            rr.update({"M": m, "K": k, "N": n, "rank": r_, "outputs": "dX bf16, dA and dB float32",
+                       "weight_copies_rotated": len(qs), **info})
+            res.append(rr)
+            del qs
+        out["next2_backward_nvfp4"] = res
+        log("bwd done")
 
     if "kv" in rows:
         out["next4_kv_fp8"] = _kv_rows(torch, ql, dev)

@@ -244,6 +244,30 @@ qlinear_status qlinear_forward_noalloc(const qlinear_qweight* w, const uint16_t*
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank);
 size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
 
+/* Backward pass of the NVFP4 + LoRA layer for LoRA training on the frozen 4-bit base
+ * (tldrocket.com QeRL page, "Key Features of QeRL" and the paragraph after it: backprop
+ * stays stable through LoRA, its gradients in higher precision; rapidrecap.app Jet-RL
+ * summary, "Key Points": BF16 backward).  Given dy = dL/dy (bf16 [m][n]) of
+ * y = x W^T + s (x A^T) B^T with W = dequant(w):
+ *   dx [m][k] = dy . W + bf16(du) . A,  du = s . dy . B      (bf16 or float32 per dx_dtype)
+ *   da [r][k] = du^T . x                                       (float32)
+ *   db [n][r] = dy^T . t,                t = s . x . A^T        (float32)
+ * with float32 accumulation; du and t enter da and db with about 16 significant bits (a
+ * bf16 pair) and du enters dx rounded to bf16, as the forward rounds t.  w must be QL_NVFP4 with n % 64 == 0 and k % 128 == 0.  Without
+ * an adapter (rank 0, a NULL lora pointer or lora_scale 0) only dx is computed and x, da,
+ * db may be NULL.  Workspace: qlinear_backward_workspace(format, m, n, k, rank) bytes of
+ * scratch (0 without an adapter: ws may then be NULL); no zeroing or reserved region is
+ * needed and it may be reused by any call once this one has finished on its stream.
+ * All pointers 16-byte aligned; the caller owns every buffer.  Errors: QL_ERR_NULL,
+ * QL_ERR_SHAPE (m <= 0, m > QLINEAR_MAX_M, n % 64, k % 128, sizes beyond
+ * QLINEAR_MAX_ELEMS), QL_ERR_FORMAT (not NVFP4, or dx_dtype), QL_ERR_ARG (rank < 0 or >
+ * QLINEAR_MAX_RANK), QL_ERR_ALIGN, QL_ERR_WORKSPACE. */
+qlinear_status qlinear_backward(const qlinear_qweight* w, const uint16_t* x, const uint16_t* dy,
+                                int64_t m, const uint16_t* lora_a, const uint16_t* lora_b,
+                                int32_t rank, float lora_scale, void* dx, int32_t dx_dtype,
+                                float* da, float* db, void* ws, size_t ws_bytes, void* stream);
+size_t qlinear_backward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank);
+
 /* ------------------------------------------------------ whole-policy requant */
 
 /* After every training step the RL recipe recalibrates the quantization of the

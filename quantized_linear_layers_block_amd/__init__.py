@@ -150,6 +150,26 @@ def forward_fp8_prequant(qw, xq, sx, x=None, lora_a=None, lora_b=None, lora_scal
     return out
 
 
+def backward(qw, dy, x=None, lora_a=None, lora_b=None, lora_scale=0.0, dx_dtype=torch.bfloat16, ws=None):
+    """Gradients of the NVFP4 layer with LoRA: (dx, da, db); da, db are float32 (None
+    without an adapter)."""
+    _dev(_u16(dy))
+    if not isinstance(qw, NVFP4Weight):
+        raise TypeError("the backward pass is defined for NVFP4 weights")
+    m = dy.shape[0]
+    rank = 0 if lora_a is None else lora_a.shape[0]
+    eff_rank = rank if (lora_a is not None and lora_b is not None and lora_scale != 0) else 0
+    dx = torch.empty((m, qw.k), dtype=dx_dtype, device=dy.device)
+    da = torch.empty((rank, qw.k), dtype=torch.float32, device=dy.device) if eff_rank else None
+    db = torch.empty((qw.n, rank), dtype=torch.float32, device=dy.device) if eff_rank else None
+    if ws is None:
+        nb = binding.qlinear_backward_workspace(QL_NVFP4, m, qw.n, qw.k, eff_rank)
+        ws = _ws(nb, dy.device) if nb else None
+    od = QL_OUT_F32 if dx_dtype == torch.float32 else QL_OUT_BF16
+    binding.qlinear_backward(qw.qweight(), x, dy, dx, od, da, db, ws, lora_a, lora_b, rank, lora_scale)
+    return dx, da, db
+
+
 class RequantTable:
     """A whole policy to requantize after every training step: a list of (bf16 weight,
     quantized weight) pairs, whose item array is copied to the device once."""

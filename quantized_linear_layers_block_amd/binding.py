@@ -37,6 +37,8 @@ EXPORTS = [
     "qlinear_update_requantize_all",
     "qlinear_kv_store_fp8",
     "qlinear_kv_load_fp8",
+    "qlinear_backward",
+    "qlinear_backward_workspace",
 ]
 
 QLINEAR_STATUS_NONFINITE, QLINEAR_STATUS_TIMEOUT, QLINEAR_STATUS_BAD_ITEM = 1, 2, 4
@@ -87,6 +89,9 @@ def _load():
         "qlinear_update_requantize_all": ([vp, vp, i32, i32, vp, sz, vp], i32),
         "qlinear_kv_store_fp8": ([vp, i64, i32, i32, vp, vp, vp, i64, vp, vp], i32),
         "qlinear_kv_load_fp8": ([vp, vp, i64, vp, i64, i32, i32, vp, vp, vp], i32),
+        "qlinear_backward": ([ctypes.POINTER(QWeight), vp, vp, i64, vp, vp, i32, f32, vp, i32, vp, vp, vp, sz, vp],
+                             i32),
+        "qlinear_backward_workspace": ([i32, i64, i64, i64, i32], sz),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -182,6 +187,21 @@ def qlinear_forward(qw, x, y, out_dtype, ws=None, lora_a=None, lora_b=None, rank
     _check(LIB.qlinear_forward(ctypes.byref(qw), _ptr(x), m, _ptr(lora_a), _ptr(lora_b), rank,
                                float(lora_scale), _ptr(y), out_dtype, _ptr(ws), wsb, _stream(stream)),
            "qlinear_forward")
+
+
+def qlinear_backward_workspace(fmt, m, n, k, rank):
+    return LIB.qlinear_backward_workspace(fmt, m, n, k, rank)
+
+
+def qlinear_backward(qw, x, dy, dx, dx_dtype, da=None, db=None, ws=None, lora_a=None, lora_b=None, rank=0,
+                     lora_scale=0.0, stream=None):
+    """dx [m,k] = dy . dequant(qw) + du . A; da [r,k] = du^T x; db [n,r] = dy^T t (du, t: bf16)."""
+    m = dy.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(LIB.qlinear_backward(ctypes.byref(qw), _ptr(x), _ptr(dy), m, _ptr(lora_a), _ptr(lora_b), rank,
+                                float(lora_scale), _ptr(dx), dx_dtype, _ptr(da), _ptr(db), _ptr(ws), wsb,
+                                _stream(stream)),
+           "qlinear_backward")
 
 
 def qlinear_forward_noalloc(qw, x, y, out_dtype, lora_a=None, lora_b=None, rank=0, lora_scale=0.0,

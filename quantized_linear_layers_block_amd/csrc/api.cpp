@@ -276,6 +276,43 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
                                         w->format == QL_FP8_POW2, t, lora_b, r, y, out_dtype == QL_OUT_F32, s));
 }
 
+// ------------------------------------------------------------------ backward
+
+static bool backward_shape_ok(int64_t m, int64_t n, int64_t k) {
+  return m > 0 && m <= QLINEAR_MAX_M && n % 64 == 0 && k % 128 == 0 && elems_ok(n, k) && elems_ok(m, n) &&
+         elems_ok(m, k);
+}
+
+size_t qlinear_backward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank) {
+  if (format != QL_NVFP4 || !backward_shape_ok(m, n, k) || rank < 0 || rank > QLINEAR_MAX_RANK) return 0;
+  return up(ql::backward_scratch_bytes(m, n, k, rank));
+}
+
+qlinear_status qlinear_backward(const qlinear_qweight* w, const uint16_t* x, const uint16_t* dy,
+                                int64_t m, const uint16_t* lora_a, const uint16_t* lora_b,
+                                int32_t rank, float lora_scale, void* dx, int32_t dx_dtype,
+                                float* da, float* db, void* ws, size_t ws_bytes, void* stream) {
+  qlinear_status st = check_qweight(w);
+  if (st != QL_OK) return st;
+  if (w->format != QL_NVFP4) return QL_ERR_FORMAT;
+  if (!dy || !dx) return QL_ERR_NULL;
+  if (!backward_shape_ok(m, w->n, w->k)) return QL_ERR_SHAPE;
+  if (rank < 0 || rank > QLINEAR_MAX_RANK) return QL_ERR_ARG;
+  if (dx_dtype != QL_OUT_BF16 && dx_dtype != QL_OUT_F32) return QL_ERR_FORMAT;
+  const int32_t r = lora_rank(lora_a, lora_b, rank, lora_scale);
+  if (r > 0 && (!x || !da || !db)) return QL_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(dx) || (x && !aligned16(x)) || (lora_a && !aligned16(lora_a)) ||
+      (lora_b && !aligned16(lora_b)) || (da && !aligned16(da)) || (db && !aligned16(db)))
+    return QL_ERR_ALIGN;
+  const size_t need = up(ql::backward_scratch_bytes(m, w->n, w->k, r));
+  if (need > 0 && (!ws || ws_bytes < need)) return QL_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return QL_ERR_ALIGN;
+  return hip_status(ql::launch_backward_nvfp4(x, dy, m, w->n, w->k, (const uint8_t*)w->codes,
+                                              (const uint8_t*)w->scales, w->tensor_scale, lora_a, lora_b, r,
+                                              lora_scale, dx, dx_dtype == QL_OUT_F32, da, db, ws,
+                                              (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------- requant
 
 size_t qlinear_requant_workspace(int32_t count) {

@@ -1,0 +1,399 @@
+// Backward pass of the NVFP4 + LoRA layer on gfx950, for LoRA training on top of the frozen
+// 4-bit base (QeRL keeps backprop stable through LoRA with its gradients in higher
+// precision: tldrocket.com QeRL page, "Key Features of QeRL" and the paragraph after it;
+// Jet-RL keeps the backward in BF16: rapidrecap.app Jet-RL summary, "Key Points"):
+//
+//   dX = S . dY . (E2M1 * E4M3)  +  du . A        du = s . dY . B          [M, K]
+//   dA = du^T . x                                                          [r, K] float32
+//   dB = dY^T . t                                 t  = s . x . A^T         [N, r] float32
+//
+// du and t come from the forward's LoRA down-projection (du from a transposed copy of B) in
+// float32, each carried as a pair of bf16 values hi = bf16(v), lo = bf16(v - hi) (about 16
+// significant bits).  The adapter gradients use both (their sums over tokens keep the
+// precision the pages ask for); dX, an activation gradient like the forward's output, uses
+// du rounded to bf16 as the forward uses t.  Three kernels are new here:
+//
+// * bwd_dx_kernel: the transposed NVFP4 product.  The forward reduces over K, along the
+//   rows of the packed codes; here the reduction runs over N, across rows, so each stage's
+//   code tile (64 rows of N x 128 columns of K) is dequantized in registers -- E2M1 by the
+//   hardware converter, times the E4M3 block scale, an exact bf16 -- and written to LDS
+//   transposed (K-major), where it is the A operand of 16x16x32 bf16 MFMAs; the dY tile
+//   (128 tokens x 64) is the B operand.  Workgroup tile 128 (K) x 128 (M), four waves of
+//   64 x 64, stages of 64 along N with the next stage's loads in flight during the MFMAs.
+//   S is applied in float32, then bf16(du) . A is added as r_pad / 32 more MFMA steps.
+// * bwd_mtm_kernel: G[c][j] = sum over a range of tokens of P[m][c] Q[m][j] (P = dY, Q = the
+//   hi | lo columns of t for dB; P = x, Q = those of du for dA): both operands are
+//   transposed into LDS (token-major rows) and multiplied with bf16 MFMAs into float32;
+//   the token range is split over workgroups and bwd_reduce_kernel adds, in a fixed order,
+//   the split partials of the hi columns, those of the lo columns, and the two sums.
+// * bwd_transpose_kernel: B [N, r] -> B^T [r, N] for the down-projection of dY.
+#include "../../include/qlinear.h"
+#include "common.hpp"
+#include "gemm_common.hpp"
+#include "launch.hpp"
+
+namespace ql {
+
+// ------------------------------------------------------------------ dX
+constexpr int kBxTK = 128, kBxTM = 128, kBxTN = 64;
+
+struct BwdDxArgs {
+  const uint16_t* dy;  // [m][n] bf16
+  int64_t m, n, k;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  const uint16_t* du;      // [m][2 rank_pad] bf16, hi columns first (zero past rank), or null
+  const uint16_t* lora_a;  // [rank][k] bf16
+  int32_t rank, rank_pad;
+  void* dx;
+  int out_f32;
+};
+
+// LDS tiles, 128-byte rows of 64 bf16 in 16-byte slots swizzled by swz(): dY [128 m][64 n]
+// and the dequantized weights transposed, W^T [128 k][64 n].  A fragment read has 16 lanes
+// reading slot 2 g + h of 16 consecutive rows (conflict-free with this swizzle).
+__global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDxArgs a) {
+  __shared__ __align__(16) uint16_t ys[kBxTM * kBxTN];
+  __shared__ __align__(16) uint16_t wt[kBxTK * kBxTN];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int wk = wave & 1, wm = wave >> 1;  // wave tile: k 64 wk .. +64, m 64 wm .. +64
+  const int64_t k0 = (int64_t)blockIdx.x * kBxTK, m0 = (int64_t)blockIdx.y * kBxTM;
+
+  // Loads of one stage.  dY: units u = tid + 256 j, token row u / 8, 8-column slot u % 8
+  // (rows past M read zero).  Codes: rows 2 p and 2 p + 1 of the stage (p = tid / 8), 16
+  // columns of K from 16 (tid % 8) (8 bytes each), and the one block scale of each.
+  uint4 yv[4];
+  uint2 c0, c1;
+  uint32_t s0, s1;
+  const int pr = tid >> 3, kq = tid & 7;
+  auto issue = [&](int64_t n0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = tid + 256 * j;
+      const int64_t mr = m0 + (u >> 3);
+      const bool ok = mr < a.m;
+      const uint4 v = *(const uint4*)(a.dy + (ok ? mr : 0) * a.n + n0 + 8 * (u & 7));
+      const uint32_t mk = ok ? 0xFFFFFFFFu : 0u;
+      yv[j] = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
+    }
+    const int64_t n_a = n0 + 2 * pr;
+    c0 = *(const uint2*)(a.codes + n_a * (a.k / 2) + k0 / 2 + 8 * kq);
+    c1 = *(const uint2*)(a.codes + (n_a + 1) * (a.k / 2) + k0 / 2 + 8 * kq);
+    s0 = a.scales[n_a * (a.k / 16) + k0 / 16 + kq];
+    s1 = a.scales[(n_a + 1) * (a.k / 16) + k0 / 16 + kq];
+  };
+  // Stage to LDS: dY as loaded; the weights dequantized (exact bf16: at most 6 significant
+  // bits) and stored as pairs (n = 2 p, 2 p + 1) at W^T[16 kq + e][2 p .. 2 p + 1].
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = tid + 256 * j;
+      const int row = u >> 3;
+      *(uint4*)(ys + row * kBxTN + swz(row, u & 7) * 8) = yv[j];
+    }
+    const float sc0 = e4m3_value(s0), sc1 = e4m3_value(s1);
+    const uint32_t w0[2] = {c0.x, c0.y}, w1[2] = {c1.x, c1.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x2 u0[4] = {e2m1_unpack2<0>(w0[h]), e2m1_unpack2<1>(w0[h]), e2m1_unpack2<2>(w0[h]),
+                           e2m1_unpack2<3>(w0[h])};
+      const f32x2 u1[4] = {e2m1_unpack2<0>(w1[h]), e2m1_unpack2<1>(w1[h]), e2m1_unpack2<2>(w1[h]),
+                           e2m1_unpack2<3>(w1[h])};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x2 v0 = u0[b], v1 = u1[b];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kl = 16 * kq + 8 * h + 2 * b + e;
+          const uint32_t lo = __float_as_uint(v0[e] * sc0) >> 16, hi = __float_as_uint(v1[e] * sc1) & 0xFFFF0000u;
+          *(uint32_t*)(wt + kl * kBxTN + swz(kl, pr >> 2) * 8 + 2 * (pr & 3)) = lo | hi;
+        }
+      }
+    }
+  };
+
+  f32x4 acc[4][4];  // [k tile i][m tile j]: lane (r, g) holds k = 16 i + 4 g + e, m = 16 j + r
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  issue(0);
+  for (int64_t n0 = 0; n0 < a.n; n0 += kBxTN) {
+    __syncthreads();  // every wave is done reading the previous stage
+    store();
+    __syncthreads();
+    if (n0 + kBxTN < a.n) issue(n0 + kBxTN);  // in flight during the MFMAs
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 af[4], bq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kl = 64 * wk + 16 * i + r;
+        af[i] = *(const bf16x8*)(wt + kl * kBxTN + swz(kl, 2 * g + h) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = 64 * wm + 16 * j + r;
+        bq[j] = *(const bf16x8*)(ys + ml * kBxTN + swz(ml, 2 * g + h) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  const float S = *a.tensor_scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] *= S;
+  // du . A: A operand A^T[k][q] (rows q past the rank read zero), B operand du[m][q]
+  for (int q0 = 0; q0 < a.rank_pad; q0 += 32) {
+    const int q = q0 + 8 * g;
+    bf16x8 af[4], bq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = k0 + 64 * wk + 16 * i + r;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t lo = q + e < a.rank ? a.lora_a[(int64_t)(q + e) * a.k + kk] : 0u;
+        const uint32_t hi = q + e + 1 < a.rank ? a.lora_a[(int64_t)(q + e + 1) * a.k + kk] : 0u;
+        w[e / 2] = lo | (hi << 16);
+      }
+      af[i] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t mr = m0 + 64 * wm + 16 * j + r;
+      const uint4 v = *(const uint4*)(a.du + (mr < a.m ? mr : 0) * 2 * a.rank_pad + q);
+      bq[j] = __builtin_bit_cast(bf16x8, mr < a.m ? v : make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
+  }
+  // store: four consecutive k of one token per lane and tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t mr = m0 + 64 * wm + 16 * j + r;
+    if (mr >= a.m) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = k0 + 64 * wk + 16 * i + 4 * g;
+      const f32x4 v = acc[i][j];
+      if (a.out_f32) {
+        *(f32x4*)((float*)a.dx + mr * a.k + kk) = v;
+      } else {
+        *(uint2*)((uint16_t*)a.dx + mr * a.k + kk) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ adapter gradients
+// Workgroup: 64 columns c of P and all qc (<= 256, a multiple of 32) columns j of Q over
+// the token range [m_lo, m_hi) of its split, in stages of 32 tokens.  LDS: P^T [64][32 + 8]
+// and Q^T [qc][32 + 8] (bf16, rows padded to 80 bytes: a fragment read of 16 rows at one
+// offset touches 16 different bank groups).  Wave w: c tile w (16 columns) x all j tiles.
+constexpr int kBgTC = 64, kBgTM = 32, kBgPitch = kBgTM + 8;
+
+struct BwdMtmArgs {
+  const uint16_t* p;  // [m][c_total]
+  const uint16_t* q;  // [m][qc]
+  int64_t m, c_total, m_per_split;
+  int32_t qc;
+  float* part;        // [split][c_total][qc]
+};
+
+__global__ __launch_bounds__(256) void bwd_mtm_kernel(BwdMtmArgs a) {
+  __shared__ __align__(16) uint16_t pt[kBgTC * kBgPitch];
+  __shared__ __align__(16) uint16_t qt[256 * kBgPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.x * kBgTC;
+  const int64_t split = blockIdx.y;
+  const int64_t m_lo = split * a.m_per_split;
+  const int64_t m_hi = min(a.m, m_lo + a.m_per_split);
+  const int jt = a.qc / 16;
+  const int qunits = kBgTM * a.qc / 8;  // 16-byte units of a Q stage
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0, 0, 0, 0};
+  for (int64_t ms = m_lo; ms < m_hi; ms += kBgTM) {
+    // P stage: token row tid / 8, columns c0 + 8 (tid % 8) .. +8 (c_total % 64 == 0)
+    {
+      const int ml = tid >> 3, cq = tid & 7;
+      const int64_t mr = ms + ml;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (mr < m_hi) v = *(const uint4*)(a.p + mr * a.c_total + c0 + 8 * cq);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      __syncthreads();  // the previous stage has been read
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pt[(8 * cq + e) * kBgPitch + ml] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    for (int u = tid; u < qunits; u += 256) {
+      const int ml = u / (a.qc / 8), jq = u % (a.qc / 8);
+      const int64_t mr = ms + ml;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (mr < m_hi) v = *(const uint4*)(a.q + mr * a.qc + 8 * jq);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qt[(8 * jq + e) * kBgPitch + ml] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    const bf16x8 af = *(const bf16x8*)(pt + (16 * wave + r) * kBgPitch + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= jt) break;
+      const bf16x8 bq = *(const bf16x8*)(qt + (16 * j + r) * kBgPitch + 8 * g);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq, acc[j], 0, 0, 0);
+    }
+  }
+  // lane (r, g) of tile j: c = c0 + 16 wave + 4 g + e, j = 16 j + r
+  float* out = a.part + split * a.c_total * a.qc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= jt) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(c0 + 16 * wave + 4 * g + e) * a.qc + 16 * j + r] = acc[j][e];
+  }
+}
+
+// out[c * stride_c + j * stride_j] = (sum over splits of part[split][c][j]) + (sum over
+// splits of part[split][c][rp + j]), each in split order, for j < rank (hi, then lo columns).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int64_t splits,
+                                                         int64_t c_total, int32_t rp, int32_t rank,
+                                                         float* __restrict__ out, int64_t stride_c,
+                                                         int64_t stride_j) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= c_total * rank) return;
+  const int64_t c = i / rank;
+  const int j = (int)(i - c * rank);
+  float hi = 0.0f, lo = 0.0f;
+  for (int64_t sp = 0; sp < splits; ++sp) {
+    hi += part[(sp * c_total + c) * 2 * rp + j];
+    lo += part[(sp * c_total + c) * 2 * rp + rp + j];
+  }
+  out[c * stride_c + j * stride_j] = hi + lo;
+}
+
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __restrict__ b, int64_t n, int32_t rank,
+                                                            uint16_t* __restrict__ bt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * rank) return;
+  const int64_t row = i / rank;
+  const int j = (int)(i - row * rank);
+  bt[(int64_t)j * n + row] = b[i];
+}
+
+// ------------------------------------------------------------------ host side
+namespace {
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+int32_t rank_pad32(int32_t r) { return (r + 31) / 32 * 32; }
+// Token splits of the adapter-gradient products: about 512 workgroups, at least 256
+// tokens per split.
+int64_t mtm_splits(int64_t m, int64_t c_total) {
+  const int64_t tiles = c_total / kBgTC;
+  int64_t sp = (512 + tiles - 1) / tiles;
+  const int64_t smax = (m + 255) / 256;
+  return sp < 1 ? 1 : (sp > smax ? smax : sp);
+}
+struct BwdWs {
+  uint16_t* bt;      // [rank][n]
+  char* down_t;      // lora_down scratch of x A^T
+  char* down_u;      // lora_down scratch of dY B
+  float* part_b;     // [splits][n][2 rp]
+  float* part_a;     // [splits][k][2 rp]
+  size_t bytes;
+};
+BwdWs bwd_ws(void* scratch, int64_t m, int64_t n, int64_t k, int32_t rank) {
+  BwdWs w{};
+  char* p = (char*)scratch;
+  size_t off = 0;
+  if (rank > 0) {
+    const size_t rp = (size_t)rank_pad32(rank);
+    w.bt = (uint16_t*)(p + off);
+    off += up256((size_t)rank * (size_t)n * 2);
+    w.down_t = p + off;
+    off += up256(lora_down_hilo_bytes(m, k, rank));
+    w.down_u = p + off;
+    off += up256(lora_down_hilo_bytes(m, n, rank));
+    w.part_b = (float*)(p + off);
+    off += up256((size_t)mtm_splits(m, n) * (size_t)n * 2 * rp * 4);
+    w.part_a = (float*)(p + off);
+    off += up256((size_t)mtm_splits(m, k) * (size_t)k * 2 * rp * 4);
+  }
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t backward_scratch_bytes(int64_t m, int64_t n, int64_t k, int32_t rank) {
+  return bwd_ws(nullptr, m, n, k, rank).bytes;
+}
+
+hipError_t launch_backward_nvfp4(const uint16_t* x, const uint16_t* dy, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                 const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank, float lora_scale,
+                                 void* dx, int out_f32, float* da, float* db, void* scratch, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  if (n % kBxTN != 0 || k % kBxTK != 0 || rank < 0 || rank > 128) return hipErrorInvalidValue;
+  const BwdWs w = bwd_ws(scratch, m, n, k, rank);
+  const int32_t rp = rank > 0 ? rank_pad32(rank) : 0;
+  uint16_t* t = nullptr;
+  uint16_t* du = nullptr;
+  if (rank > 0) {
+    bwd_transpose_kernel<<<(unsigned)((n * rank + 255) / 256), 256, 0, s>>>(lora_b, n, rank, w.bt);
+    hipError_t e = launch_lora_down_hilo(dy, m, n, w.bt, rank, lora_scale, w.down_u, &du, s);
+    if (e != hipSuccess) return e;
+    e = launch_lora_down_hilo(x, m, k, lora_a, rank, lora_scale, w.down_t, &t, s);
+    if (e != hipSuccess) return e;
+  }
+  BwdDxArgs a;
+  a.dy = dy;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.codes = codes;
+  a.scales = scales;
+  a.tensor_scale = tensor_scale;
+  a.du = du;
+  a.lora_a = lora_a;
+  a.rank = rank;
+  a.rank_pad = rp;
+  a.dx = dx;
+  a.out_f32 = out_f32;
+  bwd_dx_kernel<<<dim3((unsigned)(k / kBxTK), (unsigned)((m + kBxTM - 1) / kBxTM)), 256, 0, s>>>(a);
+  if (rank > 0) {
+    // dB[n][j] = sum_m dY[m][n] t[m][j];  dA[j][k] = sum_m du[m][j] x[m][k]  (hi and lo columns)
+    const struct { const uint16_t* p; const uint16_t* q; int64_t c; float* part; float* out; int64_t sc, sj; } jobs[2] = {
+        {dy, t, n, w.part_b, db, rank, 1}, {x, du, k, w.part_a, da, 1, k}};
+    for (const auto& jb : jobs) {
+      const int64_t sp = mtm_splits(m, jb.c);
+      BwdMtmArgs g;
+      g.p = jb.p;
+      g.q = jb.q;
+      g.m = m;
+      g.c_total = jb.c;
+      g.m_per_split = ((m + sp - 1) / sp + kBgTM - 1) / kBgTM * kBgTM;
+      g.qc = 2 * rp;
+      g.part = jb.part;
+      const int64_t used = (m + g.m_per_split - 1) / g.m_per_split;
+      bwd_mtm_kernel<<<dim3((unsigned)(jb.c / kBgTC), (unsigned)used), 256, 0, s>>>(g);
+      bwd_reduce_kernel<<<(unsigned)((jb.c * rank + 255) / 256), 256, 0, s>>>(jb.part, used, jb.c, rp, rank, jb.out,
+                                                                            jb.sc, jb.sj);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ql

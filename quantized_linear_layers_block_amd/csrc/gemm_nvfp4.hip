@@ -387,9 +387,8 @@ constexpr int64_t kNvChunk8 = 256;  // 16-byte units per wave
 // bf16(s * sum over the K splits of t_part[split][row][j]) for j < rank, 0 up to rank_pad.
 // Fixed order: eight interleaved partial sums (split sp goes to sum sp % 8), then those
 // eight in order; the loads of one round are independent so they overlap.
-__device__ __forceinline__ uint16_t lora_t_value(const float* __restrict__ t_part, int64_t m, int64_t splits,
-                                                 int32_t rank, int32_t rank_pad, float lora_scale, int64_t row,
-                                                 int j) {
+__device__ __forceinline__ float lora_t_sum(const float* __restrict__ t_part, int64_t m, int64_t splits,
+                                            int32_t rank_pad, int64_t row, int j) {
   float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int64_t sp = 0;
   for (; sp + 8 <= splits; sp += 8) {
@@ -400,7 +399,12 @@ __device__ __forceinline__ uint16_t lora_t_value(const float* __restrict__ t_par
   float sum = acc8[0];
 #pragma unroll
   for (int u = 1; u < 8; ++u) sum += acc8[u];
-  return (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * sum) : 0u);
+  return sum;
+}
+__device__ __forceinline__ uint16_t lora_t_value(const float* __restrict__ t_part, int64_t m, int64_t splits,
+                                                 int32_t rank, int32_t rank_pad, float lora_scale, int64_t row,
+                                                 int j) {
+  return (uint16_t)(j < rank ? f32_to_bf16_rne(lora_scale * lora_t_sum(t_part, m, splits, rank_pad, row, j)) : 0u);
 }
 __global__ __launch_bounds__(256) void nv_finish_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                         int64_t splits, const uint32_t* __restrict__ amax_part,
@@ -460,6 +464,27 @@ __global__ __launch_bounds__(256) void lora_t_finish_kernel(int64_t m, int64_t s
   if (row >= m) return;
   for (int j = threadIdx.x & 63; j < rank_pad; j += 64)
     t[row * rank_pad + j] = lora_t_value(t_part, m, splits, rank, rank_pad, lora_scale, row, j);
+}
+
+// v = s * (fixed-order sum of the partials) as a bf16 pair hi = bf16(v), lo = bf16(v - hi)
+// (v - hi is exact in float32): t_hl[row][j] = hi, t_hl[row][rank_pad + j] = lo, zero
+// past rank.  hi + lo carries about 16 significant bits of v.
+__global__ __launch_bounds__(256) void lora_t_hilo_kernel(int64_t m, int64_t splits,
+                                                          const float* __restrict__ t_part, int32_t rank,
+                                                          int32_t rank_pad, float lora_scale,
+                                                          uint16_t* __restrict__ t_hl) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  for (int j = threadIdx.x & 63; j < rank_pad; j += 64) {
+    uint32_t hi = 0, lo = 0;
+    if (j < rank) {
+      const float v = lora_scale * lora_t_sum(t_part, m, splits, rank_pad, row, j);
+      hi = f32_to_bf16_rne(v);
+      lo = f32_to_bf16_rne(v - __uint_as_float(hi << 16));
+    }
+    t_hl[row * 2 * rank_pad + j] = (uint16_t)hi;
+    t_hl[row * 2 * rank_pad + rank_pad + j] = (uint16_t)lo;
+  }
 }
 
 template <int OUT_F32>
@@ -834,6 +859,25 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint1
   lora_t_finish_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(m, nv_prep_splits(m, k), w.t_part, rank,
                                                                nv_rank_pad(rank), lora_scale, w.t);
   *t_out = w.t;
+  return hipGetLastError();
+}
+
+size_t lora_down_hilo_bytes(int64_t m, int64_t k, int32_t rank) {
+  if (m <= 0 || k <= 0 || rank <= 0) return 0;
+  return lora_down_ws(nullptr, m, k, rank).bytes + up256((size_t)m * (size_t)nv_rank_pad(rank) * 4);
+}
+
+hipError_t launch_lora_down_hilo(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
+                                 int32_t rank, float lora_scale, void* scratch, uint16_t** t_hl_out,
+                                 hipStream_t s) {
+  if (m <= 0 || k <= 0 || k % 16 != 0 || rank <= 0 || rank > 128 || !scratch) return hipErrorInvalidValue;
+  const LoraDownWs w = lora_down_ws(scratch, m, k, rank);
+  uint16_t* t_hl = (uint16_t*)((char*)scratch + w.bytes);
+  hipError_t e = launch_nv_stats(x, m, k, lora_a, rank, w.amax_part, w.t_part, s);
+  if (e != hipSuccess) return e;
+  lora_t_hilo_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(m, nv_prep_splits(m, k), w.t_part, rank,
+                                                             nv_rank_pad(rank), lora_scale, t_hl);
+  *t_hl_out = t_hl;
   return hipGetLastError();
 }
 

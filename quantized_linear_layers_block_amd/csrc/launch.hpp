@@ -56,6 +56,13 @@ hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int he
 hipError_t launch_kv_load(const uint8_t* codes, const float* scales, int64_t cache_slots, const int64_t* slots,
                           int64_t tokens, int heads, int head_dim, uint16_t* out, int32_t* status, hipStream_t s);
 
+// ---- backward of the NVFP4 + LoRA layer (backward.hip); n % 64 == 0, k % 128 == 0
+size_t backward_scratch_bytes(int64_t m, int64_t n, int64_t k, int32_t rank);
+hipError_t launch_backward_nvfp4(const uint16_t* x, const uint16_t* dy, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                 const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank, float lora_scale,
+                                 void* dx, int out_f32, float* da, float* db, void* scratch, hipStream_t s);
+
 // ---- NVFP4 layer for up to 64 tokens (gemv16.hip)
 struct G16Plan {
   int mt;             // m tiles of 16 (1, 2 or 4)
@@ -89,6 +96,13 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
 // t = bf16(s x A^T) as [m][rank_pad] (zero past the rank) in `scratch`; two kernels (split-K
 // partials, then their fixed-order sum), no inter-workgroup counters.  k % 16 == 0.
 size_t lora_down_bytes(int64_t m, int64_t k, int32_t rank);
+// The same product s . x . A^T kept in higher precision: bf16 [m][2 rank_pad], row = the
+// rounded value hi (columns [0, rank_pad)) and the rounded remainder lo (columns [rank_pad,
+// 2 rank_pad)).
+size_t lora_down_hilo_bytes(int64_t m, int64_t k, int32_t rank);
+hipError_t launch_lora_down_hilo(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
+                                 int32_t rank, float lora_scale, void* scratch, uint16_t** t_hl_out,
+                                 hipStream_t s);
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
                             int32_t rank, float lora_scale, void* scratch, uint16_t** t_out,
                             hipStream_t s);

@@ -173,3 +173,31 @@ def test_new_entry_argument_errors():
     assert st(t=0) == b.QL_OK          # nothing to store: nothing launched
     ld = L.qlinear_kv_load_fp8(FAKE, FAKE, 16, FAKE, 4, 8, 100, FAKE, None, None)
     assert ld == b.QL_ERR_SHAPE
+
+
+def test_backward_argument_errors():
+    L = b.LIB
+    qn = b.QWeight(b.QL_NVFP4, 0, 256, 512, FAKE, FAKE, FAKE)
+
+    def bw(q=qn, x=FAKE, dy=FAKE, m=8, a=FAKE, bb=FAKE, r=8, s=2.0, dx=FAKE, dt=b.QL_OUT_BF16, da=FAKE, db=FAKE,
+           ws=FAKE, wsb=1 << 30):
+        return L.qlinear_backward(ctypes.byref(q), x, dy, m, a, bb, r, s, dx, dt, da, db, ws, wsb, None)
+
+    assert bw(q=b.QWeight(b.QL_FP8_BLOCK128, 0, 256, 512, FAKE, FAKE, None)) == b.QL_ERR_FORMAT
+    assert bw(q=b.QWeight(b.QL_NVFP4, 0, 200, 512, FAKE, FAKE, FAKE)) == b.QL_ERR_SHAPE   # n % 64
+    assert bw(q=b.QWeight(b.QL_NVFP4, 0, 256, 528, FAKE, FAKE, FAKE)) == b.QL_ERR_SHAPE   # k % 128
+    assert bw(m=0) == b.QL_ERR_SHAPE
+    assert bw(dy=None) == b.QL_ERR_NULL
+    assert bw(dx=None) == b.QL_ERR_NULL
+    assert bw(x=None) == b.QL_ERR_NULL       # an adapter needs x, da and db
+    assert bw(da=None) == b.QL_ERR_NULL
+    assert bw(r=129) == b.QL_ERR_ARG
+    assert bw(dt=7) == b.QL_ERR_FORMAT
+    assert bw(dx=FAKE + 8) == b.QL_ERR_ALIGN
+    assert bw(ws=None) == b.QL_ERR_WORKSPACE
+    need = b.qlinear_backward_workspace(b.QL_NVFP4, 8, 256, 512, 8)
+    assert need > 0 and bw(wsb=need - 1) == b.QL_ERR_WORKSPACE
+    # no adapter: no workspace, no x / da / db needed
+    assert b.qlinear_backward_workspace(b.QL_NVFP4, 8, 256, 512, 0) == 0
+    assert b.qlinear_backward_workspace(b.QL_FP8_BLOCK128, 8, 256, 512, 0) == 0
+    assert b.qlinear_backward_workspace(b.QL_NVFP4, 8, 200, 512, 8) == 0
