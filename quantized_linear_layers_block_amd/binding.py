@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqlinear.so")
+# QLINEAR_LIB names another build of this same library (the host-sanitizer build of the ABI
+# checks loads that way); by default the in-tree one.
+LIB_PATH = os.environ.get("QLINEAR_LIB") or os.path.join(HERE, "libqlinear.so")
 
 QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_FORMAT, QL_ERR_WORKSPACE, QL_ERR_HIP, QL_ERR_ARG = range(8)
 QL_NVFP4, QL_FP8_BLOCK128, QL_FP8_POW2 = 1, 2, 3

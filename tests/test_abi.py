@@ -1,7 +1,10 @@
 """The C ABI on the host (no GPU needed): the library loads, exports every entry point
 include/qlinear.h declares, and rejects invalid arguments with the documented status
-before touching the device."""
+before touching the device.  The binding is loaded by file path, without the package (and
+so without PyTorch), which lets test_host_sanitizers.py run this file against a build of
+the ABI under the host AddressSanitizer and UndefinedBehaviorSanitizer."""
 import ctypes
+import importlib.util
 import os
 import re
 
@@ -9,7 +12,19 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-b = pytest.importorskip("quantized_linear_layers_block_amd.binding")
+
+def _binding():
+    spec = importlib.util.spec_from_file_location(
+        "qlinear_abi_binding", os.path.join(ROOT, "quantized_linear_layers_block_amd", "binding.py"))
+    mod = importlib.util.module_from_spec(spec)
+    try:
+        spec.loader.exec_module(mod)
+    except (ImportError, OSError) as e:
+        pytest.skip(f"libqlinear is not built: {e}", allow_module_level=True)
+    return mod
+
+
+b = _binding()
 
 
 def _declared():
