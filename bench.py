@@ -60,12 +60,12 @@ COUNTER_CLOCKS = {
     "a5": {"GHz": 1.90, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
            "sources_sha256": "6241ee12eab3d724c7ed304daea81de8201316c8c9737112d2f1a34b19a929b2"},
-    "a6": {"GHz": 1.99, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+    "a6": {"GHz": 2.03, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "007ef314ff16ad4f379c865274458fcaed212bde9d6b79f3c160addf54ba1f38"},
-    "a6p": {"GHz": 2.08, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "3f47381a7e1135f42b6c14cff44b9845edb20d0695fd4571ce0680687c170098"},
+    "a6p": {"GHz": 2.10, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-            "sources_sha256": "007ef314ff16ad4f379c865274458fcaed212bde9d6b79f3c160addf54ba1f38"},
+            "sources_sha256": "3f47381a7e1135f42b6c14cff44b9845edb20d0695fd4571ce0680687c170098"},
 }
 
 

@@ -14,10 +14,10 @@
 // which is the operand-scale format of gfx950's scaled FP8 MFMA: each lane hands the MFMA
 // the scale of the 32 K values it supplies (its weight block's, its token's), the MFMA
 // applies both, and accumulates straight into the float32 accumulator -- no fold, no
-// per-block vector work.
+// per-block vector work (gemm_fp8_pow2_kernel, below, with its own tiling).
 //
-// Tiling: 256 (n) x 256 (m) per workgroup of eight waves (2 along n x 4 along m), 128 x 64
-// per wave (8 x 4 MFMA tiles, 128 float32 accumulators per lane), K step 128.  Operand tiles (32 KB each) are double-buffered in
+// Tiling (float32 scales): 256 (n) x 256 (m) per workgroup of eight waves (2 along n x 4
+// along m), 128 x 64 per wave (8 x 4 MFMA tiles, 128 float32 accumulators per lane), K step 128.  Operand tiles (32 KB each) are double-buffered in
 // LDS (128 KB) with a 16-byte XOR swizzle so that the 16 lanes reading one column of
 // 16 rows hit distinct banks; the next K block is fetched into registers while the
 // current one is multiplied.  Workgroup ids are remapped so that the tiles an XCD
@@ -37,9 +37,9 @@ constexpr size_t kFp8Lds = 8 * kStagePerWave;    // >= the two operand stages (1
 
 struct Fp8GemmArgs {
   const uint8_t* xq;
-  const void* sx;          // float32 [m][k/128], or E8M0 bytes (POW2)
+  const void* sx;          // float32 [m][k/128], or E8M0 bytes (power-of-two scales)
   const uint8_t* wq;
-  const void* sw;          // float32 [n/128][k/128], or E8M0 bytes (POW2)
+  const void* sw;          // float32 [n/128][k/128], or E8M0 bytes (power-of-two scales)
   int64_t m, n, k;
   const uint16_t* t;       // bf16 [m][rank_pad] (lora_scale already applied) or null
   const uint16_t* lora_b;  // bf16 [n][rank]
@@ -56,7 +56,7 @@ __device__ __forceinline__ i32x8 frag_fp8(const uint8_t* tile, int row, int g) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int OUT_F32, bool POW2>
+template <int OUT_F32>
 __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
   constexpr int kStage = 2 * kTile * kRowBytes;
@@ -115,53 +115,6 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  if constexpr (POW2) {
-    // Scale bytes of the next K block are loaded during this one: the wave's weight block
-    // (A operand, the same for every lane) and the lane's four m rows (B operand).
-    const uint8_t* sxb = (const uint8_t*)a.sx + m0 * kblocks;
-    const uint8_t* swb = (const uint8_t*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma(0, 0, q);
-    int sa = swb[0], sb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sb[j] = sxb[osx[j]];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    i32x8 bf[4], af, afn;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = frag_fp8(smem + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
-    af = frag_fp8(smem, 128 * wn + r, g);
-    for (int64_t kb = 0; kb < kblocks; ++kb) {
-      const int buf = (int)(kb & 1);
-      const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;
-      const int san = swb[kn];
-      int sbn[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbn[j] = sxb[osx[j] + kn];
-      const uint8_t* As = smem + buf * kStage;
-      const uint8_t* An = smem + (buf ^ 1) * kStage;
-      // Same schedule as the fold path below, with each MFMA accumulating in place.
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i == 7) {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, sa, 0, sb[j]);
-          if (j == 0) afn = i < 7 ? frag_fp8(As, 128 * wn + 16 * (i + 1) + r, g) : frag_fp8(An, 128 * wn + r, g);
-          if (i < 4 && (j == 1 || j == 2)) dma(kn, buf ^ 1, 2 * i + (j - 1));
-          if (i == 7) bf[j] = frag_fp8(An + kTile * kRowBytes, 64 * wm + 16 * j + r, g);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        af = afn;
-      }
-      sa = san;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = sbn[j];
-    }
-  } else {
   const float* sxbase = (const float*)a.sx + m0 * kblocks;
   const float* swp = (const float*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
   const float swmask = nblk_ok ? 1.0f : 0.0f;
@@ -234,7 +187,6 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
-  }
 
   // Epilogue: lane holds m = m0 + 64 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
   if (a.rank_pad > 0)
@@ -273,6 +225,151 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ power-of-two scales
+// With E8M0 scales the MFMAs accumulate in place, so the accumulators need no vector work
+// until the epilogue and can live in the accumulation registers: four waves per workgroup,
+// each owning 128 (n) x 128 (m) of the 256 x 256 tile (8 x 8 MFMA tiles, 256 accumulators
+// per lane).  Per K block a wave then reads 16 operand fragments from LDS for 64 MFMAs
+// (512 bytes per MFMA) instead of 12 for 32 (768 bytes): the LDS reads, which otherwise
+// take about as long as the MFMAs, drop by a third.  Operand stages, swizzle and copies
+// are those of gemm_fp8_kernel (each wave copies 64 rows of each operand); the copies of
+// the next block go out during fragments 0-3 and the block barrier sits before fragment 7.
+constexpr int kP2Threads = 256;
+constexpr int kP2StagePerWave = 128 * kStagePitch;  // 128 rows of 128 bf16 columns per wave
+constexpr size_t kP2Lds = 4 * kP2StagePerWave;      // >= the two operand stages (128 KB)
+
+template <int OUT_F32>
+__global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
+  constexpr int kStage = 2 * kTile * kRowBytes;
+
+  int64_t tm, tn;
+  gemm_tile_coords(a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t n0 = tn * kTile, m0 = tm * kTile;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wn = wave & 1, wm = wave >> 1;  // wave tile: n 128 wn .. +128, m 128 wm .. +128
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t kblocks = a.k / 128;
+
+  // Copy q (0..15) of a K block: q < 8 weight rows 64 wave + 8 q + lane / 8, q >= 8 the same
+  // activation rows; lane l fills 16-byte slot l % 8 with logical chunk swz(row, l % 8).
+  uint32_t oa[8], ob[8];
+  const int64_t n_last = a.n - 1 - n0, m_last = a.m - 1 - m0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const uint32_t lc = (uint32_t)swz(row, lane & 7);
+    oa[i] = (uint32_t)(row < n_last ? row : n_last) * (uint32_t)a.k + lc * 16;
+    ob[i] = (uint32_t)(row < m_last ? row : m_last) * (uint32_t)a.k + lc * 16;
+  }
+  const uint8_t* wbase = a.wq + n0 * a.k;
+  const uint8_t* xbase = a.xq + m0 * a.k;
+  auto dma = [&](int64_t kb, int buf, int q) {
+    const uint32_t lb = lds_addr(smem + buf * kStage) + 64 * wave * kRowBytes;
+    if (q < 8)
+      lds_copy16(wbase + kb * 128, oa[q], lb + 8 * q * kRowBytes);
+    else
+      lds_copy16(xbase + kb * 128, ob[q - 8], lb + (kTile + 8 * (q - 8)) * kRowBytes);
+  };
+  // E8M0 scale bytes of the next block, loaded during this one: the wave's 128-row weight
+  // block (the A operand's, the same for every lane) and the lane's eight m rows.
+  uint32_t osx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = 128 * wm + 16 * j + r;
+    osx[j] = (uint32_t)((row < m_last ? row : m_last) * kblocks);
+  }
+  const int64_t nblk = (n0 + 128 * wn) / 128;
+  const bool nblk_ok = nblk * 128 < a.n;
+  const uint8_t* sxb = (const uint8_t*)a.sx + m0 * kblocks;
+  const uint8_t* swb = (const uint8_t*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+#pragma unroll
+  for (int q = 0; q < 16; ++q) dma(0, 0, q);
+  int sa = swb[0], sb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sb[j] = sxb[osx[j]];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  i32x8 bf[8], af, afn;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bf[j] = frag_fp8(smem + kTile * kRowBytes, 128 * wm + 16 * j + r, g);
+  af = frag_fp8(smem, 128 * wn + r, g);
+  for (int64_t kb = 0; kb < kblocks; ++kb) {
+    const int buf = (int)(kb & 1);
+    const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;  // the last block re-copies itself into the idle buffer
+    const int san = swb[kn];
+    int sbn[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sbn[j] = sxb[osx[j] + kn];
+    const uint8_t* As = smem + buf * kStage;
+    const uint8_t* An = smem + (buf ^ 1) * kStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i == 7) {
+        // this block's LDS reads are done and the next block's copies have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, sa, 0, sb[j]);
+        if (j == 0) afn = i < 7 ? frag_fp8(As, 128 * wn + 16 * (i + 1) + r, g) : frag_fp8(An, 128 * wn + r, g);
+        if (i < 4 && (j & 1)) dma(kn, buf ^ 1, 4 * i + (j >> 1));
+        if (i == 7) bf[j] = frag_fp8(An + kTile * kRowBytes, 128 * wm + 16 * j + r, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      af = afn;
+    }
+    sa = san;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sb[j] = sbn[j];
+  }
+
+  // Epilogue: lane holds m = m0 + 128 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
+  if (a.rank_pad > 0)
+    lora_wave<8, 8>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, n0 + 128 * wn, m0 + 128 * wm, r, g, acc);
+  if (!OUT_F32 && m0 + kTile <= a.m && n0 + kTile <= a.n && (a.n & 7) == 0) {
+    // Interior bf16 tile: the wave's 128 (m) x 128 (n) block goes through LDS (272-byte
+    // rows) and leaves as whole 256-byte rows, four rows per store instruction.
+    __syncthreads();  // every wave is done with the operand buffers
+    uint8_t* stage = smem + wave * kP2StagePerWave;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = acc[i][j];
+        *(uint2*)(stage + (16 * j + r) * kStagePitch + (16 * i + 4 * g) * 2) =
+            make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    uint16_t* ybase = (uint16_t*)a.y + (m0 + 128 * wm) * a.n + n0 + 128 * wn + (lane & 15) * 8;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int row = 4 * q + (lane >> 4);
+      *(i32x4*)(ybase + row * a.n) = *(const i32x4*)(stage + row * kStagePitch + (lane & 15) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t mrow = m0 + 128 * wm + 16 * j + r;
+        if (mrow < a.m) store4(a.y, OUT_F32, a.n, mrow, n0 + 128 * wn + 16 * i + 4 * g, acc[i][j], a.n);
+      }
+    }
+  }
+}
+
 hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t n, int64_t k,
                            const uint8_t* wq, const void* sw, bool pow2, const uint16_t* t,
                            const uint16_t* lora_b, int32_t rank, void* y, int out_f32,
@@ -298,19 +395,27 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t
   const size_t lds = kFp8Lds;
   static_assert(kFp8Lds >= 4 * kTile * kRowBytes, "staging must cover the operand buffers");
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-#define QL_FP8_LAUNCH(OF, P2)                                                                             \
+#define QL_FP8_LAUNCH(OF)                                                                                 \
   {                                                                                                       \
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<OF, P2>,                               \
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<OF>,                                   \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);             \
     if (e != hipSuccess) return e;                                                                        \
-    gemm_fp8_kernel<OF, P2><<<grid, kGThreads, lds, s>>>(a);                                               \
+    gemm_fp8_kernel<OF><<<grid, kGThreads, lds, s>>>(a);                                                   \
+  }
+#define QL_FP8_P2_LAUNCH(OF)                                                                              \
+  {                                                                                                       \
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_pow2_kernel<OF>,                             \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kP2Lds);          \
+    if (e != hipSuccess) return e;                                                                        \
+    gemm_fp8_pow2_kernel<OF><<<grid, kP2Threads, kP2Lds, s>>>(a);                                          \
   }
   if (out_f32) {
-    if (pow2) QL_FP8_LAUNCH(1, true) else QL_FP8_LAUNCH(1, false)
+    if (pow2) QL_FP8_P2_LAUNCH(1) else QL_FP8_LAUNCH(1)
   } else {
-    if (pow2) QL_FP8_LAUNCH(0, true) else QL_FP8_LAUNCH(0, false)
+    if (pow2) QL_FP8_P2_LAUNCH(0) else QL_FP8_LAUNCH(0)
   }
 #undef QL_FP8_LAUNCH
+#undef QL_FP8_P2_LAUNCH
   return hipGetLastError();
 }
 
