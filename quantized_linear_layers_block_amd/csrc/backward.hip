@@ -21,11 +21,12 @@
 //   (128 tokens x 64) is the B operand.  Workgroup tile 128 (K) x 128 (M), four waves of
 //   64 x 64, stages of 64 along N with the next stage's loads in flight during the MFMAs.
 //   S is applied in float32, then bf16(du) . A is added as r_pad / 32 more MFMA steps.
-// * bwd_mtm_kernel: G[c][j] = sum over a range of tokens of P[m][c] Q[m][j] (P = dY, Q = the
-//   hi | lo columns of t for dB; P = x, Q = those of du for dA): both operands are
-//   transposed into LDS (token-major rows) and multiplied with bf16 MFMAs into float32;
-//   the token range is split over workgroups and bwd_reduce_kernel adds, in a fixed order,
-//   the split partials of the hi columns, those of the lo columns, and the two sums.
+// * bwd_nt_kernel: G[c][j] = sum over a range of tokens of P[m][c] Q[m][j] (P = dY, Q = the
+//   hi | lo columns of t for dB; P = x, Q = those of du for dA), from token-major copies of
+//   both operands (bwd_transpose2d_kernel), each MFMA fragment one 16-byte load; bf16
+//   MFMAs into float32, the token range split over workgroups, and bwd_reduce_kernel adds,
+//   in a fixed order, the split partials of the hi columns, those of the lo columns, and
+//   the two sums.
 // * bwd_transpose_kernel: B [N, r] -> B^T [r, N] for the down-projection of dY.
 #include "../../include/qlinear.h"
 #include "common.hpp"
@@ -198,80 +199,114 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDxArgs a) {
 }
 
 // ------------------------------------------------------------------ adapter gradients
-// Workgroup: 64 columns c of P and all qc (<= 256, a multiple of 32) columns j of Q over
-// the token range [m_lo, m_hi) of its split, in stages of 32 tokens.  LDS: P^T [64][32 + 8]
-// and Q^T [qc][32 + 8] (bf16, rows padded to 80 bytes: a fragment read of 16 rows at one
-// offset touches 16 different bank groups).  Wave w: c tile w (16 columns) x all j tiles.
-constexpr int kBgTC = 64, kBgTM = 32, kBgPitch = kBgTM + 8;
+// The token reductions G[c][j] = sum_m P[m][c] Q[m][j] (dB: P = dY, Q = t; dA: P = x,
+// Q = du, each Q as its hi | lo columns) have the reduction index in the rows of both
+// operands.  Both are transposed once into the workspace (token-major rows, the token count
+// padded to a multiple of 32 and Q's column count to a multiple of 128, with zeros), after
+// which every MFMA fragment is one 16-byte load straight from memory: no LDS, no barriers.
+constexpr int kTr = 64;
 
-struct BwdMtmArgs {
-  const uint16_t* p;  // [m][c_total]
-  const uint16_t* q;  // [m][qc]
-  int64_t m, c_total, m_per_split;
-  int32_t qc;
-  float* part;        // [split][c_total][qc]
+// dst[c][r] = src[r][c] for r < rows, c < cols; zero for rows <= r < rows_pad or
+// cols <= c < cols_pad.  64 x 64 tiles through LDS; cols and src_ld multiples of 8.
+__global__ __launch_bounds__(256) void bwd_transpose2d_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                              int64_t cols, int64_t src_ld, int64_t rows_pad,
+                                                              int64_t cols_pad, uint16_t* __restrict__ dst) {
+  __shared__ uint32_t tile[kTr][kTr / 2 + 1];  // row r: elements 2 i, 2 i + 1 in word i
+  const int64_t c0 = (int64_t)blockIdx.x * kTr, r0 = (int64_t)blockIdx.y * kTr;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = tid + 256 * j;
+    const int rl = u >> 3, cq = u & 7;
+    const int64_t rr = r0 + rl, cc = c0 + 8 * cq;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < rows && cc < cols) v = *(const uint4*)(src + rr * src_ld + cc);
+    tile[rl][4 * cq] = v.x;
+    tile[rl][4 * cq + 1] = v.y;
+    tile[rl][4 * cq + 2] = v.z;
+    tile[rl][4 * cq + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = tid + 256 * j;
+    const int cl = u >> 3, rq = u & 7;
+    const int64_t cc = c0 + cl, rr = r0 + 8 * rq;
+    if (cc >= cols_pad || rr >= rows_pad) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (tile[8 * rq + 2 * e][cl >> 1] >> (16 * (cl & 1))) & 0xFFFFu;
+      const uint32_t hi = (tile[8 * rq + 2 * e + 1][cl >> 1] >> (16 * (cl & 1))) & 0xFFFFu;
+      w[e] = lo | (hi << 16);
+    }
+    *(uint4*)(dst + cc * rows_pad + rr) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+struct BwdNtArgs {
+  const uint16_t* pt;  // [c_total][ld]: P^T, token-major rows
+  const uint16_t* qt;  // [qcp][ld]: Q^T
+  int64_t c_total, ld, m_per_split;
+  int32_t qcp;         // a multiple of 128
+  float* part;         // [split][c_total][qcp]
 };
 
-__global__ __launch_bounds__(256) void bwd_mtm_kernel(BwdMtmArgs a) {
-  __shared__ __align__(16) uint16_t pt[kBgTC * kBgPitch];
-  __shared__ __align__(16) uint16_t qt[256 * kBgPitch];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+// Wave w of workgroup (x, split): columns c = 256 x + 64 w .. +64 (four 16-row tiles) by
+// 128 columns j at a time, over the split's tokens in steps of 32, the next step's
+// fragments loaded while the current one is multiplied.  c_total % 64 == 0.
+__global__ __launch_bounds__(256) void bwd_nt_kernel(BwdNtArgs a) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int64_t c0 = (int64_t)blockIdx.x * kBgTC;
+  const int64_t cw = (int64_t)blockIdx.x * 256 + 64 * wave;
+  if (cw >= a.c_total) return;
   const int64_t split = blockIdx.y;
   const int64_t m_lo = split * a.m_per_split;
-  const int64_t m_hi = min(a.m, m_lo + a.m_per_split);
-  const int jt = a.qc / 16;
-  const int qunits = kBgTM * a.qc / 8;  // 16-byte units of a Q stage
-
-  f32x4 acc[16];
+  const int64_t m_hi = min(a.ld, m_lo + a.m_per_split);
+  float* out = a.part + split * a.c_total * a.qcp;
+  for (int jh = 0; jh < a.qcp; jh += 128) {
+    f32x4 acc[4][8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0, 0, 0, 0};
-  for (int64_t ms = m_lo; ms < m_hi; ms += kBgTM) {
-    // P stage: token row tid / 8, columns c0 + 8 (tid % 8) .. +8 (c_total % 64 == 0)
-    {
-      const int ml = tid >> 3, cq = tid & 7;
-      const int64_t mr = ms + ml;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (mr < m_hi) v = *(const uint4*)(a.p + mr * a.c_total + c0 + 8 * cq);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      __syncthreads();  // the previous stage has been read
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pt[(8 * cq + e) * kBgPitch + ml] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    const uint16_t* pb = a.pt + (cw + r) * a.ld + 8 * g;
+    const uint16_t* qb = a.qt + (jh + r) * a.ld + 8 * g;
+    bf16x8 af[4], bq[8], an[4], bn[8];
+    auto fetch = [&](int64_t m, bf16x8 (&fa)[4], bf16x8 (&fb)[8]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pb + 16 * i * a.ld + m);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(qb + 16 * j * a.ld + m);
+    };
+    if (m_lo < m_hi) fetch(m_lo, af, bq);
+    for (int64_t m = m_lo; m < m_hi; m += 32) {
+      const int64_t mn = m + 32 < m_hi ? m + 32 : m;  // the last step re-reads itself
+      fetch(mn, an, bn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bq[j] = bn[j];
     }
-    for (int u = tid; u < qunits; u += 256) {
-      const int ml = u / (a.qc / 8), jq = u % (a.qc / 8);
-      const int64_t mr = ms + ml;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (mr < m_hi) v = *(const uint4*)(a.q + mr * a.qc + 8 * jq);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // lane (r, g) of tile (i, j): c = cw + 16 i + 4 g + e, column jh + 16 j + r
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qt[(8 * jq + e) * kBgPitch + ml] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
-    const bf16x8 af = *(const bf16x8*)(pt + (16 * wave + r) * kBgPitch + 8 * g);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j >= jt) break;
-      const bf16x8 bq = *(const bf16x8*)(qt + (16 * j + r) * kBgPitch + 8 * g);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq, acc[j], 0, 0, 0);
-    }
-  }
-  // lane (r, g) of tile j: c = c0 + 16 wave + 4 g + e, j = 16 j + r
-  float* out = a.part + split * a.c_total * a.qc;
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j >= jt) break;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[(c0 + 16 * wave + 4 * g + e) * a.qc + 16 * j + r] = acc[j][e];
+        for (int e = 0; e < 4; ++e) out[(cw + 16 * i + 4 * g + e) * a.qcp + jh + 16 * j + r] = acc[i][j][e];
   }
 }
 
 // out[c * stride_c + j * stride_j] = (sum over splits of part[split][c][j]) + (sum over
-// splits of part[split][c][rp + j]), each in split order, for j < rank (hi, then lo columns).
+// splits of part[split][c][rp + j]), each in split order, for j < rank (hi, then lo
+// columns; partial rows of qcp floats).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int64_t splits,
-                                                         int64_t c_total, int32_t rp, int32_t rank,
+                                                         int64_t c_total, int32_t qcp, int32_t rp, int32_t rank,
                                                          float* __restrict__ out, int64_t stride_c,
                                                          int64_t stride_j) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -280,8 +315,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
   const int j = (int)(i - c * rank);
   float hi = 0.0f, lo = 0.0f;
   for (int64_t sp = 0; sp < splits; ++sp) {
-    hi += part[(sp * c_total + c) * 2 * rp + j];
-    lo += part[(sp * c_total + c) * 2 * rp + rp + j];
+    hi += part[(sp * c_total + c) * qcp + j];
+    lo += part[(sp * c_total + c) * qcp + rp + j];
   }
   out[c * stride_c + j * stride_j] = hi + lo;
 }
@@ -299,41 +334,58 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __re
 namespace {
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int32_t rank_pad32(int32_t r) { return (r + 31) / 32 * 32; }
-// Token splits of the adapter-gradient products: about 512 workgroups, at least 256
-// tokens per split.
-int64_t mtm_splits(int64_t m, int64_t c_total) {
-  const int64_t tiles = c_total / kBgTC;
-  int64_t sp = (512 + tiles - 1) / tiles;
+int64_t ld32(int64_t m) { return (m + 31) / 32 * 32; }
+int32_t qc_pad(int32_t rank) { return (2 * rank_pad32(rank) + 127) / 128 * 128; }
+// Token splits of the adapter-gradient products: about 512 waves' worth of workgroups, at
+// least 256 tokens per split, at most 16 splits.
+int64_t nt_splits(int64_t m, int64_t c_total) {
+  const int64_t wgs = (c_total + 255) / 256;
+  int64_t sp = (512 + wgs - 1) / wgs;
   const int64_t smax = (m + 255) / 256;
-  return sp < 1 ? 1 : (sp > smax ? smax : sp);
+  if (sp > smax) sp = smax;
+  if (sp > 16) sp = 16;
+  return sp < 1 ? 1 : sp;
 }
 struct BwdWs {
   uint16_t* bt;      // [rank][n]
-  char* down_t;      // lora_down scratch of x A^T
-  char* down_u;      // lora_down scratch of dY B
-  float* part_b;     // [splits][n][2 rp]
-  float* part_a;     // [splits][k][2 rp]
+  char* down_t;      // lora_down scratch of x A^T (hi | lo)
+  char* down_u;      // lora_down scratch of dY B (hi | lo)
+  uint16_t* dyt;     // [n][ld]
+  uint16_t* xt;      // [k][ld]
+  uint16_t* tt;      // [qcp][ld]
+  uint16_t* ut;      // [qcp][ld]
+  float* part_b;     // [splits][n][qcp]
+  float* part_a;     // [splits][k][qcp]
   size_t bytes;
 };
 BwdWs bwd_ws(void* scratch, int64_t m, int64_t n, int64_t k, int32_t rank) {
   BwdWs w{};
   char* p = (char*)scratch;
   size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p + off;
+    off += up256(bytes);
+    return q;
+  };
   if (rank > 0) {
-    const size_t rp = (size_t)rank_pad32(rank);
-    w.bt = (uint16_t*)(p + off);
-    off += up256((size_t)rank * (size_t)n * 2);
-    w.down_t = p + off;
-    off += up256(lora_down_hilo_bytes(m, k, rank));
-    w.down_u = p + off;
-    off += up256(lora_down_hilo_bytes(m, n, rank));
-    w.part_b = (float*)(p + off);
-    off += up256((size_t)mtm_splits(m, n) * (size_t)n * 2 * rp * 4);
-    w.part_a = (float*)(p + off);
-    off += up256((size_t)mtm_splits(m, k) * (size_t)k * 2 * rp * 4);
+    const size_t ld = (size_t)ld32(m), qcp = (size_t)qc_pad(rank);
+    w.bt = (uint16_t*)take((size_t)rank * (size_t)n * 2);
+    w.down_t = take(lora_down_hilo_bytes(m, k, rank));
+    w.down_u = take(lora_down_hilo_bytes(m, n, rank));
+    w.dyt = (uint16_t*)take((size_t)n * ld * 2);
+    w.xt = (uint16_t*)take((size_t)k * ld * 2);
+    w.tt = (uint16_t*)take(qcp * ld * 2);
+    w.ut = (uint16_t*)take(qcp * ld * 2);
+    w.part_b = (float*)take((size_t)nt_splits(m, n) * (size_t)n * qcp * 4);
+    w.part_a = (float*)take((size_t)nt_splits(m, k) * (size_t)k * qcp * 4);
   }
   w.bytes = off;
   return w;
+}
+void transpose2d(const uint16_t* src, int64_t rows, int64_t cols, int64_t src_ld, int64_t rows_pad,
+                 int64_t cols_pad, uint16_t* dst, hipStream_t s) {
+  bwd_transpose2d_kernel<<<dim3((unsigned)((cols_pad + kTr - 1) / kTr), (unsigned)((rows_pad + kTr - 1) / kTr)), 256, 0,
+                           s>>>(src, rows, cols, src_ld, rows_pad, cols_pad, dst);
 }
 }  // namespace
 
@@ -375,22 +427,28 @@ hipError_t launch_backward_nvfp4(const uint16_t* x, const uint16_t* dy, int64_t 
   bwd_dx_kernel<<<dim3((unsigned)(k / kBxTK), (unsigned)((m + kBxTM - 1) / kBxTM)), 256, 0, s>>>(a);
   if (rank > 0) {
     // dB[n][j] = sum_m dY[m][n] t[m][j];  dA[j][k] = sum_m du[m][j] x[m][k]  (hi and lo columns)
-    const struct { const uint16_t* p; const uint16_t* q; int64_t c; float* part; float* out; int64_t sc, sj; } jobs[2] = {
-        {dy, t, n, w.part_b, db, rank, 1}, {x, du, k, w.part_a, da, 1, k}};
+    const int64_t ld = ld32(m);
+    const int32_t qcp = qc_pad(rank);
+    transpose2d(dy, m, n, n, ld, n, w.dyt, s);
+    transpose2d(x, m, k, k, ld, k, w.xt, s);
+    transpose2d(t, m, 2 * rp, 2 * rp, ld, qcp, w.tt, s);
+    transpose2d(du, m, 2 * rp, 2 * rp, ld, qcp, w.ut, s);
+    const struct { const uint16_t* pt; const uint16_t* qt; int64_t c; float* part; float* out; int64_t sc, sj; } jobs[2] = {
+        {w.dyt, w.tt, n, w.part_b, db, rank, 1}, {w.xt, w.ut, k, w.part_a, da, 1, k}};
     for (const auto& jb : jobs) {
-      const int64_t sp = mtm_splits(m, jb.c);
-      BwdMtmArgs g;
-      g.p = jb.p;
-      g.q = jb.q;
-      g.m = m;
+      const int64_t sp = nt_splits(m, jb.c);
+      BwdNtArgs g;
+      g.pt = jb.pt;
+      g.qt = jb.qt;
       g.c_total = jb.c;
-      g.m_per_split = ((m + sp - 1) / sp + kBgTM - 1) / kBgTM * kBgTM;
-      g.qc = 2 * rp;
+      g.ld = ld;
+      g.m_per_split = ((ld + sp - 1) / sp + 31) / 32 * 32;
+      g.qcp = qcp;
       g.part = jb.part;
-      const int64_t used = (m + g.m_per_split - 1) / g.m_per_split;
-      bwd_mtm_kernel<<<dim3((unsigned)(jb.c / kBgTC), (unsigned)used), 256, 0, s>>>(g);
-      bwd_reduce_kernel<<<(unsigned)((jb.c * rank + 255) / 256), 256, 0, s>>>(jb.part, used, jb.c, rp, rank, jb.out,
-                                                                            jb.sc, jb.sj);
+      const int64_t used = (ld + g.m_per_split - 1) / g.m_per_split;
+      bwd_nt_kernel<<<dim3((unsigned)((jb.c + 255) / 256), (unsigned)used), 256, 0, s>>>(g);
+      bwd_reduce_kernel<<<(unsigned)((jb.c * rank + 255) / 256), 256, 0, s>>>(jb.part, used, jb.c, qcp, rp, rank,
+                                                                            jb.out, jb.sc, jb.sj);
     }
   }
   return hipGetLastError();
