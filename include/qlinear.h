@@ -256,8 +256,9 @@ size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32
  * bf16 pair) and du enters dx rounded to bf16, as the forward rounds t.  w must be QL_NVFP4 with n % 64 == 0 and k % 128 == 0.  Without
  * an adapter (rank 0, a NULL lora pointer or lora_scale 0) only dx is computed and x, da,
  * db may be NULL.  Workspace: qlinear_backward_workspace(format, m, n, k, rank) bytes of
- * scratch (0 without an adapter: ws may then be NULL); no zeroing or reserved region is
- * needed and it may be reused by any call once this one has finished on its stream.
+ * scratch (about 2 m n bytes for an f16 copy of dy, plus the adapter's intermediates); no
+ * zeroing or reserved region is needed and it may be reused by any call once this one has
+ * finished on its stream.
  * All pointers 16-byte aligned; the caller owns every buffer.  Errors: QL_ERR_NULL,
  * QL_ERR_SHAPE (m <= 0, m > QLINEAR_MAX_M, n % 64, k % 128, sizes beyond
  * QLINEAR_MAX_ELEMS), QL_ERR_FORMAT (not NVFP4, or dx_dtype), QL_ERR_ARG (rank < 0 or >

@@ -346,10 +346,16 @@ int64_t nt_splits(int64_t m, int64_t c_total) {
   if (sp > 16) sp = 16;
   return sp < 1 ? 1 : sp;
 }
+// dX takes the transposed f16 product (gemm_nvfp4.hip) unless n or k exceed its 32-bit copy
+// offsets; then bwd_dx_kernel.
+bool dx_f16_path(int64_t n, int64_t k) { return n < kNvF16MaxK && k < kNvDxMaxK; }
 struct BwdWs {
   uint16_t* bt;      // [rank][n]
+  char* rows;        // f16 path: dY as f16 rows, du (hi | lo)
+  uint16_t* at;      // f16 path: A^T [k][rank_pad]
+  float* dx_part;    // f16 path: split-tile partials of dX
+  char* down_u;      // other path: lora_down scratch of dY B (hi | lo)
   char* down_t;      // lora_down scratch of x A^T (hi | lo)
-  char* down_u;      // lora_down scratch of dY B (hi | lo)
   uint16_t* dyt;     // [n][ld]
   uint16_t* xt;      // [k][ld]
   uint16_t* tt;      // [qcp][ld]
@@ -367,11 +373,18 @@ BwdWs bwd_ws(void* scratch, int64_t m, int64_t n, int64_t k, int32_t rank) {
     off += up256(bytes);
     return q;
   };
+  const bool f16 = dx_f16_path(n, k);
+  if (rank > 0) w.bt = (uint16_t*)take((size_t)rank * (size_t)n * 2);
+  if (f16) {
+    w.rows = take(f16_rows_bytes(m, n, rank));
+    if (rank > 0) w.at = (uint16_t*)take((size_t)k * (size_t)rank_pad32(rank) * 2);
+    w.dx_part = (float*)take(nvfp4_dx_part_bytes(m, n, k));
+  } else if (rank > 0) {
+    w.down_u = take(lora_down_hilo_bytes(m, n, rank));
+  }
   if (rank > 0) {
     const size_t ld = (size_t)ld32(m), qcp = (size_t)qc_pad(rank);
-    w.bt = (uint16_t*)take((size_t)rank * (size_t)n * 2);
     w.down_t = take(lora_down_hilo_bytes(m, k, rank));
-    w.down_u = take(lora_down_hilo_bytes(m, n, rank));
     w.dyt = (uint16_t*)take((size_t)n * ld * 2);
     w.xt = (uint16_t*)take((size_t)k * ld * 2);
     w.tt = (uint16_t*)take(qcp * ld * 2);
@@ -403,28 +416,42 @@ hipError_t launch_backward_nvfp4(const uint16_t* x, const uint16_t* dy, int64_t 
   const int32_t rp = rank > 0 ? rank_pad32(rank) : 0;
   uint16_t* t = nullptr;
   uint16_t* du = nullptr;
-  if (rank > 0) {
-    bwd_transpose_kernel<<<(unsigned)((n * rank + 255) / 256), 256, 0, s>>>(lora_b, n, rank, w.bt);
-    hipError_t e = launch_lora_down_hilo(dy, m, n, w.bt, rank, lora_scale, w.down_u, &du, s);
+  hipError_t e = hipSuccess;
+  if (rank > 0) bwd_transpose_kernel<<<(unsigned)((n * rank + 255) / 256), 256, 0, s>>>(lora_b, n, rank, w.bt);
+  if (dx_f16_path(n, k)) {
+    uint16_t* dy16 = nullptr;
+    float* rs = nullptr;
+    e = launch_f16_rows(dy, m, n, w.bt, rank, lora_scale, w.rows, &dy16, &rs, &du, s);
     if (e != hipSuccess) return e;
+    if (rank > 0) transpose2d(lora_a, rank, k, k, rp, k, w.at, s);
+    e = launch_nvfp4_dx(dy16, rs, m, n, k, codes, scales, tensor_scale, w.at, du, rp, 2 * rp, dx, out_f32, w.dx_part,
+                        s);
+    if (e != hipSuccess) return e;
+  } else {
+    if (rank > 0) {
+      e = launch_lora_down_hilo(dy, m, n, w.bt, rank, lora_scale, w.down_u, &du, s);
+      if (e != hipSuccess) return e;
+    }
+    BwdDxArgs a;
+    a.dy = dy;
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    a.codes = codes;
+    a.scales = scales;
+    a.tensor_scale = tensor_scale;
+    a.du = du;
+    a.lora_a = lora_a;
+    a.rank = rank;
+    a.rank_pad = rp;
+    a.dx = dx;
+    a.out_f32 = out_f32;
+    bwd_dx_kernel<<<dim3((unsigned)(k / kBxTK), (unsigned)((m + kBxTM - 1) / kBxTM)), 256, 0, s>>>(a);
+  }
+  if (rank > 0) {
     e = launch_lora_down_hilo(x, m, k, lora_a, rank, lora_scale, w.down_t, &t, s);
     if (e != hipSuccess) return e;
   }
-  BwdDxArgs a;
-  a.dy = dy;
-  a.m = m;
-  a.n = n;
-  a.k = k;
-  a.codes = codes;
-  a.scales = scales;
-  a.tensor_scale = tensor_scale;
-  a.du = du;
-  a.lora_a = lora_a;
-  a.rank = rank;
-  a.rank_pad = rp;
-  a.dx = dx;
-  a.out_f32 = out_f32;
-  bwd_dx_kernel<<<dim3((unsigned)(k / kBxTK), (unsigned)((m + kBxTM - 1) / kBxTM)), 256, 0, s>>>(a);
   if (rank > 0) {
     // dB[n][j] = sum_m dY[m][n] t[m][j];  dA[j][k] = sum_m du[m][j] x[m][k]  (hi and lo columns)
     const int64_t ld = ld32(m);

@@ -95,16 +95,17 @@ __device__ __forceinline__ void store4(void* y, int out_f32, int64_t n_total, in
 // LoRA up-projection for a wave's NI x NJ grid of 16 (n) x 16 (m) output tiles:
 //   acc[i][j][n][m] += sum_q B[n][q] t[m][q],  n = nbase + 16 i + ..., m = mbase + 16 j + ...
 // with B = lora_b [n][rank] (MFMA A operand, rows clamped to n_lim) and t [m][rank_pad]
-// (B operand, zero padded to rank_pad, rows clamped to m_lim); lane (r, g) supplies
-// ranks q0 + 8 g .. + 7 of row r.  Per 32-rank chunk every fragment is loaded once and
+// (B operand, zero padded to rank_pad, rows of t_stride elements -- rank_pad when 0 --
+// clamped to m_lim); lane (r, g) supplies ranks q0 + 8 g .. + 7 of row r.  Per 32-rank chunk every fragment is loaded once and
 // all NI x NJ MFMAs follow.  With rank % 8 == 0 a lane's 8 ranks are one aligned
 // 16-byte load (lora_b is 16-byte aligned) and are either all in range or all out.
 template <int NI, int NJ>
 __device__ __forceinline__ void lora_wave(const uint16_t* __restrict__ lora_b, const uint16_t* __restrict__ t,
                                           int32_t rank, int32_t rank_pad, int64_t n_lim, int64_t m_lim,
                                           int64_t nbase, int64_t mbase, int r, int g,
-                                          f32x4 (&acc)[NI][NJ]) {
+                                          f32x4 (&acc)[NI][NJ], int64_t t_stride = 0) {
   const bool vec = (rank & 7) == 0;
+  const int64_t ts = t_stride > 0 ? t_stride : rank_pad;
   for (int q0 = 0; q0 < rank_pad; q0 += 32) {
     const int q = q0 + 8 * g;
     i32x4 af[NI], bfr[NJ];
@@ -130,7 +131,7 @@ __device__ __forceinline__ void lora_wave(const uint16_t* __restrict__ lora_b, c
     for (int j = 0; j < NJ; ++j) {
       const int64_t mr0 = mbase + 16 * j + r;
       const int64_t mr = mr0 < m_lim ? mr0 : m_lim - 1;
-      bfr[j] = *(const i32x4*)(t + mr * rank_pad + q);
+      bfr[j] = *(const i32x4*)(t + mr * ts + q);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)

@@ -721,6 +721,257 @@ __global__ __launch_bounds__(256) void nv_tail_reduce_kernel(const float* __rest
   if (tn * kQTile + col < n) store4(y, out_f32, n, mr, tn * kQTile + col, v, n);
 }
 
+// ------------------------------------------------------------ transposed product (backward)
+//
+//   dX[m][k] = S rs[m] sum_n dY16[m][n] E2M1(c[n][k]) E4M3(e[n][k/16])  +  sum_q du[m][q] A[q][k]
+//
+// The gradient of the activations reduces over the weight rows n, so the weights enter
+// transposed: an MFMA A fragment needs 8 consecutive n at one k, across 8 rows of the
+// packed codes.  Each stage's codes and scales (64 rows of n x 256 columns of k) are copied
+// into LDS, dequantized to f16 exactly as in the forward (dequant8_f16) and written back to
+// LDS in their own row-major layout, 16 bytes per write; the fragments are then read with
+// gfx950's transposing LDS read ds_read_b64_tr_b16.  Within each 16-lane group that read
+// takes 4 consecutive 16-bit elements from the address of every lane and hands element c
+// of lane 4 e + b to lane 4 b + c, as element e (lane layout checked on the device); so
+// lanes 4 e + b naming k 4 b .. 4 b + 3 of W row n0 + e leave lane j holding W[n0 .. n0 + 3]
+// at column j.  dY, the B operand, comes as f16 rows scaled by powers of two (rs, the
+// forward's activation pre-pass, exact but for values below about 2^-29 of the row
+// maximum) and is copied into LDS exactly like the forward's activations.  S rs[m] is
+// applied in float32 after the n loop; du . A (bf16(du), A^T zero-padded to rank_pad) is
+// one more bf16 MFMA chunk per 32 ranks.
+//
+// Tiling: 256 (k) x 256 (m) per workgroup of eight waves (4 along k x 2 along m), 64 x 128
+// per wave, stages of 64 n.  LDS: dY two stages (copies one stage ahead), dequantized W
+// two stages (the next stage's is written while this one's is multiplied), codes and
+// scales three stages (copies two stages ahead).  Tiles and the split tail are those of
+// the forward (nv_tile_plan over (m, k) with stages along n, nv_tail_reduce_kernel).
+constexpr int kDThreads = 512;
+constexpr int kDN = 64;                         // n per stage
+constexpr int kDXBytes = kQTile * 128;          // dY16: 256 rows (m) x 64 f16
+constexpr int kDWBytes = kDN * 512;             // W: 64 rows (n) x 256 f16 (k)
+constexpr int kDCBytes = kDN * 128;             // codes: 64 rows x 128 bytes
+constexpr int kDCSBytes = kDCBytes + kDN * 16;  // + scales: 64 rows x 16 bytes
+constexpr int kDXSlots = 2, kDCSlots = 3;
+constexpr int kDWOff = kDXSlots * kDXBytes;
+constexpr int kDCOff = kDWOff + 2 * kDWBytes;
+constexpr size_t kDLds = (size_t)kDCOff + kDCSlots * kDCSBytes;
+static_assert(kDLds >= 8 * kQStagePerWave, "the output staging fits in the operand buffers");
+
+// 16-byte slot of logical slot s (k 8 s .. 8 s + 7) in W row n (32 slots of 512 bytes).
+// A transposing fragment read (fixed s pair, 2 lanes per slot) covers rows 16 g + 8 h + 4 q
+// + (0..3): over a half wave the slots' bits 1..3 take (n & 3) | (bit 4 of n) << 2, eight
+// distinct values.  A dequantized write (16 lanes: rows 2 p, 2 p + 1 x units u = 0..7 at
+// slot 4 u + v) differs in bit 0 between u < 4 and u >= 4 (from slot bit 4) and in bit 1
+// between the two rows.  So both touch 16 distinct bank groups per 256 bytes.
+__device__ __forceinline__ int wslot(int n, int s) { return s ^ ((s >> 4) & 1) ^ (2 * ((n & 3) | ((n >> 2) & 4))); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct Nvfp4DxArgs {
+  const uint16_t* dy16;  // f16 [m][n], row r scaled by 1 / rs[r]
+  const float* rs;       // [m] row factors (powers of two)
+  int64_t m, n, k;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  const uint16_t* at;    // A^T [k][rank_pad] bf16, zero past the rank
+  const uint16_t* du;    // [m][du_stride] bf16: bf16(du) in columns [0, rank_pad), zero past the rank
+  int32_t rank_pad;      // 0: no adapter
+  int64_t du_stride;
+  void* dx;
+  int64_t tiles_m, tiles_n;
+  int64_t full_tiles;
+  int32_t tail_split;
+  float* part;           // [split workgroup][256 m][256 k] float32 partial tiles
+};
+
+template <int OUT_F32>
+__global__ __launch_bounds__(kDThreads) void gemm_nvfp4_dx_kernel(Nvfp4DxArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const GemmWork work = gemm_schedule(a.tiles_m, a.tiles_n, a.full_tiles, a.tail_split);
+  const int64_t k0 = work.tn * kQTile, m0 = work.tm * kQTile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int wk = wave & 3, wm = wave >> 2;  // wave tile: k 64 wk .. +64, m 128 wm .. +128
+  const int r = lane & 15, g = lane >> 4;
+  // n stages [st0, st1) of this workgroup (all of n for a whole tile)
+  const int64_t nst_all = a.n / kDN;
+  const int64_t per = (nst_all + work.nsplit - 1) / work.nsplit;
+  const int64_t st0 = work.split * per;
+  const int64_t st1 = st0 + per < nst_all ? st0 + per : nst_all;
+  const int64_t m_last = a.m - 1 - m0;
+  const int64_t k_room = a.k - k0;  // at least 128 (k % 128 == 0)
+
+  // Copies of one stage, per wave: 4 x dY16 (8 rows of 128 bytes each, swizzled 16-byte
+  // slots; rows past the edge copy the last row), 1 x codes (rows 8 wave .. +8 of the stage,
+  // 16 bytes = 32 k per lane), 1 x scales (rows 16 (wave % 4) .. +16, 4 bytes = 64 k per
+  // lane; waves 4..7 repeat the copies of 0..3, so that every wave issues the same number
+  // of copies).  Columns past k re-read the last full unit; their outputs are never stored.
+  uint32_t xo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * (wave + 8 * q) + (lane >> 3);
+    xo[q] = (uint32_t)((row < m_last ? row : m_last) * a.n * 2 + swz(row, lane & 7) * 16);
+  }
+  uint32_t co, so;
+  {
+    const int64_t kc = 32 * (lane & 7) < k_room - 32 ? 32 * (lane & 7) : k_room - 32;
+    co = (uint32_t)((8 * wave + (lane >> 3)) * (a.k / 2) + kc / 2);
+    const int64_t ks = 64 * (lane & 3) < k_room - 64 ? 64 * (lane & 3) : k_room - 64;
+    so = (uint32_t)((16 * (wave & 3) + (lane >> 2)) * (a.k / 16) + ks / 16);
+  }
+  const uint8_t* xb = (const uint8_t*)(a.dy16 + m0 * a.n);
+  const uint8_t* cb = a.codes + k0 / 2;
+  const uint8_t* sb = a.scales + k0 / 16;
+  auto dma_x = [&](int64_t st, int slot) {
+    const uint32_t lb = lds_addr(smem) + slot * kDXBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_copy16(xb + st * (kDN * 2), xo[q], lb + 8 * (wave + 8 * q) * 128);
+  };
+  auto dma_c = [&](int64_t st, int slot) {
+    const uint32_t lb = lds_addr(smem) + kDCOff + slot * kDCSBytes;
+    lds_copy16(cb + st * kDN * (a.k / 2), co, lb + wave * 1024);
+    lds_copy4(sb + st * kDN * (a.k / 16), so, lb + kDCBytes + (wave & 3) * 256);
+  };
+  auto clamp_st = [&](int64_t st) { return st < st1 ? st : st1 - 1; };
+
+  // Dequantization: thread (wave, lane) takes W row 8 wave + lane / 8 of the stage, k 32 u
+  // .. +32 (u = lane % 8): the 16 code bytes its own lane copied and the two block scales.
+  const int wr = 8 * wave + (lane >> 3), wu = lane & 7;
+  auto dequant = [&](int cslot, int wbuf) {
+    const uint8_t* cs = smem + kDCOff + cslot * kDCSBytes;
+    const uint4 c = *(const uint4*)(cs + wr * 128 + 16 * wu);
+    const uint32_t sc = *(const uint16_t*)(cs + kDCBytes + wr * 16 + 2 * wu);
+    uint8_t* row = smem + kDWOff + wbuf * kDWBytes + wr * 512;
+    *(f16x8*)(row + wslot(wr, 4 * wu + 0) * 16) = dequant8_f16(c.x, sc & 0xFFu);
+    *(f16x8*)(row + wslot(wr, 4 * wu + 1) * 16) = dequant8_f16(c.y, sc & 0xFFu);
+    *(f16x8*)(row + wslot(wr, 4 * wu + 2) * 16) = dequant8_f16(c.z, sc >> 8);
+    *(f16x8*)(row + wslot(wr, 4 * wu + 3) * 16) = dequant8_f16(c.w, sc >> 8);
+  };
+  // Fragments of MFMA step h (n 16 g + 8 h .. +8 for lane group g, on both operands):
+  // A (tile i: k 64 wk + 16 i + r) from two transposing reads of W rows 16 g + 8 h + 4 q +
+  // r / 4 at k 64 wk + 16 i + 4 (r % 4); B (tile j: m 128 wm + 16 j + r) as in the forward.
+  const int tre = r >> 2, trb = r & 3;
+  auto read_a = [&](int wbuf, int h, int i) {
+    const uint8_t* wb = smem + kDWOff + wbuf * kDWBytes;
+    const int s = 8 * wk + 2 * i + (trb >> 1);
+    i16x4 p[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int n = 16 * g + 8 * h + 4 * q + tre;
+      p[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(wb + n * 512 + wslot(n, s) * 16 + (trb & 1) * 8));
+    }
+    return __builtin_bit_cast(f16x8, __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto read_b = [&](int xslot, int h, int j) {
+    const int row = 128 * wm + 16 * j + r;
+    return *(const f16x8*)(smem + xslot * kDXBytes + row * 128 + swz(row, 2 * g + h) * 16);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  // Stage s (relative to st0) uses dY slot s % 2, W buffer s % 2 and, for the next stage's
+  // dequantization, code slot (s + 1) % 3.  Issue order: codes 0, 1, dY 0, codes 2; then
+  // (after W 0 is written) dY 1, codes 3; and after the barrier closing stage s, dY s + 2
+  // and codes s + 4.  At the end of stage s, vmcnt(2) leaves only codes s + 3 in flight:
+  // dY s + 1 and codes s + 2 have landed.
+  if (st1 > st0) {
+    dma_c(st0, 0);
+    dma_c(clamp_st(st0 + 1), 1);
+    dma_x(st0, 0);
+    dma_c(clamp_st(st0 + 2), 2);
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    __syncthreads();
+    dequant(0, 0);
+    __syncthreads();  // W 0 complete; code slot 0 free
+    dma_x(clamp_st(st0 + 1), 1);
+    dma_c(clamp_st(st0 + 3), 0);
+  }
+  for (int64_t st = st0; st < st1; ++st) {
+    const int ls = (int)(st - st0);
+    const int cur = ls & 1;
+    const int cn = (ls + 1) % kDCSlots;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f16x8 af[4], bq[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = read_a(cur, h, i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bq[j] = read_b(cur, h, j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bq[j], acc[i][j], 0, 0, 0);
+      if (h == 0) dequant(cn, cur ^ 1);  // stage st + 1 (unused after the last stage)
+    }
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    __syncthreads();
+    dma_x(clamp_st(st + 2), cur);
+    dma_c(clamp_st(st + 4), cn);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: lane holds k = k0 + 64 wk + 16 i + 4 g + (0..3), m = m0 + 128 wm + 16 j + r.
+  const float S = *a.tensor_scale;
+  float fac[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t mr = m0 + 128 * wm + 16 * j + r;
+    fac[j] = S * a.rs[mr < a.m ? mr : a.m - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] *= fac[j];
+  if (a.rank_pad > 0 && work.split == 0)
+    lora_wave<4, 8>(a.at, a.du, a.rank_pad, a.rank_pad, a.k, a.m, k0 + 64 * wk, m0 + 128 * wm, r, g, acc,
+                    a.du_stride);
+  if (work.slot >= 0) {
+    float* pt = a.part + work.slot * (kQTile * kQTile);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *(f32x4*)(pt + (128 * wm + 16 * j + r) * kQTile + 64 * wk + 16 * i + 4 * g) = acc[i][j];
+    return;
+  }
+  if (!OUT_F32 && m0 + kQTile <= a.m && k0 + kQTile <= a.k) {
+    // Interior bf16 tile, staged through LDS as in the forward: whole 128-byte rows out.
+    __syncthreads();
+    uint8_t* stage = smem + wave * kQStagePerWave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = acc[i][j];
+        *(uint2*)(stage + (16 * j + r) * kQPitch + (16 * i + 4 * g) * 2) =
+            make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+    }
+    uint16_t* ybase = (uint16_t*)a.dx + (m0 + 128 * wm) * a.k + k0 + 64 * wk + (lane & 7) * 8;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      *(i32x4*)(ybase + row * a.k) = *(const i32x4*)(stage + row * kQPitch + (lane & 7) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t mrow = m0 + 128 * wm + 16 * j + r;
+        const int64_t kk = k0 + 64 * wk + 16 * i + 4 * g;
+        if (mrow < a.m && kk < a.k) store4(a.dx, OUT_F32, a.k, mrow, kk, acc[i][j], a.k);
+      }
+    }
+  }
+}
+
 namespace {
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int32_t nv_rank_pad(int32_t rank) { return rank > 0 ? (rank + 31) / 32 * 32 : 0; }
@@ -975,6 +1226,109 @@ hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     if (e != hipSuccess) return e;
     gemm_nvfp4_generic_kernel<0><<<grid, kNThreads, lds, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+// ---- f16 rows with the adapter's down-projection as hi | lo pairs (backward pre-pass)
+namespace {
+struct F16RowsWs {
+  uint16_t* x16;
+  float* rs;
+  uint16_t* t_hl;
+  uint32_t* amax_part;
+  float* t_part;
+  size_t bytes;
+};
+F16RowsWs f16_rows_ws(void* scratch, int64_t m, int64_t k, int32_t rank) {
+  const int64_t sp = nv_prep_splits(m, k);
+  const size_t rp = (size_t)nv_rank_pad(rank);
+  char* p = (char*)scratch;
+  F16RowsWs w;
+  size_t off = 0;
+  w.x16 = (uint16_t*)(p + off);
+  off += up256((size_t)m * (size_t)k * 2);
+  w.rs = (float*)(p + off);
+  off += up256((size_t)m * 4);
+  w.t_hl = (uint16_t*)(p + off);
+  off += up256((size_t)m * rp * 4);
+  w.amax_part = (uint32_t*)(p + off);
+  off += up256((size_t)sp * (size_t)m * 4);
+  w.t_part = (float*)(p + off);
+  off += up256((size_t)sp * (size_t)m * rp * 4);
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t f16_rows_bytes(int64_t m, int64_t k, int32_t rank) { return f16_rows_ws(nullptr, m, k, rank).bytes; }
+
+hipError_t launch_f16_rows(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int32_t rank,
+                           float lora_scale, void* scratch, uint16_t** x16, float** rs, uint16_t** t_hl,
+                           hipStream_t s) {
+  if (m <= 0 || k % kQK != 0 || k >= kNvF16MaxK || rank < 0 || rank > 128 || !scratch) return hipErrorInvalidValue;
+  const F16RowsWs w = f16_rows_ws(scratch, m, k, rank);
+  const int64_t sp = nv_prep_splits(m, k);
+  hipError_t e = launch_nv_stats(x, m, k, rank > 0 ? lora_a : nullptr, rank, w.amax_part, w.t_part, s);
+  if (e != hipSuccess) return e;
+  if (rank > 0)
+    lora_t_hilo_kernel<<<(unsigned)((m + 3) / 4), 256, 0, s>>>(m, sp, w.t_part, rank, nv_rank_pad(rank), lora_scale,
+                                                               w.t_hl);
+  const int64_t fin_units = m * ((k / 8 + kNvChunk8 - 1) / kNvChunk8);
+  nv_finish_kernel<<<(unsigned)((fin_units + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, 0, 0, 0.0f,
+                                                                    w.x16, w.rs, nullptr);
+  *x16 = w.x16;
+  *rs = w.rs;
+  *t_hl = rank > 0 ? w.t_hl : nullptr;
+  return hipGetLastError();
+}
+
+// ---- dX = S rs dY16 W (+ bf16(du) A) of the backward
+size_t nvfp4_dx_part_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0) return 0;
+  const NvTilePlan tp = nv_tile_plan(m, k, n);
+  return tp.split > 1 ? (size_t)tp.tail() * (size_t)tp.split * kQTile * kQTile * 4 : 0;
+}
+
+hipError_t launch_nvfp4_dx(const uint16_t* dy16, const float* rs, int64_t m, int64_t n, int64_t k,
+                           const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                           const uint16_t* at, const uint16_t* du, int32_t rank_pad, int64_t du_stride, void* dx,
+                           int out_f32, float* part, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  if (n % kDN != 0 || n >= kNvF16MaxK || k % 128 != 0 || k >= kNvDxMaxK || rank_pad < 0 || rank_pad % 32 != 0)
+    return hipErrorInvalidValue;
+  Nvfp4DxArgs a;
+  a.dy16 = dy16;
+  a.rs = rs;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.codes = codes;
+  a.scales = scales;
+  a.tensor_scale = tensor_scale;
+  a.at = at;
+  a.du = du;
+  a.rank_pad = rank_pad;
+  a.du_stride = du_stride;
+  a.dx = dx;
+  const NvTilePlan tp = nv_tile_plan(m, k, n);
+  a.tiles_m = tp.tiles_m;
+  a.tiles_n = tp.tiles_n;
+  a.full_tiles = tp.full;
+  a.tail_split = tp.split;
+  a.part = part;
+  const unsigned grid = (unsigned)(tp.full + (tp.split > 1 ? tp.tail() * tp.split : 0));
+  if (out_f32) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_dx_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDLds);
+    if (e != hipSuccess) return e;
+    gemm_nvfp4_dx_kernel<1><<<grid, kDThreads, kDLds, s>>>(a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_nvfp4_dx_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDLds);
+    if (e != hipSuccess) return e;
+    gemm_nvfp4_dx_kernel<0><<<grid, kDThreads, kDLds, s>>>(a);
+  }
+  if (tp.split > 1)
+    nv_tail_reduce_kernel<<<(unsigned)(tp.tail() * 64), 256, 0, s>>>(part, tp.tiles_m, tp.tiles_n, tp.full, tp.split,
+                                                                    m, k, dx, out_f32);
   return hipGetLastError();
 }
 

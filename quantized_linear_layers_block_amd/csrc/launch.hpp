@@ -122,6 +122,23 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
                                  const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
                                  int out_f32, void* scratch, hipStream_t s);
 size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
+// x as f16 rows scaled by powers of two (x16 [m][k], rs [m]: x[r] = rs[r] x16[r], exact but
+// for values below about 2^-29 of the row maximum) and, with rank > 0, t = s x A^T as hi | lo
+// bf16 pairs [m][2 rank_pad] (null without).  k % 64 == 0, k < kNvF16MaxK.
+size_t f16_rows_bytes(int64_t m, int64_t k, int32_t rank);
+hipError_t launch_f16_rows(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int32_t rank,
+                           float lora_scale, void* scratch, uint16_t** x16, float** rs, uint16_t** t_hl,
+                           hipStream_t s);
+// Backward dX [m][k] = S rs[m] (dY16 W)[m][k] + (du A)[m][k] over the n weight rows, with
+// A^T [k][rank_pad] and du [m][du_stride] (first rank_pad columns) zero past the rank
+// (rank_pad 0: no adapter).  n % 64 == 0, n < kNvF16MaxK, k % 128 == 0, k < kNvDxMaxK (copy
+// offsets within a stage are 32-bit); part: nvfp4_dx_part_bytes of split-tile partials.
+constexpr int64_t kNvDxMaxK = int64_t(1) << 27;
+size_t nvfp4_dx_part_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_nvfp4_dx(const uint16_t* dy16, const float* rs, int64_t m, int64_t n, int64_t k,
+                           const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                           const uint16_t* at, const uint16_t* du, int32_t rank_pad, int64_t du_stride, void* dx,
+                           int out_f32, float* part, hipStream_t s);
 // k % 128 == 0 and k < kFp8MaxK (copy offsets within a 256-row tile are 32-bit).
 constexpr int64_t kFp8MaxK = int64_t(1) << 24;
 // pow2: sx, sw are E8M0 bytes applied by the scaled MFMA; else float32, folded per K block.

@@ -212,7 +212,9 @@ def test_backward_argument_errors():
     assert bw(ws=None) == b.QL_ERR_WORKSPACE
     need = b.qlinear_backward_workspace(b.QL_NVFP4, 8, 256, 512, 8)
     assert need > 0 and bw(wsb=need - 1) == b.QL_ERR_WORKSPACE
-    # no adapter: no workspace, no x / da / db needed
-    assert b.qlinear_backward_workspace(b.QL_NVFP4, 8, 256, 512, 0) == 0
+    # no adapter: still a workspace (dY as f16 rows), but no x / da / db
+    need0 = b.qlinear_backward_workspace(b.QL_NVFP4, 8, 256, 512, 0)
+    assert 0 < need0 < need
+    assert bw(x=None, a=None, bb=None, r=0, da=None, db=None, ws=None) == b.QL_ERR_WORKSPACE
     assert b.qlinear_backward_workspace(b.QL_FP8_BLOCK128, 8, 256, 512, 0) == 0
     assert b.qlinear_backward_workspace(b.QL_NVFP4, 8, 200, 512, 8) == 0

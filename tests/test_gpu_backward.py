@@ -4,10 +4,13 @@
 Gates: dX, dA and dB each within max |got - ref| / max |ref| <= 2e-3 (float32 outputs);
 bf16 dX equals the RNE rounding of the float32 dX; repeated calls are bitwise identical.
 Cases: ragged token counts around the 128-token tile (1, 5, 130, 257), ranks 8..64 and 12
-(not a multiple of 8), no adapter, and the config-3 weight (K 5120 -> N 27648, W ~N(0, 0.015)
-with outlier channels) at M 256 on samples the oracle computes exactly: 8 random tokens x
-256 random-block K columns of dX, all tokens for 256 K columns of dA, and 128 random rows
-of dB.
+(not a multiple of 8), no adapter, K with a half tile (128, 384), a tile plan whose last n
+split is empty (M 2048, N 320 = 5 stages over 4 splits, K 2048), and the config-3 weight
+(K 5120 -> N 27648, W ~N(0, 0.015) with outlier channels) at M 256 on samples the oracle
+computes exactly: 8 random tokens x 256 random-block K columns of dX, all tokens for 256 K
+columns of dA, and 128 random rows of dB.  A weight 2^22 rows wide (beyond the f16 dX
+path's copy offsets, so dX takes the generic kernel) uses random codes and scales, checked
+on one 16-column block of dX and dA and 256 random rows of dB.
 """
 import numpy as np
 import pytest
@@ -40,7 +43,8 @@ def _case(m, n, k, r, seed):
 
 
 @pytest.mark.parametrize("m,n,k,r", [(1, 64, 128, 8), (5, 128, 256, 16), (130, 192, 384, 32),
-                                     (257, 256, 512, 64), (64, 512, 1024, 0), (33, 128, 256, 12)])
+                                     (257, 256, 512, 64), (64, 512, 1024, 0), (33, 128, 256, 12),
+                                     (2048, 320, 2048, 16)])
 def test_backward_small(m, n, k, r):
     print(f"backward m={m} n={n} k={k} r={r}", flush=True)
     s = 2.0 if r else 0.0
@@ -93,4 +97,30 @@ def test_backward_config3_weight_sampled():
     rows = np.sort(g.choice(n, size=128, replace=False))
     codes_r, scales_r = onv.quantize_rows(np.ascontiguousarray(w[rows]), S)
     _, _, rdb = obw.backward_nvfp4(dy[:, rows], x, codes_r, scales_r, S, a, b[rows], s)
+    assert ogemm.rel_err_inf(db.cpu().numpy()[rows], rdb) <= TOL
+
+
+def test_backward_wide_n_generic_dx():
+    m, n, k, r, s = 3, 1 << 22, 128, 8, 2.0
+    print(f"backward wide n m={m} n={n} k={k} r={r}", flush=True)
+    g = np.random.default_rng(4242)
+    codes = g.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = g.integers(0x20, 0x48, size=(n, k // 16), dtype=np.uint8)   # E4M3 2^-4 .. 3.5
+    S = np.float32(0.003)
+    x = synth.normal_bf16((m, k), 1.0, g)
+    dy = synth.normal_bf16((m, n), 1.0, g)
+    a = synth.normal_bf16((r, k), 0.02, g)
+    b = synth.normal_bf16((n, r), 0.02, g)
+    q = ql.NVFP4Weight(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                       torch.tensor([S], dtype=torch.float32, device=DEV), n, k)
+    dx, da, db = ql.backward(q, _to_dev(dy), _to_dev(x), _to_dev(a), _to_dev(b), s, dx_dtype=torch.float32)
+    torch.cuda.synchronize()
+    blk = int(g.integers(0, k // 16))
+    ks = slice(16 * blk, 16 * blk + 16)
+    rdx, rda, _ = obw.backward_nvfp4(dy, x[:, ks], codes[:, 8 * blk:8 * blk + 8], scales[:, blk:blk + 1], S,
+                                     a[:, ks], b, s)
+    assert ogemm.rel_err_inf(dx.cpu().numpy()[:, ks], rdx) <= TOL
+    assert ogemm.rel_err_inf(da.cpu().numpy()[:, ks], rda) <= TOL
+    rows = np.sort(g.choice(n, size=256, replace=False))
+    _, _, rdb = obw.backward_nvfp4(dy[:, rows], x, codes[rows], scales[rows], S, a, b[rows], s)
     assert ogemm.rel_err_inf(db.cpu().numpy()[rows], rdb) <= TOL
