@@ -11,22 +11,26 @@
 // float32, each carried as a pair of bf16 values hi = bf16(v), lo = bf16(v - hi) (about 16
 // significant bits).  The adapter gradients use both (their sums over tokens keep the
 // precision the pages ask for); dX, an activation gradient like the forward's output, uses
-// du rounded to bf16 as the forward uses t.  Three kernels are new here:
+// du rounded to bf16 as the forward uses t.
 //
-// * bwd_dx_kernel: the transposed NVFP4 product.  The forward reduces over K, along the
-//   rows of the packed codes; here the reduction runs over N, across rows, so each stage's
-//   code tile (64 rows of N x 128 columns of K) is dequantized in registers -- E2M1 by the
-//   hardware converter, times the E4M3 block scale, an exact bf16 -- and written to LDS
-//   transposed (K-major), where it is the A operand of 16x16x32 bf16 MFMAs; the dY tile
-//   (128 tokens x 64) is the B operand.  Workgroup tile 128 (K) x 128 (M), four waves of
-//   64 x 64, stages of 64 along N with the next stage's loads in flight during the MFMAs.
-//   S is applied in float32, then bf16(du) . A is added as r_pad / 32 more MFMA steps.
-// * bwd_nt_kernel: G[c][j] = sum over a range of tokens of P[m][c] Q[m][j] (P = dY, Q = the
-//   hi | lo columns of t for dB; P = x, Q = those of du for dA), from token-major copies of
-//   both operands (bwd_transpose2d_kernel), each MFMA fragment one 16-byte load; bf16
-//   MFMAs into float32, the token range split over workgroups, and bwd_reduce_kernel adds,
-//   in a fixed order, the split partials of the hi columns, those of the lo columns, and
-//   the two sums.
+// dX normally takes the transposed f16 product of gemm_nvfp4.hip (dY as row-scaled f16,
+// the weights dequantized into LDS and read with the transposing LDS read), its pre-pass
+// also forming du.  Kernels here:
+//
+// * bwd_dx_kernel: the generic transposed product, for weights too wide for that path's
+//   32-bit copy offsets.  Each stage's code tile (64 rows of N x 128 columns of K) is
+//   dequantized in registers -- E2M1 by the hardware converter, times the E4M3 block
+//   scale, an exact bf16 -- and written to LDS transposed (K-major), where it is the A
+//   operand of 16x16x32 bf16 MFMAs; the dY tile (128 tokens x 64) is the B operand.
+//   Workgroup tile 128 (K) x 128 (M), four waves of 64 x 64, stages of 64 along N with the
+//   next stage's loads in flight during the MFMAs.  S is applied in float32, then
+//   bf16(du) . A is added as r_pad / 32 more MFMA steps.
+// * bwd_tn_kernel: G[c][j] = sum over a range of tokens of P[m][c] Q[m][j] (P = dY, Q = the
+//   hi | lo columns of t for dB; P = x, Q = those of du for dA): P's token-major tiles are
+//   copied into LDS and read as MFMA fragments with the transposing LDS read, Q^T (small)
+//   is transposed once (bwd_transpose2d_kernel); bf16 MFMAs into float32, the token range
+//   split over workgroups, and bwd_reduce_kernel adds, in a fixed order, the split
+//   partials of the hi columns, those of the lo columns, and the two sums.
 // * bwd_transpose_kernel: B [N, r] -> B^T [r, N] for the down-projection of dY.
 #include "../../include/qlinear.h"
 #include "common.hpp"
@@ -201,9 +205,12 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDxArgs a) {
 // ------------------------------------------------------------------ adapter gradients
 // The token reductions G[c][j] = sum_m P[m][c] Q[m][j] (dB: P = dY, Q = t; dA: P = x,
 // Q = du, each Q as its hi | lo columns) have the reduction index in the rows of both
-// operands.  Both are transposed once into the workspace (token-major rows, the token count
-// padded to a multiple of 32 and Q's column count to a multiple of 128, with zeros), after
-// which every MFMA fragment is one 16-byte load straight from memory: no LDS, no barriers.
+// operands.  P, large, is read in its own token-major layout: each stage's tile (32 tokens
+// x 256 columns) is copied into LDS and the MFMA A fragments (16 columns x 8 tokens per
+// lane group) are taken with the transposing LDS read, as in the dX product.  Q, small,
+// is transposed once into the workspace (bwd_transpose2d_kernel: Q^T [qcp][ld], the token
+// count padded to ld, a multiple of 32, with zeros) and its stage tile copied into LDS
+// beside P's; the B fragments are then plain 16-byte LDS reads.
 constexpr int kTr = 64;
 
 // dst[c][r] = src[r][c] for r < rows, c < cols; zero for rows <= r < rows_pad or
@@ -244,61 +251,135 @@ __global__ __launch_bounds__(256) void bwd_transpose2d_kernel(const uint16_t* __
   }
 }
 
-struct BwdNtArgs {
-  const uint16_t* pt;  // [c_total][ld]: P^T, token-major rows
-  const uint16_t* qt;  // [qcp][ld]: Q^T
-  int64_t c_total, ld, m_per_split;
-  int32_t qcp;         // a multiple of 128
+constexpr int kTnM = 32;                               // tokens per stage
+constexpr int kTnC = 256;                              // columns c per workgroup (4 waves x 64)
+constexpr int kTnJ = 64;                               // columns j per workgroup
+constexpr int kTnPBytes = kTnM * kTnC * 2;             // P: 32 rows (tokens) of 512 bytes
+constexpr int kTnQBytes = kTnJ * kTnM * 2;             // Q^T: 64 rows (j) of 64 bytes
+constexpr int kTnStage = kTnPBytes + kTnQBytes;
+constexpr int kTnSlots = 4;                            // copies run three stages ahead
+constexpr size_t kTnLds = (size_t)kTnSlots * kTnStage;
+
+// 16-byte slot of logical slot s (c 8 s .. 8 s + 7) in token row m of a P tile (32 slots): a
+// fragment read takes one slot pair of rows 8 g + 4 q + (0..3); over a half wave (g = 0, 1)
+// the slots' bits 1..3 take (m & 3) | (bit 3 of m) << 2, eight distinct values.
+__device__ __forceinline__ int tn_pslot(int m, int s) { return s ^ (2 * ((m & 3) | ((m >> 1) & 4))); }
+// 16-byte slot of logical slot s (tokens 8 s .. 8 s + 7) in row j of a Q^T tile (4 slots):
+// the 16 lanes of a B fragment read take rows 16 jt + (0..15), slot g.
+__device__ __forceinline__ int tn_qslot(int j, int s) { return s ^ ((j >> 2) & 3); }
+
+
+struct BwdTnArgs {
+  const uint16_t* p;   // [m][p_ld] bf16
+  int64_t p_ld;
+  const uint16_t* qt;  // [qcp][ld] bf16: Q^T, zero past m
+  int64_t m, ld, c_total, m_per_split;
+  int32_t qcp;         // a multiple of 64
   float* part;         // [split][c_total][qcp]
 };
 
-// Wave w of workgroup (x, split): columns c = 256 x + 64 w .. +64 (four 16-row tiles) by
-// 128 columns j at a time, over the split's tokens in steps of 32, the next step's
-// fragments loaded while the current one is multiplied.  c_total % 64 == 0.
-__global__ __launch_bounds__(256) void bwd_nt_kernel(BwdNtArgs a) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+// Workgroup (x, y, split): columns c = 256 x .. +256 (wave w: 64 w .. +64, four 16-column
+// tiles), j = 64 y .. +64 (four tiles), the split's tokens in stages of 32.  Token rows past
+// m copy row m - 1 and are zeroed in the fragments; columns past c_total copy the last
+// in-range unit and their outputs are not stored.
+__global__ __launch_bounds__(256) void bwd_tn_kernel(BwdTnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int r = lane & 15, g = lane >> 4;
-  const int64_t cw = (int64_t)blockIdx.x * 256 + 64 * wave;
-  if (cw >= a.c_total) return;
-  const int64_t split = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * kTnC, jb = (int64_t)blockIdx.y * kTnJ, split = blockIdx.z;
   const int64_t m_lo = split * a.m_per_split;
-  const int64_t m_hi = min(a.ld, m_lo + a.m_per_split);
-  float* out = a.part + split * a.c_total * a.qcp;
-  for (int jh = 0; jh < a.qcp; jh += 128) {
-    f32x4 acc[4][8];
+  const int64_t m_hi = a.ld < m_lo + a.m_per_split ? a.ld : m_lo + a.m_per_split;
+  const int64_t nst = m_hi > m_lo ? (m_hi - m_lo) / kTnM : 0;
+  // Copies of one stage, per wave: 4 x P (token rows 8 wave + 2 v + lane / 32, 16 bytes at
+  // physical slot lane % 32) and 1 x Q^T (rows 16 wave + lane / 4, physical slot lane % 4).
+  int prow[4];
+  const uint16_t* pcol[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int v = 0; v < 4; ++v) {
+    prow[v] = 8 * wave + 2 * v + (lane >> 5);
+    const int64_t c = c0 + 8 * tn_pslot(prow[v], lane & 31);
+    pcol[v] = a.p + (c < a.c_total ? c : a.c_total - 8);
+  }
+  const int qrow = 16 * wave + (lane >> 2);
+  const uint16_t* qsrc = a.qt + (jb + qrow) * a.ld + 8 * tn_qslot(qrow, lane & 3);
+  auto dma = [&](int64_t st, int slot) {
+    const int64_t mb = m_lo + st * kTnM;
+    const uint32_t lb = lds_addr(smem) + slot * kTnStage;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
-    const uint16_t* pb = a.pt + (cw + r) * a.ld + 8 * g;
-    const uint16_t* qb = a.qt + (jh + r) * a.ld + 8 * g;
-    bf16x8 af[4], bq[8], an[4], bn[8];
-    auto fetch = [&](int64_t m, bf16x8 (&fa)[4], bf16x8 (&fb)[8]) {
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mr = mb + prow[v] < a.m ? mb + prow[v] : a.m - 1;
+      lds_copy16_va(pcol[v] + mr * a.p_ld, lb + 1024 * (4 * wave + v));
+    }
+    lds_copy16_va(qsrc + mb, lb + kTnPBytes + 1024 * wave);
+  };
+  auto clamp_st = [&](int64_t st) { return st < nst ? st : nst - 1; };
+
+  f32x4 acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pb + 16 * i * a.ld + m);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(qb + 16 * j * a.ld + m);
-    };
-    if (m_lo < m_hi) fetch(m_lo, af, bq);
-    for (int64_t m = m_lo; m < m_hi; m += 32) {
-      const int64_t mn = m + 32 < m_hi ? m + 32 : m;  // the last step re-reads itself
-      fetch(mn, an, bn);
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+  if (nst > 0) {
+    dma(0, 0);
+    dma(clamp_st(1), 1);
+    dma(clamp_st(2), 2);
+  }
+  const int tre = r >> 2, trb = r & 3;
+  for (int64_t st = 0; st < nst; ++st) {
+    const int slot = (int)(st & 3);
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // stage st has landed; st + 1, st + 2 in flight
+    __syncthreads();  // ... for every wave, and every wave is done with stage st - 1's slot
+    dma(clamp_st(st + 3), (int)((st + 3) & 3));
+    const uint8_t* pb = smem + slot * kTnStage;
+    const uint8_t* qb = pb + kTnPBytes;
+    // A (tile i: c 64 wave + 16 i + r): two transposing reads of token rows 8 g + 4 q + r / 4
+    // at c 64 wave + 16 i + 4 (r % 4); element e of the fragment is token 8 g + e.
+    bf16x8 af[4], bq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = 8 * wave + 2 * i + (trb >> 1);
+      i16x4 pr[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int mrow = 8 * g + 4 * q + tre;
+        pr[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(pb + mrow * 512 + tn_pslot(mrow, sl) * 16 + (trb & 1) * 8));
+      }
+      af[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const int64_t mb = m_lo + st * kTnM;
+    if (mb + kTnM > a.m) {
+      // the stage runs past the last token: zero the copied duplicates of row m - 1
+      const int64_t room = a.m - mb - 8 * g;  // elements e < room are real tokens
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = an[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bq[j] = bn[j];
+        for (int e = 0; e < 8; ++e)
+          if (e >= room) af[i][e] = (__bf16)0.0f;
     }
-    // lane (r, g) of tile (i, j): c = cw + 16 i + 4 g + e, column jh + 16 j + r
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j = 16 * jt + r;
+      bq[jt] = *(const bf16x8*)(qb + j * 64 + tn_qslot(j, g) * 16);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int jt = 0; jt < 4; ++jt) acc[i][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bq[jt], acc[i][jt], 0, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lane (r, g) of tile (i, jt): c = c0 + 64 wave + 16 i + 4 g + e, column jb + 16 jt + r
+  float* out = a.part + split * a.c_total * a.qcp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[(cw + 16 * i + 4 * g + e) * a.qcp + jh + 16 * j + r] = acc[i][j][e];
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = c0 + 64 * wave + 16 * i + 4 * g + e;
+      if (c >= a.c_total) continue;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) out[c * a.qcp + jb + 16 * jt + r] = acc[i][jt][e];
+    }
   }
 }
 
@@ -335,15 +416,15 @@ namespace {
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int32_t rank_pad32(int32_t r) { return (r + 31) / 32 * 32; }
 int64_t ld32(int64_t m) { return (m + 31) / 32 * 32; }
-int32_t qc_pad(int32_t rank) { return (2 * rank_pad32(rank) + 127) / 128 * 128; }
-// Token splits of the adapter-gradient products: about 512 waves' worth of workgroups, at
-// least 256 tokens per split, at most 16 splits.
-int64_t nt_splits(int64_t m, int64_t c_total) {
-  const int64_t wgs = (c_total + 255) / 256;
-  int64_t sp = (512 + wgs - 1) / wgs;
-  const int64_t smax = (m + 255) / 256;
+int32_t qc_pad(int32_t rank) { return 2 * rank_pad32(rank); }  // hi | lo columns, a multiple of 64
+// Token splits of the adapter-gradient products: about 1024 workgroups (two per compute
+// unit fit in LDS), at least 128 tokens per split, at most 32 splits.
+int64_t tn_splits(int64_t m, int64_t c_total, int32_t qcp) {
+  const int64_t wgs = (c_total + kTnC - 1) / kTnC * (qcp / kTnJ);
+  int64_t sp = (1024 + wgs - 1) / wgs;
+  const int64_t smax = (m + 127) / 128;
   if (sp > smax) sp = smax;
-  if (sp > 16) sp = 16;
+  if (sp > 32) sp = 32;
   return sp < 1 ? 1 : sp;
 }
 // dX takes the transposed f16 product (gemm_nvfp4.hip) unless n or k exceed its 32-bit copy
@@ -356,8 +437,6 @@ struct BwdWs {
   float* dx_part;    // f16 path: split-tile partials of dX
   char* down_u;      // other path: lora_down scratch of dY B (hi | lo)
   char* down_t;      // lora_down scratch of x A^T (hi | lo)
-  uint16_t* dyt;     // [n][ld]
-  uint16_t* xt;      // [k][ld]
   uint16_t* tt;      // [qcp][ld]
   uint16_t* ut;      // [qcp][ld]
   float* part_b;     // [splits][n][qcp]
@@ -385,12 +464,10 @@ BwdWs bwd_ws(void* scratch, int64_t m, int64_t n, int64_t k, int32_t rank) {
   if (rank > 0) {
     const size_t ld = (size_t)ld32(m), qcp = (size_t)qc_pad(rank);
     w.down_t = take(lora_down_hilo_bytes(m, k, rank));
-    w.dyt = (uint16_t*)take((size_t)n * ld * 2);
-    w.xt = (uint16_t*)take((size_t)k * ld * 2);
     w.tt = (uint16_t*)take(qcp * ld * 2);
     w.ut = (uint16_t*)take(qcp * ld * 2);
-    w.part_b = (float*)take((size_t)nt_splits(m, n) * (size_t)n * qcp * 4);
-    w.part_a = (float*)take((size_t)nt_splits(m, k) * (size_t)k * qcp * 4);
+    w.part_b = (float*)take((size_t)tn_splits(m, n, (int32_t)qcp) * (size_t)n * qcp * 4);
+    w.part_a = (float*)take((size_t)tn_splits(m, k, (int32_t)qcp) * (size_t)k * qcp * 4);
   }
   w.bytes = off;
   return w;
@@ -456,24 +533,27 @@ hipError_t launch_backward_nvfp4(const uint16_t* x, const uint16_t* dy, int64_t 
     // dB[n][j] = sum_m dY[m][n] t[m][j];  dA[j][k] = sum_m du[m][j] x[m][k]  (hi and lo columns)
     const int64_t ld = ld32(m);
     const int32_t qcp = qc_pad(rank);
-    transpose2d(dy, m, n, n, ld, n, w.dyt, s);
-    transpose2d(x, m, k, k, ld, k, w.xt, s);
     transpose2d(t, m, 2 * rp, 2 * rp, ld, qcp, w.tt, s);
     transpose2d(du, m, 2 * rp, 2 * rp, ld, qcp, w.ut, s);
-    const struct { const uint16_t* pt; const uint16_t* qt; int64_t c; float* part; float* out; int64_t sc, sj; } jobs[2] = {
-        {w.dyt, w.tt, n, w.part_b, db, rank, 1}, {w.xt, w.ut, k, w.part_a, da, 1, k}};
+    e = hipFuncSetAttribute((const void*)bwd_tn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTnLds);
+    if (e != hipSuccess) return e;
+    const struct { const uint16_t* p; int64_t p_ld; const uint16_t* qt; int64_t c; float* part; float* out; int64_t sc, sj; }
+        jobs[2] = {{dy, n, w.tt, n, w.part_b, db, rank, 1}, {x, k, w.ut, k, w.part_a, da, 1, k}};
     for (const auto& jb : jobs) {
-      const int64_t sp = nt_splits(m, jb.c);
-      BwdNtArgs g;
-      g.pt = jb.pt;
+      const int64_t sp = tn_splits(m, jb.c, qcp);
+      BwdTnArgs g;
+      g.p = jb.p;
+      g.p_ld = jb.p_ld;
       g.qt = jb.qt;
-      g.c_total = jb.c;
+      g.m = m;
       g.ld = ld;
-      g.m_per_split = ((ld + sp - 1) / sp + 31) / 32 * 32;
+      g.c_total = jb.c;
+      g.m_per_split = ((ld + sp - 1) / sp + kTnM - 1) / kTnM * kTnM;
       g.qcp = qcp;
       g.part = jb.part;
       const int64_t used = (ld + g.m_per_split - 1) / g.m_per_split;
-      bwd_nt_kernel<<<dim3((unsigned)((jb.c + 255) / 256), (unsigned)used), 256, 0, s>>>(g);
+      bwd_tn_kernel<<<dim3((unsigned)((jb.c + kTnC - 1) / kTnC), (unsigned)(qcp / kTnJ), (unsigned)used), 256, kTnLds,
+                      s>>>(g);
       bwd_reduce_kernel<<<(unsigned)((jb.c * rank + 255) / 256), 256, 0, s>>>(jb.part, used, jb.c, qcp, rp, rank,
                                                                             jb.out, jb.sc, jb.sj);
     }

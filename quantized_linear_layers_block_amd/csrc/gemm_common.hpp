@@ -163,6 +163,15 @@ __device__ __forceinline__ void lds_copy16(const uint8_t* base, uint32_t off, ui
                : "memory");
 }
 
+// 16 bytes per lane from a per-lane 64-bit global address into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void lds_copy16_va(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(lds_base)
+               : "memory");
+}
+
 // 4 bytes per lane from global memory straight into LDS at m0 + 4 * lane.
 __device__ __forceinline__ void lds_copy4(const uint8_t* base, uint32_t off, uint32_t lds_base) {
   uint32_t saved;

@@ -765,8 +765,6 @@ static_assert(kDLds >= 8 * kQStagePerWave, "the output staging fits in the opera
 // between the two rows.  So both touch 16 distinct bank groups per 256 bytes.
 __device__ __forceinline__ int wslot(int n, int s) { return s ^ ((s >> 4) & 1) ^ (2 * ((n & 3) | ((n >> 2) & 4))); }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Nvfp4DxArgs {
   const uint16_t* dy16;  // f16 [m][n], row r scaled by 1 / rs[r]
@@ -849,6 +847,7 @@ __global__ __launch_bounds__(kDThreads) void gemm_nvfp4_dx_kernel(Nvfp4DxArgs a)
     *(f16x8*)(row + wslot(wr, 4 * wu + 2) * 16) = dequant8_f16(c.z, sc >> 8);
     *(f16x8*)(row + wslot(wr, 4 * wu + 3) * 16) = dequant8_f16(c.w, sc >> 8);
   };
+
   // Fragments of MFMA step h (n 16 g + 8 h .. +8 for lane group g, on both operands):
   // A (tile i: k 64 wk + 16 i + r) from two transposing reads of W rows 16 g + 8 h + 4 q +
   // r / 4 at k 64 wk + 16 i + 4 (r % 4); B (tile j: m 128 wm + 16 j + r) as in the forward.
@@ -877,9 +876,18 @@ __global__ __launch_bounds__(kDThreads) void gemm_nvfp4_dx_kernel(Nvfp4DxArgs a)
 
   // Stage s (relative to st0) uses dY slot s % 2, W buffer s % 2 and, for the next stage's
   // dequantization, code slot (s + 1) % 3.  Issue order: codes 0, 1, dY 0, codes 2; then
-  // (after W 0 is written) dY 1, codes 3; and after the barrier closing stage s, dY s + 2
-  // and codes s + 4.  At the end of stage s, vmcnt(2) leaves only codes s + 3 in flight:
-  // dY s + 1 and codes s + 2 have landed.
+  // (after W 0 is written) dY 1, codes 3; and after the barrier inside stage s, dY s + 2
+  // and codes s + 4.  At that barrier vmcnt(2) leaves only codes s + 3 in flight: dY s + 1
+  // and codes s + 2 have landed.
+  //
+  // Software pipeline.  A stage is two MFMA steps of four groups (one A fragment i x the
+  // eight B fragments).  Each A fragment is refetched for the next step right after its
+  // group, each B fragment after its last use in group 3, so the reads overlap the MFMAs
+  // of the following groups.  Step 0 also reads the next stage's codes and writes its
+  // dequantized weights.  The barrier sits between the steps: every wave has then read
+  // all of stage s, so its dY slot and code slot take new copies, and the next stage's W
+  // is complete, so step 1's refetches read stage s + 1's step 0.
+  f16x8 af[4], bq[8];
   if (st1 > st0) {
     dma_c(st0, 0);
     dma_c(clamp_st(st0 + 1), 1);
@@ -891,28 +899,61 @@ __global__ __launch_bounds__(kDThreads) void gemm_nvfp4_dx_kernel(Nvfp4DxArgs a)
     __syncthreads();  // W 0 complete; code slot 0 free
     dma_x(clamp_st(st0 + 1), 1);
     dma_c(clamp_st(st0 + 3), 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = read_a(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[j] = read_b(0, 0, j);
   }
   for (int64_t st = st0; st < st1; ++st) {
     const int ls = (int)(st - st0);
-    const int cur = ls & 1;
+    const int cur = ls & 1, nxt = cur ^ 1;
     const int cn = (ls + 1) % kDCSlots;
+    // step 0, with the next stage's dequantization (its codes and scales read first)
+    const uint8_t* cs = smem + kDCOff + cn * kDCSBytes;
+    const uint4 cw = *(const uint4*)(cs + wr * 128 + 16 * wu);
+    const uint32_t sc = *(const uint16_t*)(cs + kDCBytes + wr * 16 + 2 * wu);
+    uint8_t* wrow = smem + kDWOff + nxt * kDWBytes + wr * 512;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f16x8 af[4], bq[8];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = read_a(cur, h, i);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bq[j] = read_b(cur, h, j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bq[j], acc[i][j], 0, 0, 0);
-      if (h == 0) dequant(cn, cur ^ 1);  // stage st + 1 (unused after the last stage)
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bq[j], acc[i][j], 0, 0, 0);
+        if (i == 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          bq[j] = read_b(cur, 1, j);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      af[i] = read_a(cur, 1, i);
+      if (i == 1) {
+        *(f16x8*)(wrow + wslot(wr, 4 * wu + 0) * 16) = dequant8_f16(cw.x, sc & 0xFFu);
+        *(f16x8*)(wrow + wslot(wr, 4 * wu + 1) * 16) = dequant8_f16(cw.y, sc & 0xFFu);
+      } else if (i == 2) {
+        *(f16x8*)(wrow + wslot(wr, 4 * wu + 2) * 16) = dequant8_f16(cw.z, sc >> 8);
+        *(f16x8*)(wrow + wslot(wr, 4 * wu + 3) * 16) = dequant8_f16(cw.w, sc >> 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     __syncthreads();
     dma_x(clamp_st(st + 2), cur);
     dma_c(clamp_st(st + 4), cn);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1, refetching step 0 of the next stage (unused after the last stage)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bq[j], acc[i][j], 0, 0, 0);
+        if (i == 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          bq[j] = read_b(nxt, 0, j);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      af[i] = read_a(nxt, 0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
