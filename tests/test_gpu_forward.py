@@ -86,7 +86,10 @@ def test_nvfp4_decode_config2_full_size(shape_idx, m):
                                      # 33..64 tokens with K % 128 == 0: one stage, K % 256 != 0,
                                      # several K splits, ragged N, rank not a multiple of 8
                                      (64, 72, 128, 0), (33, 200, 1152, 8), (48, 1000, 2048, 32),
-                                     (50, 4100, 3840, 40), (37, 130, 640, 20), (64, 512, 3584, 32)])
+                                     (50, 4100, 3840, 40), (37, 130, 640, 20), (64, 512, 3584, 32),
+                                     # ... with N past 2048: ragged last tile, rank not a multiple
+                                     # of 8, a K split of fewer stages than the rest
+                                     (40, 2056, 1280, 12), (64, 2048, 640, 0)])
 def test_nvfp4_skinny_ragged(m, n, k, r):
     g = np.random.default_rng(m * 1000 + n + k)
     w = synth.normal_bf16((n, k), 0.02, g, 0.01, 15.0)
