@@ -375,6 +375,161 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
   }
 }
 
+// nv_stats_lds_kernel: nv_stats_kernel's outputs for m >= kNvStatsWideRows and an adapter
+// (128 rows per workgroup, two row fragments per wave), with the operands staged through
+// LDS.  Loaded straight into the MFMA operand layout, every instruction of nv_stats_kernel
+// fetches 16 rows x 64 bytes -- half of each 128-byte line -- and every wave fetches the A
+// slice on its own (at rank 64 twice the x bytes; 104 us for a 4096 x 27648 x).  Here
+// (87 us there; without an adapter it gains nothing, so nv_stats_kernel stays for rank 0)
+// each 128-column stage of the x tile (128 rows x 256
+// B) and of A (16 RT rows) is copied into LDS by whole lines (one copy: 4 rows x 256 B),
+// once per workgroup, and the fragments are read from LDS (16-byte unit u of row j at slot
+// u ^ (j % 16): conflict-free).  Same split boundaries, same k order inside each 32-wide
+// step, same fixed order of MFMA steps: amax_part and t_part equal nv_stats_kernel's (a
+// zero sum may come out +0 where it gave -0: steps past the split add zero products).
+// Columns past the split (the last stage may run past it) are zeroed in the fragments;
+// rows past m and A rows past the rank read a valid row and are masked as in
+// nv_stats_kernel.
+template <int RT>
+struct NvStatsLds {
+  static constexpr int kRows = 128, kARows = 16 * RT;
+  static constexpr int kStage = (kRows + kARows) * 256;
+  static constexpr int kSlots = 3 * kStage <= 160 * 1024 ? 3 : 2;
+  static constexpr int kXI = kRows / 16, kAI = kARows / 16;  // copies per wave per stage
+  static constexpr size_t kLds = (size_t)kSlots * kStage;
+};
+
+template <int RT>
+__global__ __launch_bounds__(256) void nv_stats_lds_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
+                                                           const uint16_t* __restrict__ lora_a, int32_t rank,
+                                                           int64_t tiles, int64_t kchunk,
+                                                           uint32_t* __restrict__ amax_part,
+                                                           float* __restrict__ t_part) {
+  using P = NvStatsLds<RT>;
+  constexpr int MF = 2, RA = RT > 0 ? RT : 1;
+  constexpr int L = P::kSlots - 1;  // stages of copy lead
+  constexpr int D = P::kXI + P::kAI;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t split = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int64_t k0 = split * kchunk;
+  const int64_t k1 = k0 + kchunk < k ? k0 + kchunk : k;
+  const int64_t nst = k1 > k0 ? (k1 - k0 + 127) / 128 : 0;
+  const int64_t row0 = tile * P::kRows;
+  // copy sources: x copy v of wave w covers tile rows 4 (w kXI + v) + lane / 16, A copy v
+  // A rows 4 (w kAI + v) + lane / 16; physical unit lane % 16 holds logical unit
+  // (lane % 16) ^ (row % 16)
+  const uint16_t* xs[P::kXI];
+  int xu[P::kXI];
+#pragma unroll
+  for (int v = 0; v < P::kXI; ++v) {
+    const int row = 4 * (wave * P::kXI + v) + (lane >> 4);
+    const int64_t gr = row0 + row < m ? row0 + row : m - 1;
+    xs[v] = x + gr * k;
+    xu[v] = (lane & 15) ^ (row & 15);
+  }
+  const uint16_t* as[P::kAI > 0 ? P::kAI : 1];
+  int au[P::kAI > 0 ? P::kAI : 1];
+#pragma unroll
+  for (int v = 0; v < P::kAI; ++v) {
+    const int row = 4 * (wave * P::kAI + v) + (lane >> 4);
+    as[v] = lora_a + (int64_t)(row < rank ? row : 0) * k;
+    au[v] = (lane & 15) ^ (row & 15);
+  }
+  auto dma = [&](int64_t st, int slot) {
+    const int64_t kb = k0 + st * 128;
+    const uint32_t lb = lds_addr(smem) + slot * P::kStage;
+#pragma unroll
+    for (int v = 0; v < P::kXI; ++v) {
+      const int64_t col = kb + 8 * xu[v] <= k - 8 ? kb + 8 * xu[v] : k - 8;
+      lds_copy16_va(xs[v] + col, lb + 1024 * (wave * P::kXI + v));
+    }
+#pragma unroll
+    for (int v = 0; v < P::kAI; ++v) {
+      const int64_t col = kb + 8 * au[v] <= k - 8 ? kb + 8 * au[v] : k - 8;
+      lds_copy16_va(as[v] + col, lb + P::kRows * 256 + 1024 * (wave * P::kAI + v));
+    }
+  };
+  auto clamp_st = [&](int64_t st) { return st < nst ? st : nst - 1; };
+
+  bool aok[RA];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) aok[i] = 16 * i + r < rank;
+  f32x4 acc[MF][RA];
+  uint32_t mx[MF];
+#pragma unroll
+  for (int h = 0; h < MF; ++h) {
+    mx[h] = 0;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) acc[h][i] = f32x4{0, 0, 0, 0};
+  }
+  if (nst > 0) {
+#pragma unroll
+    for (int v = 0; v < L; ++v) dma(clamp_st(v), v);
+  }
+  for (int64_t st = 0; st < nst; ++st) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((L - 1) * D) : "memory");  // stage st has landed
+    __syncthreads();  // ... for every wave, and every wave is done with stage st - 1's slot
+    dma(clamp_st(st + L), (int)((st + L) % P::kSlots));
+    const uint8_t* X = smem + (st % P::kSlots) * P::kStage;
+    const uint8_t* A = X + P::kRows * 256;
+    const int64_t kb = k0 + st * 128;
+    const bool tail = kb + 128 > k1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int u = 4 * ks + g;
+      const bool in = !tail || kb + 8 * u < k1;
+      i32x4 xv[MF], av[RA];
+#pragma unroll
+      for (int h = 0; h < MF; ++h) {
+        const int row = 16 * (MF * wave + h) + r;
+        xv[h] = *(const i32x4*)(X + row * 256 + 16 * (u ^ (row & 15)));
+        if (!in) xv[h] = i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int row = 16 * i + r;
+        av[i] = *(const i32x4*)(A + row * 256 + 16 * (u ^ (row & 15)));
+      }
+#pragma unroll
+      for (int h = 0; h < MF; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = (uint32_t)xv[h][e];
+          const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+          mx[h] = mx[h] > lo ? mx[h] : lo;
+          mx[h] = mx[h] > hi ? mx[h] : hi;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const i32x4 a = aok[i] ? av[i] : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < MF; ++h)
+          acc[h][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, xv[h]), acc[h][i], 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped copies past the range too
+#pragma unroll
+  for (int h = 0; h < MF; ++h) {
+    const int64_t row = row0 + 16 * (MF * wave + h) + r;
+    uint32_t v = mx[h];
+    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    if (row < m) {
+      if (g == 0) amax_part[split * m + row] = v;
+      // lane (r, g) of tile i holds rank 16 i + 4 g + (0..3) of row r
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        *(f32x4*)(t_part + (split * m + row) * (16 * RT) + 16 * i + 4 * g) = acc[h][i];
+    }
+  }
+}
+
 // nv_finish_kernel: one (row, chunk) unit per wave, chunk c covering the row's 16-byte
 // units 256 c .. +256 (four per lane, so a K = 5120 row takes three waves).  Row maximum
 // over the splits -> e putting it in [2^14, 2^15) (zero, Inf and NaN rows keep e = 0),
@@ -1072,10 +1227,17 @@ hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const uint16
   const unsigned sgrid = (unsigned)(tiles * sp);
 #define QL_NV_STATS(RT_)                                                                               \
   case RT_ / 16:                                                                                      \
-    if (mf == 2)                                                                                      \
+    if (mf == 2 && RT_ > 0) {                                                                         \
+      const size_t lds = NvStatsLds<RT_ / 16>::kLds;                                                  \
+      hipError_t e = hipFuncSetAttribute((const void*)nv_stats_lds_kernel<RT_ / 16>,                 \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);      \
+      if (e != hipSuccess) return e;                                                                  \
+      nv_stats_lds_kernel<RT_ / 16><<<sgrid, 256, lds, s>>>(x, m, k, lora_a, rank, tiles, kchunk, amax_part, t_part); \
+    } else if (mf == 2) {                                                                             \
       nv_stats_kernel<RT_ / 16, 2><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, amax_part, t_part); \
-    else                                                                                              \
+    } else {                                                                                          \
       nv_stats_kernel<RT_ / 16, 1><<<sgrid, 256, 0, s>>>(x, m, k, lora_a, rank, tiles, kchunk, amax_part, t_part); \
+    }                                                                                                 \
     break;
   switch (rank_pad / 16) {
     QL_NV_STATS(0)
