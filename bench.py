@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27870985, "fetch_bytes": 26577128, "write_bytes": 1293856,
+DECODE_TRAFFIC = {"bytes_per_launch": 27867265, "fetch_bytes": 26573409, "write_bytes": 1293856,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "196070371184e7890481574a0ae54f7840296f58789316cac0f5fb713e85d080"}
+                  "sources_sha256": "0ca8382403b5be51e7ca52c2936e2e34c31680601fbe3e0427876884bd8ff673"}
 
 # Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
 # duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over
@@ -57,15 +57,20 @@ DECODE_TRAFFIC = {"bytes_per_launch": 27870985, "fetch_bytes": 26577128, "write_
 # (mean over both shapes of the row).  Reported only while the kernel sources are the ones
 # measured (hash), like the traffic above.
 COUNTER_CLOCKS = {
-    "a5": {"GHz": 1.90, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "a5": {"GHz": 1.95, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "6241ee12eab3d724c7ed304daea81de8201316c8c9737112d2f1a34b19a929b2"},
-    "a6": {"GHz": 2.03, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "9f9125892aebb87e026637885bf827d6996b9c3375607267a3f92508bae7325f"},
+    "a6": {"GHz": 2.02, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "3f47381a7e1135f42b6c14cff44b9845edb20d0695fd4571ce0680687c170098"},
-    "a6p": {"GHz": 2.10, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
+    "a6p": {"GHz": 2.09, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-            "sources_sha256": "3f47381a7e1135f42b6c14cff44b9845edb20d0695fd4571ce0680687c170098"},
+            "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
+    # the backward's dX kernel (gemm_nvfp4_dx_kernel)
+    "bwd": {"GHz": 2.07, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp",
+                                     "quantized_linear_layers_block_amd/csrc/backward.hip"],
+            "sources_sha256": "259098c4e1368d7083095c4da314895b3785a705ed2230ebe24516e5e2fbac65"},
 }
 
 
@@ -627,6 +632,7 @@ def run_rows(rows, torch, ql, dev):
             flop = 2.0 * m * n * k + 2.0 * m * r_ * (2 * n + 3 * k)
             rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
             rr.update({"M": m, "K": k, "N": n, "rank": r_, "outputs": "dX bf16, dA and dB float32",
+                       "counter_clock_GHz_dx_kernel": counter_clock("bwd"),
                        "weight_copies_rotated": len(qs), **info})
             res.append(rr)
             del qs
