@@ -69,6 +69,16 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m quantized_linear_layers_block_amd.build`")
+    # One HIP runtime per process.  PyTorch ships its own libamdhip64 (same soname); loaded
+    # after this library it is mapped beside the system one, and device memory and streams
+    # of the one are unknown to the other (launches then fail).  Loaded first, it is the
+    # runtime this library binds to.  QLINEAR_NO_TORCH=1 skips it (the host-sanitizer run
+    # of the ABI checks, which launches nothing).
+    if not os.environ.get("QLINEAR_NO_TORCH"):
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {

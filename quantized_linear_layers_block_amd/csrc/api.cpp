@@ -114,6 +114,7 @@ qlinear_status qlinear_quantize_nvfp4(const uint16_t* w, int64_t n, int64_t k, u
     return QL_ERR_ALIGN;
   if (!ws || ws_bytes < qlinear_quantize_workspace(QL_NVFP4, n, k)) return QL_ERR_WORKSPACE;
   if (!aligned16(ws)) return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_nvfp4_quantize(w, n, k, codes, scales, tensor_scale, status_word,
                                               (uint32_t*)ws, (hipStream_t)stream));
 }
@@ -125,6 +126,7 @@ qlinear_status qlinear_quantize_fp8_block(const uint16_t* w, int64_t n, int64_t 
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) ||
       (status_word && ((uintptr_t)status_word & 3)))
     return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_fp8_weight_quantize(w, n, k, codes, scales, false, status_word,
                                                    (hipStream_t)stream));
 }
@@ -136,6 +138,7 @@ qlinear_status qlinear_quantize_fp8_pow2(const uint16_t* w, int64_t n, int64_t k
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) ||
       (status_word && ((uintptr_t)status_word & 3)))
     return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_fp8_weight_quantize(w, n, k, codes, scales, true, status_word,
                                                    (hipStream_t)stream));
 }
@@ -145,6 +148,7 @@ qlinear_status qlinear_quantize_act_fp8(const uint16_t* x, int64_t m, int64_t k,
   if (!x || !xq || !sx) return QL_ERR_NULL;
   if (!elems_ok(m, k) || k % 128) return QL_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_fp8_act_quantize(x, m, k, xq, sx, false, (hipStream_t)stream));
 }
 
@@ -153,6 +157,7 @@ qlinear_status qlinear_quantize_act_fp8_pow2(const uint16_t* x, int64_t m, int64
   if (!x || !xq || !sx) return QL_ERR_NULL;
   if (!elems_ok(m, k) || k % 128) return QL_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_fp8_act_quantize(x, m, k, xq, sx, true, (hipStream_t)stream));
 }
 
@@ -211,6 +216,7 @@ qlinear_status ql::forward_impl(const qlinear_qweight* w, const uint16_t* x, int
   hipStream_t s = (hipStream_t)stream;
   const int out_f32 = out_dtype == QL_OUT_F32;
   char* scratch = ql::ws_scratch(ws);
+  ql::clear_hip_error();
 
   if (w->format == QL_NVFP4) {
     const uint8_t* codes = (const uint8_t*)w->codes;
@@ -269,6 +275,7 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
   st = check_forward_ws(w, m, r, true, ws, ws_bytes);
   if (st != QL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  ql::clear_hip_error();
   uint16_t* t = nullptr;
   if (r > 0 && ql::launch_lora_down(x, m, w->k, lora_a, r, lora_scale, ql::ws_scratch(ws), &t, s) != hipSuccess)
     return QL_ERR_HIP;
@@ -307,6 +314,7 @@ qlinear_status qlinear_backward(const qlinear_qweight* w, const uint16_t* x, con
   const size_t need = up(ql::backward_scratch_bytes(m, w->n, w->k, r));
   if (need > 0 && (!ws || ws_bytes < need)) return QL_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_backward_nvfp4(x, dy, m, w->n, w->k, (const uint8_t*)w->codes,
                                               (const uint8_t*)w->scales, w->tensor_scale, lora_a, lora_b, r,
                                               lora_scale, dx, dx_dtype == QL_OUT_F32, da, db, ws,
@@ -327,6 +335,7 @@ static qlinear_status requant_common(const qlinear_requant_item* items, const ui
   if (format != QL_NVFP4 && !is_fp8(format)) return QL_ERR_FORMAT;
   if (!ws || ws_bytes < ql::requant_workspace(count)) return QL_ERR_WORKSPACE;
   if (!aligned16(items) || !aligned16(ws) || (deltas && ((uintptr_t)deltas & 7))) return QL_ERR_ALIGN;
+  ql::clear_hip_error();
   return hip_status(ql::launch_requant(items, deltas, count, format, ws, (hipStream_t)stream));
 }
 
@@ -364,6 +373,7 @@ qlinear_status qlinear_kv_store_fp8(const uint16_t* kv, int64_t tokens, int32_t 
   if (!aligned16(kv) || !aligned16(cache_codes) || !aligned16(cache_scales) || ((uintptr_t)slots & 7))
     return QL_ERR_ALIGN;
   if (tokens == 0) return QL_OK;
+  ql::clear_hip_error();
   return hip_status(ql::launch_kv_store(kv, tokens, heads, head_dim, slots, cache_codes, cache_scales, cache_slots,
                                         status_word, (hipStream_t)stream));
 }
@@ -378,6 +388,7 @@ qlinear_status qlinear_kv_load_fp8(const uint8_t* cache_codes, const float* cach
   if (!aligned16(out) || !aligned16(cache_codes) || !aligned16(cache_scales) || ((uintptr_t)slots & 7))
     return QL_ERR_ALIGN;
   if (tokens == 0) return QL_OK;
+  ql::clear_hip_error();
   return hip_status(ql::launch_kv_load(cache_codes, cache_scales, cache_slots, slots, tokens, heads, head_dim, out,
                                        status_word, (hipStream_t)stream));
 }

@@ -10,6 +10,11 @@
 
 namespace ql {
 
+// hipGetLastError reports the last failure of any HIP call on the thread, not only of the
+// launches just made: every entry point clears it before its first launch, so a launch
+// status reflects this library's launches alone.
+inline void clear_hip_error() { (void)hipGetLastError(); }
+
 // qlinear_forward's checks and dispatch (api.cpp), shared with the allocation-free variant.
 qlinear_status forward_impl(const qlinear_qweight* w, const uint16_t* x, int64_t m,
                             const uint16_t* lora_a, const uint16_t* lora_b, int32_t rank,

@@ -27,6 +27,17 @@ def _binding():
 b = _binding()
 
 
+def test_one_hip_runtime_in_process():
+    # PyTorch's bundled HIP runtime and the system one must not both be mapped: the binding
+    # loads PyTorch (when present) before the library, whatever imported first
+    if os.environ.get("QLINEAR_NO_TORCH"):
+        pytest.skip("PyTorch deliberately not loaded")
+    pytest.importorskip("torch")
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, sorted(paths)
+
+
 def _declared():
     src = open(os.path.join(ROOT, "include", "qlinear.h")).read()
     return sorted(set(re.findall(r"\b(qlinear_[a-z0-9_]+)\s*\(", src)))

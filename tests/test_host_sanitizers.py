@@ -33,7 +33,7 @@ def test_abi_checks_under_host_sanitizers(tmp_path):
              "-o", str(lib), "-Wl,-Bsymbolic", "-L" + PKG, "-l:libqlinear.so", "-Wl,-rpath," + PKG]
     r = subprocess.run(build, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
-    env = dict(os.environ, QLINEAR_LIB=str(lib), LD_PRELOAD=asan,
+    env = dict(os.environ, QLINEAR_LIB=str(lib), QLINEAR_NO_TORCH="1", LD_PRELOAD=asan,
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
