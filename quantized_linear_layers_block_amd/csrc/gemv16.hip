@@ -713,8 +713,9 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
 // 33 to 64 tokens, K % 128 == 0.  A workgroup owns 64 weight rows and all (up to) 64 tokens
 // over its K range, walked in stages of 128 columns.  Each stage's activations (16 KB),
 // codes (4 KB) and block scales are copied straight from global memory into LDS
-// (global_load_lds), activations three stages deep and codes and scales six, so the codes
-// stream five stages ahead of the multiply and no register holds data in flight.  Wave w
+// (global_load_lds, issued as inline assembly), activations three stages deep and codes
+// and scales six, so the codes stream five stages ahead of the multiply and no register
+// holds data in flight.  Wave w
 // takes MFMA K step w (32 columns) of every stage for all 64 rows and all 64 tokens: each
 // activation byte is then read from LDS by one wave only, and the four waves' tiles are
 // added in LDS in a fixed order at the end (wave w keeps rows 16 w .. +16).
@@ -725,18 +726,6 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
 // row's four; scales [73728, 79872) as 6 slots of 64 rows x 8 B (waves 2 and 3 copy a
 // second, unread image).  Both placements make every fragment read conflict-free.
 
-// Global -> LDS copies through the compiler's LDS-DMA builtin (16 or 4 bytes per lane, to
-// lds + 16 lane or lds + 4 lane; lds uniform): the compiler then knows them for what they
-// are and waits only where the explicit vmcnt waits below say (issued as inline assembly
-// it inserted vmcnt waits before unrelated LDS reads, which emptied the prefetch queue).
-typedef __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-__device__ __forceinline__ void lds_copy16_b(const uint8_t* base, uint32_t off, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4_b(const uint8_t* base, uint32_t off, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)lds, 4, 0, 0);
-}
 constexpr int kS128X = 16384, kS128C = 4096, kS128S = 1024;
 constexpr int kS128XSlots = 3, kS128CSlots = 6;
 constexpr int kS128COff = kS128XSlots * kS128X;
@@ -753,14 +742,13 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
   const int64_t split = id / a.tiles_w;
   const int64_t s0 = split * a.sps, s1 = min(s0 + a.sps, a.kst);
   const int64_t rbase = tile * 64;
-
-  // LoRA B rows of this wave's finishing rows (16 w .. +16) and S, before the stream
-  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
   const int64_t row_f = rbase + 16 * wave;
-  i32x4 bw[1][2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) bw[0][c] = g16_b_frag_vec(a, row_f + r, early_b && row_f + r < a.n, c);
-  const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // No copy of this item is in flight yet: a wait the compiler can see clears what it
+  // believes of loads on the kernel's other paths.  Without it, and with copies it could
+  // track, it put vmcnt(0) into every stage -- each stage then waited out a whole memory
+  // round trip and the copy leads below did nothing (18944 -> 3584 at 64 tokens: 37.9 ->
+  // 33.5 us once fixed; deeper rings then gain nothing more).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // per-lane global byte offsets (stage 0) of this wave's copies
   uint32_t xo[4];
@@ -781,14 +769,18 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
     const int64_t gs = rbase + srow < a.n ? rbase + srow : a.n - 1;
     so = (uint32_t)(gs * (a.k / 16) + 4 * (lane & 1));
   }
+  // Copies as inline assembly (lds_copy16/lds_copy4), awaited only by the explicit vmcnt
+  // below: through the compiler's builtin, with slot indices known only at run time, the
+  // compiler waited for every copy in flight before the stage's LDS reads.
+  const uint32_t lb = lds_addr(smem);
   auto dma_x = [&](int64_t st, int slot) {
     const uint8_t* base = (const uint8_t*)a.x + st * 256;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy16_b(base, xo[j], smem + slot * kS128X + (4 * wave + j) * 1024);
+    for (int j = 0; j < 4; ++j) lds_copy16(base, xo[j], lb + slot * kS128X + (4 * wave + j) * 1024);
   };
   auto dma_c = [&](int64_t st, int slot) {
-    lds_copy16_b(a.codes + st * 64, co, smem + kS128COff + slot * kS128C + wave * 1024);
-    lds_copy4_b(a.scales + st * 8, so, smem + kS128SOff + slot * kS128S + wave * 256);
+    lds_copy16(a.codes + st * 64, co, lb + kS128COff + slot * kS128C + wave * 1024);
+    lds_copy4(a.scales + st * 8, so, lb + kS128SOff + slot * kS128S + wave * 256);
   };
   auto cl = [&](int64_t st) { return st < s1 ? st : s1 - 1; };
 
@@ -842,6 +834,14 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped copies past the range too
   __syncthreads();
+
+  // LoRA B rows of this wave's finishing rows (16 w .. +16) and S: loads the compiler
+  // tracks stay out of the copy loop (see the wait at the top)
+  const bool early_b = a.rank > 0 && a.rank <= kG16EarlyRank && (a.rank & 7) == 0;
+  i32x4 bw[1][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) bw[0][c] = g16_b_frag_vec(a, row_f + r, early_b && row_f + r < a.n, c);
+  const float ts = __hip_atomic_load(a.tensor_scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // the four waves' K steps added in wave order; wave w keeps row tile w
   f32x4* red = (f32x4*)smem;
