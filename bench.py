@@ -760,16 +760,41 @@ def _policy(rows, torch, ql, dev, with_ceiling):
             loras.append((sg.normal_bf16((r_, k), 0.01, sg.gen(sg.seed_of(5, li, 3, i // 7)), device=dev),
                           sg.normal_bf16((n, r_), 0.01, sg.gen(sg.seed_of(5, li, 4, i // 7)), device=dev)))
 
+        # the layers that read the same activations run as one call each (q, k, v and gate,
+        # up: qlinear_forward_group); o and down on their own
+        groups = [(0, 1, 2), (3,), (4, 5), (6,)]
+        gws = []
+        for gi in groups:
+            k = synth.CFG5_LINEARS[gi[0]][1]
+            ns = [synth.CFG5_LINEARS[li][2] for li in gi]
+            gws.append(torch.zeros(ql.binding.qlinear_forward_group_workspace(m, k, ns, r_) + 16,
+                                   dtype=torch.uint8, device=dev))
+
         def decode_step():
+            for layer in range(c["layers"]):
+                for gi, w_ in zip(groups, gws):
+                    base = 7 * layer
+                    if len(gi) == 1:
+                        li = gi[0]
+                        a, b = loras[base + li]
+                        ql.forward(qs[base + li], xs[li], a, b, c["lora_scale"], out=ys[li], ws=w_)
+                    else:
+                        ql.forward_group([qs[base + li] for li in gi], xs[gi[0]], [loras[base + li] for li in gi],
+                                         c["lora_scale"], outs=[ys[li] for li in gi], ws=w_)
+
+        def decode_step_ungrouped():
             for i, q in enumerate(qs):
                 li = i % 7
                 a, b = loras[i]
                 ql.forward(q, xs[li], a, b, c["lora_scale"], out=ys[li], ws=wss[li])
 
         ms, info = _timed(torch, [decode_step], iters=20, repeats=5, warmup=2)
+        ms_u, _ = _timed(torch, [decode_step_ungrouped], iters=10, repeats=3, warmup=1)
         flop = sum(2.0 * m * (n * k + r_ * (k + n)) for (_, k, n) in synth.CFG5_LINEARS) * c["layers"]
         rr = with_ceiling(_row("mfma", flop, ms, BF16_PEAK, "flop"), "bf16_16x16x32")
-        rr.update({"M": m, "linears": len(qs), **info,
+        rr.update({"M": m, "linears": len(qs), "calls": c["layers"] * len(groups),
+                   "grouping": "q+k+v and gate+up as qlinear_forward_group, o and down alone", **info,
+                   "ungrouped_448_calls_us": round(ms_u * 1e3, 1),
                    "requant_over_decode": round(out["a8_requantize_all"]["us"] / (ms * 1e3), 3)})
         out["a9_policy_decode_step"] = rr
     return out

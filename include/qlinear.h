@@ -242,6 +242,41 @@ qlinear_status qlinear_forward_noalloc(const qlinear_qweight* w, const uint16_t*
 
 /* Workspace sizes (0 for invalid arguments and for shapes the kernels cannot run). */
 size_t qlinear_forward_workspace(int32_t format, int64_t m, int64_t n, int64_t k, int32_t rank);
+
+/* One layer of a qlinear_forward_group call (host struct holding device pointers). */
+typedef struct {
+  qlinear_qweight w;       /* QL_NVFP4, the group's common k                        */
+  const uint16_t* lora_a;  /* bf16 [rank][k], or NULL (then every layer's is NULL)  */
+  const uint16_t* lora_b;  /* bf16 [n][rank], NULL when lora_a is                   */
+  void* y;                 /* [m][n], bf16 or f32 per out_dtype                      */
+} qlinear_group_layer;
+
+/* Up to QLINEAR_MAX_GROUP NVFP4 layers that read the same activations -- the q, k and v
+ * projections of a decoder layer, or its gate and up projections -- each computing
+ * qlinear_forward's y = x . dequant(w)^T + lora_scale (x A^T) B^T into its own output.
+ * The whole policy runs every one of them once per decode step (tldrocket.com QeRL page,
+ * the paragraph after "Key Features of QeRL": rollout decoding is where the NVFP4 layer
+ * pays; the 32B-class layer's projections share their inputs).  For m > 64 and
+ * k % 64 == 0, with every adapter's rank a multiple of 32 and count * rank <= 128, the
+ * layers run as ONE activation pre-pass (row statistics, and every adapter's x A^T with
+ * the A matrices stacked) and ONE GEMM over all their weight rows (each layer's n rounded
+ * up to whole 256-row tiles, every tile in one layer, with that layer's tensor scale,
+ * adapter and output): the activations are converted once, and the split-K schedule that
+ * fills the chip covers the layers together.  Otherwise the layers run one after another
+ * exactly as qlinear_forward.  Results match qlinear_forward on each layer within the
+ * forward's tolerance (the K split order may differ).
+ * layers: host array of `count` entries; all share k (layers[0].w.k) and rank; either
+ * every layer has both adapter matrices or (rank 0, lora_scale 0, or all NULL) none.
+ * Workspace: qlinear_forward_group_workspace(m, k, n, count, rank) bytes (n: host array
+ * of the layers' n), with qlinear_forward's layout and reuse rules.
+ * Errors: as qlinear_forward for each layer, plus QL_ERR_ARG (count < 1 or >
+ * QLINEAR_MAX_GROUP), QL_ERR_SHAPE (a layer's k differs from the first), QL_ERR_NULL
+ * (layers NULL, or adapters on some layers but not all). */
+#define QLINEAR_MAX_GROUP 4
+qlinear_status qlinear_forward_group(const qlinear_group_layer* layers, int32_t count, const uint16_t* x,
+                                     int64_t m, int32_t rank, float lora_scale, int32_t out_dtype,
+                                     void* ws, size_t ws_bytes, void* stream);
+size_t qlinear_forward_group_workspace(int64_t m, int64_t k, const int64_t* n, int32_t count, int32_t rank);
 size_t qlinear_forward_prequant_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
 
 /* Backward pass of the NVFP4 + LoRA layer for LoRA training on the frozen 4-bit base

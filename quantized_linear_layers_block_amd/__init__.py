@@ -136,6 +136,26 @@ def forward(qw, x, lora_a=None, lora_b=None, lora_scale=0.0, out_dtype=torch.bfl
     return out
 
 
+def forward_group(qws, x, loras=None, lora_scale=0.0, out_dtype=torch.bfloat16, outs=None, ws=None):
+    """Several NVFP4 layers on the same x (a fused q/k/v or gate/up projection): returns
+    [x . dequant(qw)^T + lora_scale (x A^T) B^T for each qw]; loras is a list of (A, B)."""
+    _dev(_u16(x))
+    m = x.shape[0]
+    if loras is None:
+        loras = [(None, None)] * len(qws)
+    rank = 0 if loras[0][0] is None else loras[0][0].shape[0]
+    if outs is None:
+        outs = [torch.empty((m, qw.n), dtype=out_dtype, device=x.device) for qw in qws]
+    od = QL_OUT_F32 if outs[0].dtype == torch.float32 else QL_OUT_BF16
+    with_lora = all(a is not None and b is not None for a, b in loras)
+    eff_rank = rank if (with_lora and lora_scale != 0) else 0
+    if ws is None:
+        ws = _ws(binding.qlinear_forward_group_workspace(m, qws[0].k, [qw.n for qw in qws], eff_rank), x.device)
+    layers = [(qw.qweight(), a, b, y) for qw, (a, b), y in zip(qws, loras, outs)]
+    binding.qlinear_forward_group(layers, x, od, ws, rank, lora_scale)
+    return outs
+
+
 def forward_fp8_prequant(qw, xq, sx, x=None, lora_a=None, lora_b=None, lora_scale=0.0,
                          out_dtype=torch.bfloat16, out=None, ws=None):
     m = xq.shape[0]

@@ -41,6 +41,8 @@ EXPORTS = [
     "qlinear_kv_load_fp8",
     "qlinear_backward",
     "qlinear_backward_workspace",
+    "qlinear_forward_group",
+    "qlinear_forward_group_workspace",
 ]
 
 QLINEAR_STATUS_NONFINITE, QLINEAR_STATUS_TIMEOUT, QLINEAR_STATUS_BAD_ITEM = 1, 2, 4
@@ -63,6 +65,10 @@ class QWeight(ctypes.Structure):
 
 class RequantItem(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("q", QWeight)]
+
+
+class GroupLayer(ctypes.Structure):
+    _fields_ = [("w", QWeight), ("lora_a", ctypes.c_void_p), ("lora_b", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 def _load():
@@ -104,6 +110,8 @@ def _load():
         "qlinear_backward": ([ctypes.POINTER(QWeight), vp, vp, i64, vp, vp, i32, f32, vp, i32, vp, vp, vp, sz, vp],
                              i32),
         "qlinear_backward_workspace": ([i32, i64, i64, i64, i32], sz),
+        "qlinear_forward_group": ([vp, i32, vp, i64, i32, f32, i32, vp, sz, vp], i32),
+        "qlinear_forward_group_workspace": ([i64, i64, vp, i32, i32], sz),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -199,6 +207,21 @@ def qlinear_forward(qw, x, y, out_dtype, ws=None, lora_a=None, lora_b=None, rank
     _check(LIB.qlinear_forward(ctypes.byref(qw), _ptr(x), m, _ptr(lora_a), _ptr(lora_b), rank,
                                float(lora_scale), _ptr(y), out_dtype, _ptr(ws), wsb, _stream(stream)),
            "qlinear_forward")
+
+
+def qlinear_forward_group_workspace(m, k, ns, rank):
+    arr = (ctypes.c_int64 * len(ns))(*ns)
+    return LIB.qlinear_forward_group_workspace(m, k, ctypes.cast(arr, ctypes.c_void_p), len(ns), rank)
+
+
+def qlinear_forward_group(layers, x, out_dtype, ws=None, rank=0, lora_scale=0.0, stream=None):
+    """Layers reading the same x [m,k]: layers is a list of (qweight, lora_a, lora_b, y)."""
+    m = x.shape[0]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    arr = (GroupLayer * len(layers))(*[GroupLayer(qw, _ptr(a), _ptr(b), _ptr(y)) for qw, a, b, y in layers])
+    _check(LIB.qlinear_forward_group(ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(x), m, rank,
+                                     float(lora_scale), out_dtype, _ptr(ws), wsb, _stream(stream)),
+           "qlinear_forward_group")
 
 
 def qlinear_backward_workspace(fmt, m, n, k, rank):

@@ -283,6 +283,84 @@ qlinear_status qlinear_forward_fp8_prequant(const qlinear_qweight* w, const uint
                                         w->format == QL_FP8_POW2, t, lora_b, r, y, out_dtype == QL_OUT_F32, s));
 }
 
+// ---------------------------------------------------------- layers sharing x
+
+static_assert(QLINEAR_MAX_GROUP == ql::kNvMaxSeg, "group size");
+
+// Whether a group runs fused (one pre-pass, one GEMM) rather than layer by layer.
+static bool group_fused(int32_t count, int64_t m, int64_t k, int32_t r) {
+  return count > 1 && m > kG16MaxM && nvfp4_f16_path(k) && r % 32 == 0 && count * r <= 128;
+}
+
+size_t qlinear_forward_group_workspace(int64_t m, int64_t k, const int64_t* n, int32_t count, int32_t rank) {
+  if (!n || count < 1 || count > QLINEAR_MAX_GROUP || m <= 0 || k <= 0 || rank < 0 || rank > QLINEAR_MAX_RANK)
+    return 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (n[i] <= 0) return 0;
+  size_t s = 0;
+  if (group_fused(count, m, k, rank)) {
+    s = up(ql::gemm_nvfp4_f16_layers_workspace(m, k, n, count, rank));
+  } else {
+    for (int32_t i = 0; i < count; ++i) {
+      const size_t si = forward_scratch(QL_NVFP4, m, n[i], k, rank, false);
+      if (si == SIZE_MAX) return 0;
+      if (si > s) s = si;
+    }
+  }
+  return ql::kWsReserved + s;
+}
+
+qlinear_status qlinear_forward_group(const qlinear_group_layer* layers, int32_t count, const uint16_t* x,
+                                     int64_t m, int32_t rank, float lora_scale, int32_t out_dtype,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  if (!layers) return QL_ERR_NULL;
+  if (count < 1 || count > QLINEAR_MAX_GROUP) return QL_ERR_ARG;
+  if (!x) return QL_ERR_NULL;
+  if (!aligned16(x)) return QL_ERR_ALIGN;
+  int with = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlinear_group_layer& l = layers[i];
+    qlinear_status st = check_forward_common(&l.w, m, l.lora_a, l.lora_b, rank, l.y, out_dtype);
+    if (st != QL_OK) return st;
+    if (l.w.format != QL_NVFP4) return QL_ERR_FORMAT;
+    if (l.w.k != layers[0].w.k) return QL_ERR_SHAPE;
+    with += (l.lora_a && l.lora_b) ? 1 : 0;
+  }
+  const bool lora = rank > 0 && lora_scale != 0.0f;
+  if (lora && with != 0 && with != count) return QL_ERR_NULL;
+  const int32_t r = lora && with == count ? rank : 0;
+  const int64_t k = layers[0].w.k;
+  int64_t ns[QLINEAR_MAX_GROUP];
+  for (int32_t i = 0; i < count; ++i) ns[i] = layers[i].w.n;
+  const size_t need = qlinear_forward_group_workspace(m, k, ns, count, r);
+  if (need == 0) return QL_ERR_SHAPE;
+  if (!ws || ws_bytes < need) return QL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QL_ERR_ALIGN;
+  if (!group_fused(count, m, k, r)) {
+    for (int32_t i = 0; i < count; ++i) {
+      const qlinear_group_layer& l = layers[i];
+      const qlinear_status st = ql::forward_impl(&l.w, x, m, r ? l.lora_a : nullptr, r ? l.lora_b : nullptr, r,
+                                                 lora_scale, l.y, out_dtype, ws, ws_bytes, stream);
+      if (st != QL_OK) return st;
+    }
+    return QL_OK;
+  }
+  ql::NvLayer nl[QLINEAR_MAX_GROUP];
+  for (int32_t i = 0; i < count; ++i) {
+    const qlinear_group_layer& l = layers[i];
+    nl[i].codes = (const uint8_t*)l.w.codes;
+    nl[i].scales = (const uint8_t*)l.w.scales;
+    nl[i].tensor_scale = l.w.tensor_scale;
+    nl[i].lora_a = r ? l.lora_a : nullptr;
+    nl[i].lora_b = r ? l.lora_b : nullptr;
+    nl[i].y = l.y;
+    nl[i].n = l.w.n;
+  }
+  ql::clear_hip_error();
+  return hip_status(ql::launch_gemm_nvfp4_f16_layers(x, m, k, nl, count, r, lora_scale, out_dtype == QL_OUT_F32,
+                                                     ql::ws_scratch(ws), (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ backward
 
 static bool backward_shape_ok(int64_t m, int64_t n, int64_t k) {

@@ -252,6 +252,26 @@ constexpr int kQPitch = 144;                 // output staging row: 64 bf16 + 16
 constexpr int kQStagePerWave = 128 * kQPitch;
 constexpr size_t kQLds = kQRingBytes > 8 * kQStagePerWave ? kQRingBytes : 8 * kQStagePerWave;
 
+// Up to kNvMaxSeg layers of one fused projection, as the GEMM and its tail see them.
+struct NvSegs {
+  int32_t nseg;                        // 1: a single layer
+  int64_t tile[kNvMaxSeg + 1];         // first n tile of each layer; tile[nseg] = all n tiles
+  const uint8_t* codes[kNvMaxSeg];
+  const uint8_t* scales[kNvMaxSeg];
+  const float* tensor_scale[kNvMaxSeg];
+  const uint16_t* lora_b[kNvMaxSeg];
+  void* y[kNvMaxSeg];
+  int64_t n[kNvMaxSeg];
+};
+
+// Layer of n tile tn (the segments are few and their bounds uniform).
+__device__ __forceinline__ int nv_seg_of(const NvSegs& sg, int64_t tn) {
+  int s = 0;
+  for (int i = 1; i < sg.nseg; ++i)
+    if (tn >= sg.tile[i]) s = i;
+  return s;
+}
+
 struct Nvfp4F16Args {
   const uint16_t* x16;  // f16 [m][k], row r scaled by 1 / rs[r]
   const float* rs;      // [m] row factors (powers of two)
@@ -267,6 +287,11 @@ struct Nvfp4F16Args {
   int64_t full_tiles;  // workgroups that take whole tiles
   int32_t tail_split;  // K splits of each remaining tile
   float* part;         // [split workgroup][256 m][256 n] float32 partial tiles
+  // Layers that share x (a fused projection): n tiles [seg.tile[s], seg.tile[s + 1]) are
+  // those of layer s, with its own codes, scales, tensor scale, B, output and n (the
+  // fields above are unused then), and its t columns at s * rank of rows t_stride long.
+  NvSegs seg;
+  int32_t t_stride;
 };
 
 // Activation pre-pass, in two kernels.
@@ -280,9 +305,24 @@ struct Nvfp4F16Args {
 // so that they share the same range of A in L2.  k % 16 == 0; split boundaries are
 // multiples of 32, and a last step that runs past k reads zeros for the 8-element units
 // beyond it.
+// The A matrices of up to kNvMaxSeg adapters stacked into one: stacked row j is row
+// j - s seg_rank of adapter s, s = j / seg_rank (one adapter: seg_rank = its rank).
+struct NvLoraA {
+  const uint16_t* a[kNvMaxSeg];
+  int32_t seg_rank;
+};
+__device__ __forceinline__ const uint16_t* nv_a_row(const NvLoraA& A, int j, int64_t k) {
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < kNvMaxSeg; ++i)
+    if (j >= i * A.seg_rank) s = i;
+  const uint16_t* p = s == 0 ? A.a[0] : s == 1 ? A.a[1] : s == 2 ? A.a[2] : A.a[3];
+  return p + (int64_t)(j - s * A.seg_rank) * k;
+}
+
 template <int RT, int MF>
 __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
-                                                       const uint16_t* __restrict__ lora_a, int32_t rank,
+                                                       NvLoraA lora_a, int32_t rank,
                                                        int64_t tiles, int64_t kchunk,
                                                        uint32_t* __restrict__ amax_part,
                                                        float* __restrict__ t_part) {
@@ -305,7 +345,7 @@ __global__ __launch_bounds__(256) void nv_stats_kernel(const uint16_t* __restric
   for (int i = 0; i < RT; ++i) {
     const int j = 16 * i + r;
     aok[i] = j < rank;
-    ar[i] = lora_a + (int64_t)(aok[i] ? j : 0) * k + 8 * g;
+    ar[i] = nv_a_row(lora_a, aok[i] ? j : 0, k) + 8 * g;
   }
   f32x4 acc[MF][RA];
   uint32_t mx[MF];
@@ -401,7 +441,7 @@ struct NvStatsLds {
 
 template <int RT>
 __global__ __launch_bounds__(256) void nv_stats_lds_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
-                                                           const uint16_t* __restrict__ lora_a, int32_t rank,
+                                                           NvLoraA lora_a, int32_t rank,
                                                            int64_t tiles, int64_t kchunk,
                                                            uint32_t* __restrict__ amax_part,
                                                            float* __restrict__ t_part) {
@@ -435,7 +475,7 @@ __global__ __launch_bounds__(256) void nv_stats_lds_kernel(const uint16_t* __res
 #pragma unroll
   for (int v = 0; v < P::kAI; ++v) {
     const int row = 4 * (wave * P::kAI + v) + (lane >> 4);
-    as[v] = lora_a + (int64_t)(row < rank ? row : 0) * k;
+    as[v] = nv_a_row(lora_a, row < rank ? row : 0, k);
     au[v] = (lane & 15) ^ (row & 15);
   }
   auto dma = [&](int64_t st, int slot) {
@@ -646,7 +686,14 @@ template <int OUT_F32>
 __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GemmWork work = gemm_schedule(a.tiles_m, a.tiles_n, a.full_tiles, a.tail_split);
-  const int64_t n0 = work.tn * kQTile, m0 = work.tm * kQTile;
+  // the layer this n tile belongs to, and the tile's place in it
+  const int sg = nv_seg_of(a.seg, work.tn);
+  const int64_t N = a.seg.n[sg];
+  const uint8_t* const codes = a.seg.codes[sg];
+  const uint8_t* const scales = a.seg.scales[sg];
+  const uint16_t* const lora_b = a.seg.lora_b[sg];
+  void* const yout = a.seg.y[sg];
+  const int64_t n0 = (work.tn - a.seg.tile[sg]) * kQTile, m0 = work.tm * kQTile;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int wn = wave & 3, wm = wave >> 2;  // wave tile: n 64 wn .. +64, m 128 wm .. +128
@@ -656,7 +703,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   const int64_t kper = (kst_all + work.nsplit - 1) / work.nsplit;
   const int64_t st0 = work.split * kper;
   const int64_t st1 = st0 + kper < kst_all ? st0 + kper : kst_all;
-  const int64_t n_last = a.n - 1 - n0, m_last = a.m - 1 - m0;
+  const int64_t n_last = N - 1 - n0, m_last = a.m - 1 - m0;
 
   // Copies of one stage, per wave: 4 x activations (8 rows of 128 bytes each, swizzled
   // 16-byte slots), 1 x codes (32 rows of 32 bytes), 1 x scales (64 rows of 4 bytes from
@@ -677,8 +724,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
     so = (uint32_t)((srow < n_last ? srow : n_last) * (a.k / 16));
   }
   const uint8_t* xb = (const uint8_t*)(a.x16 + m0 * a.k);
-  const uint8_t* cb = a.codes + n0 * (a.k / 2);
-  const uint8_t* sb = a.scales + n0 * (a.k / 16);
+  const uint8_t* cb = codes + n0 * (a.k / 2);
+  const uint8_t* sb = scales + n0 * (a.k / 16);
   // Copies of stage st into activation slot xb / code slot cb.  Activations are shared by
   // every workgroup of an m tile (mostly L2 hits); codes stream from HBM once per m tile,
   // so their ring is deeper.
@@ -802,7 +849,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue: lane holds n = n0 + 64 wn + 16 i + 4 g + (0..3), m = m0 + 128 wm + 16 j + r.
-  const float S = *a.tensor_scale;
+  const float S = *a.seg.tensor_scale[sg];
   float fac[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -814,7 +861,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] *= fac[j];
   if (a.rank_pad > 0 && work.split == 0)
-    lora_wave<4, 8>(a.lora_b, a.t, a.rank, a.rank_pad, a.n, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g, acc);
+    lora_wave<4, 8>(lora_b, a.t + (int64_t)sg * a.rank, a.rank, a.rank_pad, N, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g,
+                    acc, a.t_stride);
   if (work.slot >= 0) {
     // split tile: scaled float32 partial (LoRA in split 0), summed by nv_tail_reduce_kernel
     float* pt = a.part + work.slot * (kQTile * kQTile);
@@ -825,7 +873,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
         *(f32x4*)(pt + (128 * wm + 16 * j + r) * kQTile + 64 * wn + 16 * i + 4 * g) = acc[i][j];
     return;
   }
-  if (!OUT_F32 && m0 + kQTile <= a.m && n0 + kQTile <= a.n && (a.n & 7) == 0) {
+  if (!OUT_F32 && m0 + kQTile <= a.m && n0 + kQTile <= N && (N & 7) == 0) {
     // Interior bf16 tile: the wave's 128 (m) x 64 (n) block is transposed through LDS (row
     // pitch 144 bytes keeps the 8-byte writes conflict-free) and leaves as whole 128-byte
     // rows, eight rows per store instruction.
@@ -840,11 +888,11 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
             make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
       }
     }
-    uint16_t* ybase = (uint16_t*)a.y + (m0 + 128 * wm) * a.n + n0 + 64 * wn + (lane & 7) * 8;
+    uint16_t* ybase = (uint16_t*)yout + (m0 + 128 * wm) * N + n0 + 64 * wn + (lane & 7) * 8;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = 8 * q + (lane >> 3);
-      *(i32x4*)(ybase + row * a.n) = *(const i32x4*)(stage + row * kQPitch + (lane & 7) * 16);
+      *(i32x4*)(ybase + row * N) = *(const i32x4*)(stage + row * kQPitch + (lane & 7) * 16);
     }
   } else {
 #pragma unroll
@@ -852,7 +900,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t mrow = m0 + 128 * wm + 16 * j + r;
-        if (mrow < a.m) store4(a.y, OUT_F32, a.n, mrow, n0 + 64 * wn + 16 * i + 4 * g, acc[i][j], a.n);
+        if (mrow < a.m) store4(yout, OUT_F32, N, mrow, n0 + 64 * wn + 16 * i + 4 * g, acc[i][j], N);
       }
     }
   }
@@ -862,7 +910,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
 // epilogue.  Workgroup: 4 rows of one tail tile, 4 consecutive n per thread.
 __global__ __launch_bounds__(256) void nv_tail_reduce_kernel(const float* __restrict__ part, int64_t tiles_m,
                                                              int64_t tiles_n, int64_t full, int32_t splits,
-                                                             int64_t m, int64_t n, void* y, int out_f32) {
+                                                             int64_t m, NvSegs seg, int out_f32) {
   const int64_t tail = blockIdx.x / 64;
   const int row = (int)(blockIdx.x % 64) * 4 + (int)(threadIdx.x >> 6);
   const int col = (int)(threadIdx.x & 63) * 4;
@@ -870,10 +918,12 @@ __global__ __launch_bounds__(256) void nv_tail_reduce_kernel(const float* __rest
   gemm_group_tile(full + tail, tiles_m, tiles_n, tm, tn);
   const int64_t mr = tm * kQTile + row;
   if (mr >= m) return;
+  const int sg = nv_seg_of(seg, tn);
+  const int64_t n = seg.n[sg], c = (tn - seg.tile[sg]) * kQTile + col;
   const float* p = part + tail * splits * (kQTile * kQTile) + row * kQTile + col;
   f32x4 v = *(const f32x4*)p;
   for (int sp = 1; sp < splits; ++sp) v += *(const f32x4*)(p + sp * (kQTile * kQTile));
-  if (tn * kQTile + col < n) store4(y, out_f32, n, mr, tn * kQTile + col, v, n);
+  if (c < n) store4(seg.y[sg], out_f32, n, mr, c, v, n);
 }
 
 // ------------------------------------------------------------ transposed product (backward)
@@ -1215,8 +1265,9 @@ struct NvPrepWs {
   size_t bytes;
 };
 
-// Row statistics and LoRA partials (nv_stats_kernel) over nv_prep_splits(m, k) K splits.
-hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int32_t rank,
+// Row statistics and LoRA partials (nv_stats_kernel) over nv_prep_splits(m, k) K splits;
+// rank: rows of the stacked A.
+hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const NvLoraA& lora_a, int32_t rank,
                            uint32_t* amax_part, float* t_part, hipStream_t s) {
   const int32_t rank_pad = nv_rank_pad(rank);
   // Large m: 128 rows per workgroup, so each load of A serves two row fragments (the split
@@ -1249,6 +1300,14 @@ hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const uint16
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_nv_stats(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int32_t rank,
+                           uint32_t* amax_part, float* t_part, hipStream_t s) {
+  NvLoraA A = {};
+  A.a[0] = lora_a;
+  A.seg_rank = rank > 0 ? rank : 1;
+  return launch_nv_stats(x, m, k, A, rank, amax_part, t_part, s);
 }
 
 NvPrepWs nv_prep_ws(void* ws, int64_t m, int64_t n, int64_t k, int32_t rank) {
@@ -1340,41 +1399,69 @@ size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank) {
   return nv_prep_ws(nullptr, m, n, k, rank).bytes;
 }
 
-hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
-                                 const uint8_t* codes, const uint8_t* scales,
-                                 const float* tensor_scale, const uint16_t* lora_a,
-                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
-                                 int out_f32, void* ws, hipStream_t s) {
-  if (m <= 0 || n <= 0) return hipSuccess;
-  // Copy offsets are 32-bit within a 256-row tile.
-  if (k % kQK != 0 || k >= kNvF16MaxK || !ws || rank < 0 || rank > 128)
+// n of the tile plan of layers sharing x: each layer's n rounded up to whole tiles.
+static int64_t nv_layers_n(const int64_t* n, int nl) {
+  int64_t t = 0;
+  for (int i = 0; i < nl; ++i) t += (n[i] + kQTile - 1) / kQTile;
+  return t * kQTile;
+}
+
+size_t gemm_nvfp4_f16_layers_workspace(int64_t m, int64_t k, const int64_t* n, int nl, int32_t rank) {
+  if (nl < 1 || nl > kNvMaxSeg) return 0;
+  return gemm_nvfp4_f16_workspace(m, nv_layers_n(n, nl), k, nl * rank);
+}
+
+hipError_t launch_gemm_nvfp4_f16_layers(const uint16_t* x, int64_t m, int64_t k, const NvLayer* layers, int nl,
+                                        int32_t rank, float lora_scale, int out_f32, void* ws, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  // Copy offsets are 32-bit within a 256-row tile.  Several layers stack their adapters'
+  // ranks (each a multiple of 32, so every layer's t columns start on a 64-byte boundary).
+  if (k % kQK != 0 || k >= kNvF16MaxK || !ws || rank < 0 || nl < 1 || nl > kNvMaxSeg ||
+      nl * rank > 128 || (nl > 1 && rank % 32 != 0))
     return hipErrorInvalidValue;
-  const int32_t rank_pad = nv_rank_pad(rank);
-  const NvPrepWs w = nv_prep_ws(ws, m, n, k, rank);
+  int64_t ns[kNvMaxSeg];
+  for (int i = 0; i < nl; ++i) {
+    if (layers[i].n <= 0) return hipErrorInvalidValue;
+    ns[i] = layers[i].n;
+  }
+  const int32_t rank_all = nl * rank;
+  const int32_t rank_pad = nv_rank_pad(rank_all);
+  const int64_t n_all = nv_layers_n(ns, nl);
+  const NvPrepWs w = nv_prep_ws(ws, m, n_all, k, rank_all);
   const int64_t sp = nv_prep_splits(m, k);
-  hipError_t e0 = launch_nv_stats(x, m, k, lora_a, rank, w.amax_part, w.t_part, s);
+  NvLoraA A = {};
+  for (int i = 0; i < nl; ++i) A.a[i] = layers[i].lora_a;
+  A.seg_rank = rank > 0 ? rank : 1;
+  hipError_t e0 = launch_nv_stats(x, m, k, A, rank_all, w.amax_part, w.t_part, s);
   if (e0 != hipSuccess) return e0;
   const int64_t fin_units = m * ((k / 8 + kNvChunk8 - 1) / kNvChunk8);
-  nv_finish_kernel<<<(unsigned)((fin_units + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank,
+  nv_finish_kernel<<<(unsigned)((fin_units + 3) / 4), 256, 0, s>>>(x, m, k, sp, w.amax_part, w.t_part, rank_all,
                                                                     rank_pad, lora_scale, w.x16, w.rs, w.t);
-  uint16_t* x16 = w.x16;
-  float* rs = w.rs;
-  uint16_t* t = rank > 0 ? w.t : nullptr;
-  Nvfp4F16Args a;
-  a.x16 = x16;
-  a.rs = rs;
+  Nvfp4F16Args a = {};
+  a.x16 = w.x16;
+  a.rs = w.rs;
   a.m = m;
-  a.n = n;
+  a.n = n_all;
   a.k = k;
-  a.codes = codes;
-  a.scales = scales;
-  a.tensor_scale = tensor_scale;
-  a.t = t;
-  a.lora_b = lora_b;
+  a.t = rank > 0 ? w.t : nullptr;
   a.rank = rank;
-  a.rank_pad = rank_pad;
-  a.y = y;
-  const NvTilePlan tp = nv_tile_plan(m, n, k);
+  // one layer: its t rows are rank_pad long; several: layer i's ranks at i * rank
+  a.rank_pad = rank > 0 ? (nl > 1 ? rank : rank_pad) : 0;
+  a.t_stride = rank_pad;
+  a.seg.nseg = nl;
+  int64_t tile = 0;
+  for (int i = 0; i < nl; ++i) {
+    a.seg.tile[i] = tile;
+    tile += (layers[i].n + kQTile - 1) / kQTile;
+    a.seg.codes[i] = layers[i].codes;
+    a.seg.scales[i] = layers[i].scales;
+    a.seg.tensor_scale[i] = layers[i].tensor_scale;
+    a.seg.lora_b[i] = layers[i].lora_b;
+    a.seg.y[i] = layers[i].y;
+    a.seg.n[i] = layers[i].n;
+  }
+  a.seg.tile[nl] = tile;
+  const NvTilePlan tp = nv_tile_plan(m, n_all, k);
   a.tiles_m = tp.tiles_m;
   a.tiles_n = tp.tiles_n;
   a.full_tiles = tp.full;
@@ -1392,8 +1479,26 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
   }
   if (tp.split > 1)
     nv_tail_reduce_kernel<<<(unsigned)(tp.tail() * 64), 256, 0, s>>>(w.tile_part, tp.tiles_m, tp.tiles_n, tp.full,
-                                                                    tp.split, m, n, y, out_f32);
+                                                                    tp.split, m, a.seg, out_f32);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* codes, const uint8_t* scales,
+                                 const float* tensor_scale, const uint16_t* lora_a,
+                                 const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
+                                 int out_f32, void* ws, hipStream_t s) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  if (rank > 128) return hipErrorInvalidValue;
+  NvLayer l;
+  l.codes = codes;
+  l.scales = scales;
+  l.tensor_scale = tensor_scale;
+  l.lora_a = lora_a;
+  l.lora_b = lora_b;
+  l.y = y;
+  l.n = n;
+  return launch_gemm_nvfp4_f16_layers(x, m, k, &l, 1, rank, lora_scale, out_f32, ws, s);
 }
 
 hipError_t launch_gemm_nvfp4(const uint16_t* x, int64_t m, int64_t n, int64_t k,
@@ -1529,9 +1634,15 @@ hipError_t launch_nvfp4_dx(const uint16_t* dy16, const float* rs, int64_t m, int
     if (e != hipSuccess) return e;
     gemm_nvfp4_dx_kernel<0><<<grid, kDThreads, kDLds, s>>>(a);
   }
-  if (tp.split > 1)
+  if (tp.split > 1) {
+    NvSegs one = {};
+    one.nseg = 1;
+    one.tile[1] = tp.tiles_n;
+    one.y[0] = dx;
+    one.n[0] = k;
     nv_tail_reduce_kernel<<<(unsigned)(tp.tail() * 64), 256, 0, s>>>(part, tp.tiles_m, tp.tiles_n, tp.full, tp.split,
-                                                                    m, k, dx, out_f32);
+                                                                    m, one, out_f32);
+  }
   return hipGetLastError();
 }
 

@@ -127,6 +127,23 @@ hipError_t launch_gemm_nvfp4_f16(const uint16_t* x, int64_t m, int64_t n, int64_
                                  const uint16_t* lora_b, int32_t rank, float lora_scale, void* y,
                                  int out_f32, void* scratch, hipStream_t s);
 size_t gemm_nvfp4_f16_workspace(int64_t m, int64_t n, int64_t k, int32_t rank);
+// Up to kNvMaxSeg layers that read the same x (a fused projection) as one pre-pass and one
+// GEMM over all their n tiles (each layer's n rounded up to whole 256-row tiles); the
+// adapters (all of rank `rank`, a multiple of 32 for more than one layer, nl * rank <= 128)
+// are stacked for the pre-pass.  nl == 1 is launch_gemm_nvfp4_f16.
+constexpr int kNvMaxSeg = 4;
+struct NvLayer {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  const uint16_t* lora_a;
+  const uint16_t* lora_b;
+  void* y;
+  int64_t n;
+};
+size_t gemm_nvfp4_f16_layers_workspace(int64_t m, int64_t k, const int64_t* n, int nl, int32_t rank);
+hipError_t launch_gemm_nvfp4_f16_layers(const uint16_t* x, int64_t m, int64_t k, const NvLayer* layers, int nl,
+                                        int32_t rank, float lora_scale, int out_f32, void* scratch, hipStream_t s);
 // x as f16 rows scaled by powers of two (x16 [m][k], rs [m]: x[r] = rs[r] x16[r], exact but
 // for values below about 2^-29 of the row maximum) and, with rank > 0, t = s x A^T as hi | lo
 // bf16 pairs [m][2 rank_pad] (null without).  k % 64 == 0, k < kNvF16MaxK.

@@ -229,3 +229,40 @@ def test_backward_argument_errors():
     assert bw(x=None, a=None, bb=None, r=0, da=None, db=None, ws=None) == b.QL_ERR_WORKSPACE
     assert b.qlinear_backward_workspace(b.QL_FP8_BLOCK128, 8, 256, 512, 0) == 0
     assert b.qlinear_backward_workspace(b.QL_NVFP4, 8, 200, 512, 8) == 0
+
+
+def test_forward_group_workspace_and_argument_errors():
+    L = b.LIB
+    m, k = 256, 5120
+    # fused (m > 64, k % 64 == 0, rank % 32 == 0, count * rank <= 128): one pre-pass over x
+    # with the adapters stacked (f16 x, row factors, t of 3 x 32 ranks) and one GEMM
+    fused = b.qlinear_forward_group_workspace(m, k, [8192, 1024, 1024], 32)
+    assert fused >= RES + m * k * 2 + m * 4 + m * 96 * 2
+    # layer by layer otherwise: the largest single-layer workspace
+    few = b.qlinear_forward_group_workspace(8, k, [8192, 1024], 32)
+    assert few == max(b.qlinear_forward_workspace(b.QL_NVFP4, 8, n, k, 32) for n in (8192, 1024))
+    odd = b.qlinear_forward_group_workspace(m, k, [512, 256], 12)  # rank not a multiple of 32
+    assert odd == max(b.qlinear_forward_workspace(b.QL_NVFP4, m, n, k, 12) for n in (512, 256))
+    assert b.qlinear_forward_group_workspace(m, k, [], 32) == 0
+    assert b.qlinear_forward_group_workspace(m, k, [256] * 5, 32) == 0
+    assert b.qlinear_forward_group_workspace(m, k, [256, 0], 32) == 0
+    assert b.qlinear_forward_group_workspace(m, k, [256], 129) == 0
+
+    def call(layers, count=None, x=FAKE, rank=0, s=0.0, ws=FAKE, wsb=1 << 40):
+        arr = (b.GroupLayer * len(layers))(*layers) if layers else None
+        ptr = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
+        return L.qlinear_forward_group(ptr, len(layers) if count is None else count, x, 4, rank, s,
+                                       b.QL_OUT_BF16, ws, wsb, None)
+
+    def layer(n=256, kk=512, fmt=b.QL_NVFP4, a=None, bb=None):
+        return b.GroupLayer(b.QWeight(fmt, 0, n, kk, FAKE, FAKE, FAKE), a, bb, FAKE)
+
+    assert call([]) == b.QL_ERR_NULL
+    assert call([layer()], count=0) == b.QL_ERR_ARG
+    assert call([layer()] * 5) == b.QL_ERR_ARG
+    assert call([layer()], x=None) == b.QL_ERR_NULL
+    assert call([layer(), layer(kk=1024)]) == b.QL_ERR_SHAPE
+    assert call([layer(), layer(fmt=b.QL_FP8_BLOCK128)]) == b.QL_ERR_FORMAT
+    assert call([layer(a=FAKE, bb=FAKE), layer()], rank=8, s=2.0) == b.QL_ERR_NULL
+    assert call([layer(a=FAKE, bb=FAKE), layer(a=FAKE, bb=FAKE)], rank=8, s=2.0, wsb=64) == b.QL_ERR_WORKSPACE
+    assert call([layer(), layer()], ws=None) == b.QL_ERR_WORKSPACE
