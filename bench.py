@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27867265, "fetch_bytes": 26573409, "write_bytes": 1293856,
+DECODE_TRAFFIC = {"bytes_per_launch": 27854378, "fetch_bytes": 26560522, "write_bytes": 1293856,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "0ca8382403b5be51e7ca52c2936e2e34c31680601fbe3e0427876884bd8ff673"}
+                  "sources_sha256": "9b83f5cfbdb5a40c38307cba9876270f3b6ecc21403ee99a254cf3a6c42ba3eb"}
 
 # Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
 # duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over
@@ -57,9 +57,9 @@ DECODE_TRAFFIC = {"bytes_per_launch": 27867265, "fetch_bytes": 26573409, "write_
 # (mean over both shapes of the row).  Reported only while the kernel sources are the ones
 # measured (hash), like the traffic above.
 COUNTER_CLOCKS = {
-    "a5": {"GHz": 1.95, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "a5": {"GHz": 1.91, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "9f9125892aebb87e026637885bf827d6996b9c3375607267a3f92508bae7325f"},
+           "sources_sha256": "ec910852a00ae348287c145a02c82be52ddaa9d1073f981b35b29ada87205a73"},
     "a6": {"GHz": 2.02, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
            "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
@@ -67,10 +67,10 @@ COUNTER_CLOCKS = {
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
             "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
     # the backward's dX kernel (gemm_nvfp4_dx_kernel)
-    "bwd": {"GHz": 2.07, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "bwd": {"GHz": 2.06, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp",
                                      "quantized_linear_layers_block_amd/csrc/backward.hip"],
-            "sources_sha256": "259098c4e1368d7083095c4da314895b3785a705ed2230ebe24516e5e2fbac65"},
+            "sources_sha256": "edd96679c3a6f0900a409bc355bcc2dfe9143694c8d319c3c08627c12caaad17"},
 }
 
 
