@@ -42,6 +42,8 @@
 #include "gemv_common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace ql {
 
 constexpr int kG16Threads = 256;
@@ -802,36 +804,73 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
   dma_c(cl(s0 + 2), 2);
   dma_c(cl(s0 + 3), 3);
   dma_c(cl(s0 + 4), 4);
+  // Codes and scales of a wave's K step: the four row tiles' 8-element words and their
+  // block scales.
+  auto read_codes = [&](int slot, uint32_t (&cw)[4], uint32_t (&sb)[4]) {
+    const uint8_t* C = smem + kS128COff + slot * kS128C;
+    const uint8_t* Sc = smem + kS128SOff + slot * kS128S;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rho = 16 * i + r;
+      cw[i] = *(const uint32_t*)(C + (4 * rho + ((wave + (r >> 2)) & 3)) * 16 + 4 * g);
+      sb[i] = Sc[rho * 8 + 2 * wave + (g >> 1)];
+    }
+  };
+  // Software pipeline: stage st + 1's weights are dequantized under stage st's MFMAs.  Its
+  // codes and scales were issued before X(st), so they have landed for every wave once the
+  // stage-st barrier is passed (the copies of C(st + 1) precede X(st) in issue order).  Per
+  // MFMA about five VALU instructions of the next stage's dequantization are interleaved.
+  // The dequantized weights alternate between two register sets (the loop is unrolled by
+  // two stages): a set is rewritten one stage after the MFMAs that read it were issued,
+  // instead of right behind them, where each write would wait for the queued MFMAs.
+  bf16x8 av[2][4];
   int xsl = 0, csl = 0;
-  for (int64_t st = s0; st < s1; ++st) {
+  auto stage = [&](int64_t st, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __syncthreads();  // stage st landed for every wave; nobody reads stage st - 1 any more
     const int xsl2 = xsl + 2 >= kS128XSlots ? xsl + 2 - kS128XSlots : xsl + 2;
     const int csl5 = csl + 5 >= kS128CSlots ? csl + 5 - kS128CSlots : csl + 5;
+    const int csl1 = csl + 1 == kS128CSlots ? 0 : csl + 1;
     dma_x(cl(st + 2), xsl2);
     dma_c(cl(st + 5), csl5);
     const uint8_t* X = smem + xsl * kS128X;
-    const uint8_t* C = smem + kS128COff + csl * kS128C;
-    const uint8_t* Sc = smem + kS128SOff + csl * kS128S;
-    bf16x8 av[4], bv[MT];
+    bf16x8 bv[MT];
 #pragma unroll
     for (int q = 0; q < MT; ++q)
       bv[q] = *(const bf16x8*)(X + (16 * q + r) * 256 + 16 * ((4 * wave + g) ^ r));
+    // the next stage's codes (past the last stage: a clamped copy, dequantized and unused)
+    uint32_t cwn[4], sbn[4];
+    read_codes(csl1, cwn, sbn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rho = 16 * i + r;
-      const uint32_t cw = *(const uint32_t*)(C + (4 * rho + ((wave + (r >> 2)) & 3)) * 16 + 4 * g);
-      const uint32_t sb = Sc[rho * 8 + 2 * wave + (g >> 1)];
-      av[i] = gv_dequant8(cw, e4m3_value(sb));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < MT; ++q)
-        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[q], acc[i][q], 0, 0, 0);
+        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cur][i], bv[q], acc[i][q], 0, 0, 0);
+      av[nxt][i] = gv_dequant8(cwn[i], e4m3_value(sbn[i]));
+    }
+#pragma unroll
+    for (int u = 0; u < 4 * MT; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five vector ALU
+    }
     xsl = xsl + 1 == kS128XSlots ? 0 : xsl + 1;
-    csl = csl + 1 == kS128CSlots ? 0 : csl + 1;
+    csl = csl1;
+  };
+  {  // the first stage's weights, before the loop (its codes came in the first copies)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+    uint32_t cw[4], sb[4];
+    read_codes(0, cw, sb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[0][i] = gv_dequant8(cw[i], e4m3_value(sb[i]));
   }
+  int64_t st = s0;
+  for (; st + 1 < s1; st += 2) {
+    stage(st, std::integral_constant<int, 0>{});
+    stage(st + 1, std::integral_constant<int, 1>{});
+  }
+  if (st < s1) stage(st, std::integral_constant<int, 0>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped copies past the range too
   __syncthreads();
 
