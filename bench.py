@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27854378, "fetch_bytes": 26560522, "write_bytes": 1293856,
+DECODE_TRAFFIC = {"bytes_per_launch": 27860276, "fetch_bytes": 26566420, "write_bytes": 1293856,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "9b83f5cfbdb5a40c38307cba9876270f3b6ecc21403ee99a254cf3a6c42ba3eb"}
+                  "sources_sha256": "628ab70d69bde3e44e73ac1d6038c9dac7785b569d67ff80fd6bc6fa3b3f543a"}
 
 # Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
 # duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over
