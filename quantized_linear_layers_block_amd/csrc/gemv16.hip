@@ -84,6 +84,7 @@ struct G16Args {
   int xstride;        // LDS row stride of the activations (elements)
   int64_t kst;        // 128-wide K stages (33..64 tokens with K % 128 == 0), else 0
   int64_t sps;        // stages per K split
+  int64_t full;       // stage path: tiles [0, full) run whole, the rest split `splits` ways
   uint32_t* ctr;      // counters and flags in the reserved region (g16_line_*)
   int ctr_stride;     // words between two of them
   int32_t* status;    // the workspace's status word
@@ -489,18 +490,18 @@ __device__ __forceinline__ void g16_lora_item(const G16Args& a, uint16_t* xs, in
 }
 
 
-// Finishing a 64-row streaming tile (wave w: rows row0 .. +16 RT, all four token tiles):
-// split partials (device scope) and the last arrival's fixed-order sum, S, the LoRA term
-// once t is published, and the store.
+// Finishing a 64-row streaming tile (wave w: rows row0 .. +16 RT, all four token tiles)
+// whose K range is split `nsplit` ways: split partials (device scope) and the last
+// arrival's fixed-order sum, S, the LoRA term once t is published, and the store.
 template <int RT>
 __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, int64_t tile, int64_t split,
-                                                  int64_t row0, f32x4 (&acc)[RT][4], const i32x4 (&bw)[RT][2],
+                                                  int nsplit, int64_t row0, f32x4 (&acc)[RT][4], const i32x4 (&bw)[RT][2],
                                                   bool early_b, float ts) {
   constexpr int MT = 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15, g = lane >> 4;
   // tiles (rt, q): acc[rt][q] is C[n][m] with m = 16 q + r, n = row0 + 16 rt + 4 g + i
-  if (a.splits > 1) {
+  if (nsplit > 1) {
     const auto ws_rs = dev_rsrc(a.part_w);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -510,7 +511,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
         if (mi < a.m)
           st_dev4v(ws_rs, (uint32_t)(((split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4), acc[rt][q]);
       }
-    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)a.splits, flag)) return;
+    if (!g16_arrive(g16_ctr(a, tile), (uint32_t)nsplit, flag)) return;
     // the partials of all MT token tiles in flight together (up to kSB splits each at a time:
     // a device-scope round trip costs microseconds), added in split order
     constexpr int kSB = 8;
@@ -520,13 +521,13 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
       f32x4 sum[MT];
 #pragma unroll
       for (int q = 0; q < MT; ++q) sum[q] = f32x4{0, 0, 0, 0};
-      for (int sp0 = 0; sp0 < a.splits; sp0 += kSB) {
+      for (int sp0 = 0; sp0 < nsplit; sp0 += kSB) {
         f32x4 part[kSB][MT];
 #pragma unroll
         for (int u = 0; u < kSB; ++u)
 #pragma unroll
           for (int q = 0; q < MT; ++q) {
-            const int sp = sp0 + u < a.splits ? sp0 + u : 0;
+            const int sp = sp0 + u < nsplit ? sp0 + u : 0;
             const int64_t mi = min((int64_t)(16 * q + r), a.m - 1);
             part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
           }
@@ -534,7 +535,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
         for (int u = 0; u < kSB; ++u)
 #pragma unroll
           for (int q = 0; q < MT; ++q)
-            if (sp0 + u < a.splits) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
+            if (sp0 + u < nsplit) sum[q] += sp0 + u == split ? acc[rt][q] : part[u][q];
       }
 #pragma unroll
       for (int q = 0; q < MT; ++q) acc[rt][q] = sum[q];
@@ -708,7 +709,7 @@ __device__ __forceinline__ void g16_stream_item(const G16Args& a, uint16_t* xs, 
     __syncthreads();
   }
 
-  g16_stream_finish<RT>(a, flag, tile, split, row0, acc, bw, early_b, ts);
+  g16_stream_finish<RT>(a, flag, tile, split, a.splits, row0, acc, bw, early_b, ts);
 }
 
 // ------------------------------------------------------------------ 128-wide stage item
@@ -740,9 +741,23 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int r = lane & 15, g = lane >> 4;
-  const int64_t tile = id % a.tiles_w;
-  const int64_t split = id / a.tiles_w;
-  const int64_t s0 = split * a.sps, s1 = min(s0 + a.sps, a.kst);
+  // the first `full` items take whole tiles (all of K); the remaining tiles are split along K
+  int64_t tile, split, s0, s1;
+  int nsplit;
+  if (id < a.full) {
+    tile = id;
+    split = 0;
+    nsplit = 1;
+    s0 = 0;
+    s1 = a.kst;
+  } else {
+    const int64_t tail = a.tiles_w - a.full, j = id - a.full;
+    tile = a.full + j % tail;
+    split = j / tail;
+    nsplit = a.splits;
+    s0 = split * a.sps;
+    s1 = min(s0 + a.sps, a.kst);
+  }
   const int64_t rbase = tile * 64;
   const int64_t row_f = rbase + 16 * wave;
   // No copy of this item is in flight yet: a wait the compiler can see clears what it
@@ -897,7 +912,7 @@ __device__ __forceinline__ void g16_stream128_item(const G16Args& a, uint16_t* x
     for (int w = 1; w < 4; ++w) sum += red[((w * 4 + wave) * MT + q) * kWave + lane];
     v[0][q] = sum;
   }
-  g16_stream_finish<1>(a, flag, tile, split, row_f, v, bw, early_b, ts);
+  g16_stream_finish<1>(a, flag, tile, split, nsplit, row_f, v, bw, early_b, ts);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -1076,14 +1091,20 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
       // 33..64 tokens, 128-wide stages (g16_stream128_item).  K is split into as many parts
       // as keep every workgroup on a CU of its own (two on one CU run markedly slower than
       // one), at most eight and of at least four stages each: split partials cost 4 M N
-      // bytes each way.
+      // bytes each way.  More tiles than CUs: whole-tile rounds, then the leftover tiles
+      // (when at most half a round) split the same way, so that the last round fills the
+      // chip instead of leaving most CUs idle while a few run a second whole tile.
       p.kst = k / 128;
-      int64_t splits = 256 / p.tiles_w;
+      const int64_t rem = p.tiles_w > kG16CUs ? p.tiles_w % kG16CUs : 0;
+      p.full = rem > 0 && rem <= kG16CUs / 2 ? p.tiles_w - rem : 0;
+      const int64_t tail = p.tiles_w - p.full;
+      int64_t splits = p.tiles_w > kG16CUs && p.full == 0 ? 1 : kG16CUs / tail;
       if (splits > 8) splits = 8;
       if (splits > p.kst / 4) splits = p.kst / 4;
       if (splits < 1) splits = 1;
       p.sps = g16_cdiv(p.kst, splits);
       p.splits = (int)g16_cdiv(p.kst, p.sps);
+      if (p.splits == 1) p.full = 0;  // nothing split: every tile whole either way
       p.cps = 0;
       p.xstride = 0;
       p.lds_bytes = (size_t)kS128Lds;
@@ -1179,6 +1200,7 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.xstride = p.xstride;
   a.kst = p.kst;
   a.sps = p.sps;
+  a.full = p.full;
   a.ctr = ws_counters(ws);
   a.ctr_stride = p.ctr_stride;
   a.status = ws_status(ws);
@@ -1189,7 +1211,7 @@ hipError_t launch_g16(const G16Plan& p, const uint16_t* x, int64_t m, int64_t n,
   a.part_w = (float*)(w + off);
   off += p.splits > 1 ? g16_align((size_t)p.splits * (size_t)m * (size_t)p.n_pad * 4) : 0;
   a.part_l = (float*)(w + off);
-  const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.tiles_w * p.splits);
+  const unsigned items = (unsigned)(p.tiles_l * p.lgroups + p.full + (p.tiles_w - p.full) * p.splits);
   const bool aligned = (k % kG16Chunk) == 0;
   if (!g16_plan_ok(p, m)) return hipErrorInvalidValue;  // the C ABI checks this first
   hipError_t e;

@@ -84,6 +84,7 @@ struct G16Plan {
   int xstride;        // LDS row stride of the staged activations
   int64_t kst = 0;    // 128-wide K stages of the 33..64-token stage path (0: not used)
   int64_t sps = 0;    // stages per K split on that path
+  int64_t full = 0;   // that path: tiles [0, full) whole, the others split `splits` ways
   size_t lds_bytes;
   int ctr_stride = 0; // words between two counters in the reserved region (0: does not fit)
 };

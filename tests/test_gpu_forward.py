@@ -99,6 +99,22 @@ def test_nvfp4_skinny_ragged(m, n, k, r):
     _nvfp4_case(w, x, a, b, 2.0 if r else 0.0)
 
 
+# 33..64 tokens, more 64-row tiles than the chip's 256 CUs: the first 256 tiles run whole,
+# the few left over are split along K (here 2 and 4 tail tiles, 2 splits each; ragged N and
+# a last split of fewer stages in the second case).  Every row of the last whole tile and of
+# the split tiles is compared, plus a seeded sample of the rest.
+@pytest.mark.parametrize("m,n,k,r", [(40, 16593, 1024, 16), (64, 16500, 1152, 8)])
+def test_nvfp4_skinny_whole_tiles_then_split_tail(m, n, k, r):
+    g = np.random.default_rng(m * 1000 + n + k)
+    w = synth.normal_bf16((n, k), 0.02, g, 0.01, 15.0)
+    x = synth.normal_bf16((m, k), 1.0, g)
+    a = synth.normal_bf16((r, k), 0.01, g)
+    b = synth.normal_bf16((n, r), 0.01, g)
+    rows_n = np.unique(np.concatenate([_sample(n, 1024, n), np.arange(255 * 64, n)]))
+    print(f"forward skinny whole+split tail m={m} n={n} k={k} r={r}", flush=True)
+    _nvfp4_case(w, x, a, b, 2.0, rows_n=rows_n)
+
+
 @pytest.mark.parametrize("m,n,k,r", [(65, 130, 272, 8), (300, 512, 1040, 40), (256, 256, 512, 0), (257, 1024, 4096, 64),
                                        (1100, 512, 2048, 48),
                                        # 272 tiles: 256 whole tiles, then 16 tail tiles split along K
