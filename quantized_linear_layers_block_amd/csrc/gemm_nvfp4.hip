@@ -1228,7 +1228,13 @@ constexpr int64_t kNvStatsWideRows = 1024;  // from this many rows on, two row f
 int64_t nv_prep_splits(int64_t m, int64_t k) {
   const int64_t tiles = (m + 63) / 64;
   int64_t sp = (1024 + tiles - 1) / tiles;
-  const int64_t smax = k / 256 > 0 ? k / 256 : 1;
+  // Splits of at least 256 columns; with at most four row tiles (up to 256 tokens) and
+  // K <= 5120, of 128: at 256 tokens the 256-column floor left 80 workgroups for K = 5120
+  // (the stacked q/k/v adapters' pass 14.4 -> 9.1 us, gate/up 8.0 -> 5.6 at 128).  Larger K
+  // keeps 256: nv_finish_kernel adds every split's partials (K = 27648 at 216 splits: 13.0
+  // -> 17.4 us), and at K = 8192, 40 uneven splits were slower than 32 even ones.
+  const int64_t s128 = tiles <= 4 && k / 128 <= 40 ? k / 128 : 0;
+  const int64_t smax = k / 256 > s128 ? k / 256 : (s128 > 0 ? s128 : 1);
   return sp < 1 ? 1 : (sp > smax ? smax : sp);
 }
 
