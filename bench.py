@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 27860276, "fetch_bytes": 26566420, "write_bytes": 1293856,
+DECODE_TRAFFIC = {"bytes_per_launch": 28540924, "fetch_bytes": 26918641, "write_bytes": 1622283,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "628ab70d69bde3e44e73ac1d6038c9dac7785b569d67ff80fd6bc6fa3b3f543a"}
+                  "sources_sha256": "7b0e6ac4b8ed8b3ab52571406bd70ad5307d61bac0446447ea0d78a58abc2746"}
 
 # Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
 # duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over
@@ -59,7 +59,7 @@ DECODE_TRAFFIC = {"bytes_per_launch": 27860276, "fetch_bytes": 26566420, "write_
 COUNTER_CLOCKS = {
     "a5": {"GHz": 1.91, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "ec910852a00ae348287c145a02c82be52ddaa9d1073f981b35b29ada87205a73"},
+           "sources_sha256": "7c9dd1a1bad5c896ebded9fa7b6eea82e39db1c2065c0d76365d5a2288e6b317"},
     "a6": {"GHz": 2.02, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
            "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
@@ -67,10 +67,10 @@ COUNTER_CLOCKS = {
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
             "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
     # the backward's dX kernel (gemm_nvfp4_dx_kernel)
-    "bwd": {"GHz": 2.06, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "bwd": {"GHz": 2.07, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp",
                                      "quantized_linear_layers_block_amd/csrc/backward.hip"],
-            "sources_sha256": "edd96679c3a6f0900a409bc355bcc2dfe9143694c8d319c3c08627c12caaad17"},
+            "sources_sha256": "4efa679b6d5f5fad83c2c52f6f5a0c2c68d456a447aa272018efbb53dc636ed3"},
 }
 
 
