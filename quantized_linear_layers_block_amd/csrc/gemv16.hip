@@ -221,15 +221,23 @@ __device__ __forceinline__ G16Chunk g16_transpose(const G16Chunk& cr) {
 // unit past the range).  With TAIL (K not a multiple of 256) units past K are zeroed;
 // K % 16 == 0 and units are 8-element aligned, so a unit lies entirely inside or entirely
 // past K.
+// Row of unit u: u / per_row through a float reciprocal taken once, not an integer division
+// per unit (about 45 instructions each, ahead of the first code load).  Exact: u < 2^11 and
+// per_row = 32 chunks <= 2^9, so (u + 1/2) / per_row lies at least 2^-10 from an integer,
+// far beyond the error of the rounded reciprocal and product (below 2^-16 here).
+__device__ __forceinline__ float g16_row_inv(int per_row) { return 1.0f / (float)per_row; }
+__device__ __forceinline__ int g16_row_of(int u, float inv) { return (int)(((float)u + 0.5f) * inv); }
+
 template <int XU, bool TAIL>
 __device__ __forceinline__ void g16_x_issue(const G16Args& a, int mrows, int64_t c0, int64_t c1,
                                             i32x4 (&xv)[XU]) {
   const int per_row = (int)(c1 - c0) * (kG16Chunk / 8);
   const int units = mrows * per_row;
+  const float inv = g16_row_inv(per_row);
 #pragma unroll
   for (int j = 0; j < XU; ++j) {
     const int u = threadIdx.x + kG16Threads * j;
-    const int i = u / per_row;
+    const int i = g16_row_of(u, inv);
     const int64_t kk = c0 * kG16Chunk + (int64_t)(u - i * per_row) * 8;
     const bool ok = TAIL ? (u < units && kk < a.k) : u < units;
     const i32x4 v = *(const i32x4*)(ok ? a.x + (int64_t)i * a.k + kk : a.x);
@@ -242,17 +250,18 @@ __device__ __forceinline__ void g16_x_issue(const G16Args& a, int mrows, int64_t
   }
 }
 // LDS byte offset of unit u (row u / per_row, column 8 (u % per_row)), or -1 past the range.
-__device__ __forceinline__ int g16_x_off(const G16Args& a, int u, int per_row, int units) {
-  const int i = u / per_row;
+__device__ __forceinline__ int g16_x_off(const G16Args& a, int u, int per_row, int units, float inv) {
+  const int i = g16_row_of(u, inv);
   return u < units ? (i * a.xstride + (u - i * per_row) * 8) * 2 : -1;
 }
 
 template <int XU>
 __device__ __forceinline__ void g16_x_store(const G16Args& a, uint16_t* xs, int per_row, int units,
                                             const i32x4 (&xv)[XU]) {
+  const float inv = g16_row_inv(per_row);
 #pragma unroll
   for (int j = 0; j < XU; ++j) {
-    const int xo = g16_x_off(a, threadIdx.x + kG16Threads * j, per_row, units);
+    const int xo = g16_x_off(a, threadIdx.x + kG16Threads * j, per_row, units, inv);
     if (xo >= 0) *(i32x4*)((char*)xs + xo) = xv[j];
   }
 }
