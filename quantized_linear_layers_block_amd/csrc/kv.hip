@@ -24,26 +24,42 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v, int lanes) {
   return v;
 }
 
+// Token and head of vector v (t = v / heads): a 32-bit division when every vector index
+// fits in 32 bits (the host passes `narrow`), else the 64-bit one.
+__device__ __forceinline__ void kv_token_head(int64_t v, int heads, bool narrow, int64_t& t, int& h) {
+  if (narrow) {
+    const uint32_t q = (uint32_t)v / (uint32_t)heads;
+    t = q;
+    h = (int)((uint32_t)v - q * (uint32_t)heads);
+  } else {
+    t = v / heads;
+    h = (int)(v - t * heads);
+  }
+}
+
 __global__ __launch_bounds__(kKvThreads) void kv_store_kernel(const uint16_t* __restrict__ kv, int64_t vectors,
                                                               int heads, int head_dim, const int64_t* __restrict__ slots,
                                                               uint8_t* __restrict__ codes, float* __restrict__ scales,
-                                                              int64_t cache_slots, int32_t* status) {
-  const int lanes = head_dim / 8;
-  const int64_t per_block = kKvThreads / lanes;
-  const int part = (int)(threadIdx.x % lanes);
+                                                              int64_t cache_slots, int32_t* status, bool narrow) {
+  const int lsh = __builtin_ctz((unsigned)head_dim) - 3;  // lanes per vector: head_dim / 8, a power of two
+  const int lanes = 1 << lsh;
+  const int64_t per_block = kKvThreads >> lsh;
+  const int part = (int)(threadIdx.x & (lanes - 1));
   for (int64_t v0 = (int64_t)blockIdx.x * per_block; v0 < vectors; v0 += (int64_t)gridDim.x * per_block) {
-    const int64_t v = v0 + threadIdx.x / lanes;
+    const int64_t v = v0 + (threadIdx.x >> lsh);
     const bool in = v < vectors;
-    const int64_t t = in ? v / heads : 0;
-    const int h = in ? (int)(v - t * heads) : 0;
-    const uint4 x = in ? *(const uint4*)(kv + v * head_dim + part * 8) : make_uint4(0, 0, 0, 0);
+    // every load issued at once, from a clamped vector past the end
+    int64_t t;
+    int h;
+    kv_token_head(in ? v : vectors - 1, heads, narrow, t, h);
+    const int64_t slot = slots[t];
+    const uint4 x = *(const uint4*)(kv + (in ? v : vectors - 1) * head_dim + part * 8);
     u16x2 m = abs_bits2(x.x);
     m = max_u16x2(m, abs_bits2(x.y));
     m = max_u16x2(m, abs_bits2(x.z));
     m = max_u16x2(m, abs_bits2(x.w));
     const uint32_t amax_bits = group_max(hmax_u16x2(m), lanes);  // every lane of the group
     if (!in) continue;
-    const int64_t slot = slots[t];
     if (slot < 0 || slot >= cache_slots) {
       if (part == 0 && status) atomicOr(status, (int32_t)kStatusBadItem);
       continue;
@@ -71,21 +87,25 @@ __global__ __launch_bounds__(kKvThreads) void kv_load_kernel(const uint8_t* __re
                                                              const float* __restrict__ scales, int64_t cache_slots,
                                                              const int64_t* __restrict__ slots, int64_t vectors,
                                                              int heads, int head_dim, uint16_t* __restrict__ out,
-                                                             int32_t* status) {
-  const int lanes = head_dim / 8;
-  const int64_t per_block = kKvThreads / lanes;
-  const int part = (int)(threadIdx.x % lanes);
+                                                             int32_t* status, bool narrow) {
+  const int lsh = __builtin_ctz((unsigned)head_dim) - 3;
+  const int lanes = 1 << lsh;
+  const int64_t per_block = kKvThreads >> lsh;
+  const int part = (int)(threadIdx.x & (lanes - 1));
   for (int64_t v0 = (int64_t)blockIdx.x * per_block; v0 < vectors; v0 += (int64_t)gridDim.x * per_block) {
-    const int64_t v = v0 + threadIdx.x / lanes;
+    const int64_t v = v0 + (threadIdx.x >> lsh);
     if (v >= vectors) continue;
-    const int64_t t = v / heads;
-    const int h = (int)(v - t * heads);
+    int64_t t;
+    int h;
+    kv_token_head(v, heads, narrow, t, h);
     const int64_t slot = slots[t];
+    const bool ok = slot >= 0 && slot < cache_slots;
+    // the codes and the scale of a slot outside the cache are read from slot 0 and dropped
+    const int64_t sv = (ok ? slot : 0) * heads + h;
+    const uint2 c = *(const uint2*)(codes + sv * head_dim + part * 8);
+    const float sc = scales[sv];
     uint4 o = make_uint4(0, 0, 0, 0);
-    if (slot >= 0 && slot < cache_slots) {
-      const int64_t src = (slot * heads + h) * head_dim + part * 8;
-      const uint2 c = *(const uint2*)(codes + src);
-      const float sc = scales[slot * heads + h];
+    if (ok) {
       auto dec2 = [&](uint32_t w, int b) {  // bytes b, b + 1 of w
         return pack_bf16x2_rne(e4m3_value((w >> (8 * b)) & 0xFFu) * sc, e4m3_value((w >> (8 * b + 8)) & 0xFFu) * sc);
       };
@@ -107,7 +127,8 @@ hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int he
                            uint8_t* codes, float* scales, int64_t cache_slots, int32_t* status, hipStream_t s) {
   const int64_t vectors = tokens * heads;
   kv_store_kernel<<<kv_grid(vectors, head_dim), kKvThreads, 0, s>>>(kv, vectors, heads, head_dim, slots, codes,
-                                                                     scales, cache_slots, status);
+                                                                     scales, cache_slots, status,
+                                                                     vectors <= (int64_t)UINT32_MAX);
   return hipGetLastError();
 }
 
@@ -115,7 +136,8 @@ hipError_t launch_kv_load(const uint8_t* codes, const float* scales, int64_t cac
                           int64_t tokens, int heads, int head_dim, uint16_t* out, int32_t* status, hipStream_t s) {
   const int64_t vectors = tokens * heads;
   kv_load_kernel<<<kv_grid(vectors, head_dim), kKvThreads, 0, s>>>(codes, scales, cache_slots, slots, vectors,
-                                                                    heads, head_dim, out, status);
+                                                                    heads, head_dim, out, status,
+                                                                    vectors <= (int64_t)UINT32_MAX);
   return hipGetLastError();
 }
 
