@@ -80,7 +80,7 @@ struct G16Args {
   int64_t lgroups;    // LoRA chunk groups
   int lc;             // chunks per LoRA item (a multiple of four: the waves take them in turn)
   int rank_pad;       // t row length (multiple of 32)
-  int64_t n_pad;      // row length of the weight partials
+  int64_t n_pad;      // row length of the weight partials (the split tiles' rows)
   int xstride;        // LDS row stride of the activations (elements)
   int64_t kst;        // 128-wide K stages (33..64 tokens with K % 128 == 0), else 0
   int64_t sps;        // stages per K split
@@ -89,7 +89,7 @@ struct G16Args {
   int ctr_stride;     // words between two of them
   int32_t* status;    // the workspace's status word
   uint32_t* t;        // [m][rank_pad / 2] bf16 pairs
-  float* part_w;      // [splits][m][n_pad]
+  float* part_w;      // [splits][m][n_pad]: rows from 64 full on (only split tiles write partials)
   float* part_l;      // [lgroups][m][tiles_l * 16]
 };
 
@@ -511,6 +511,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
   const int r = lane & 15, g = lane >> 4;
   // tiles (rt, q): acc[rt][q] is C[n][m] with m = 16 q + r, n = row0 + 16 rt + 4 g + i
   if (nsplit > 1) {
+    const int64_t prow = row0 - 64 * a.full;  // partial rows start at the first split tile
     const auto ws_rs = dev_rsrc(a.part_w);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -518,7 +519,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
       for (int q = 0; q < MT; ++q) {
         const int64_t mi = 16 * q + r;
         if (mi < a.m)
-          st_dev4v(ws_rs, (uint32_t)(((split * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4), acc[rt][q]);
+          st_dev4v(ws_rs, (uint32_t)(((split * a.m + mi) * a.n_pad + prow + 16 * rt + 4 * g) * 4), acc[rt][q]);
       }
     if (!g16_arrive(g16_ctr(a, tile), (uint32_t)nsplit, flag)) return;
     // the partials of all MT token tiles in flight together (up to kSB splits each at a time:
@@ -538,7 +539,7 @@ __device__ __forceinline__ void g16_stream_finish(const G16Args& a, int* flag, i
           for (int q = 0; q < MT; ++q) {
             const int sp = sp0 + u < nsplit ? sp0 + u : 0;
             const int64_t mi = min((int64_t)(16 * q + r), a.m - 1);
-            part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + row0 + 16 * rt + 4 * g) * 4));
+            part[u][q] = ld_dev4v(rs, (uint32_t)((((int64_t)sp * a.m + mi) * a.n_pad + prow + 16 * rt + 4 * g) * 4));
           }
 #pragma unroll
         for (int u = 0; u < kSB; ++u)
@@ -1114,6 +1115,7 @@ G16Plan plan_g16(int64_t m, int64_t n, int64_t k, int32_t rank) {
       p.sps = g16_cdiv(p.kst, splits);
       p.splits = (int)g16_cdiv(p.kst, p.sps);
       if (p.splits == 1) p.full = 0;  // nothing split: every tile whole either way
+      p.n_pad = (p.tiles_w - p.full) * 64;  // partials of the split tiles only
       p.cps = 0;
       p.xstride = 0;
       p.lds_bytes = (size_t)kS128Lds;
