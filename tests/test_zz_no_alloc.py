@@ -33,8 +33,10 @@ def _both(q, x, a, b, r, out_dtype):
 
 
 def test_noalloc_matches_forward_two_calls():
-    # decode at 8 tokens with an 11-way K split and LoRA r32, then one token on a smaller layer
-    for m, n, k, r, seed in [(8, 3584, 18944, 32, 1), (1, 512, 3584, 32, 2), (40, 300, 784, 16, 3)]:
+    # 64 tokens on 260 row tiles (256 whole, the 4 left over split along K), decode at 8
+    # tokens with an 11-way K split and LoRA r32, then one token on a smaller layer
+    for m, n, k, r, seed in [(64, 16593, 1024, 16, 5), (8, 3584, 18944, 32, 1), (1, 512, 3584, 32, 2),
+                             (40, 300, 784, 16, 3)]:
         print(f"noalloc m {m} n {n} k {k} r {r}", flush=True)
         q, x, a, b = _layer(m, n, k, r, seed)
         for od in (torch.float32, torch.bfloat16):
