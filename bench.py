@@ -45,11 +45,11 @@ DECODE_SHAPES = [(3584, 3584), (3584, 512), (3584, 18944), (18944, 3584)]  # (K,
 # what it reads for a plain 1 GiB device copy (bench.py --copy-calibration 1073741824):
 # FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.  The figure belongs to the kernel sources it
 # was measured on (hash below); after any change to them it is reported as null.
-DECODE_TRAFFIC = {"bytes_per_launch": 28527183, "fetch_bytes": 26904900, "write_bytes": 1622283,
+DECODE_TRAFFIC = {"bytes_per_launch": 28527321, "fetch_bytes": 26905038, "write_bytes": 1622283,
                   "sources": ["quantized_linear_layers_block_amd/csrc/gemv16.hip",
                               "quantized_linear_layers_block_amd/csrc/gemv_common.hpp",
                               "quantized_linear_layers_block_amd/csrc/common.hpp"],
-                  "sources_sha256": "93cf9e40bab940161bc9740c039cff9570554002056699a3d5915c7514b1b348"}
+                  "sources_sha256": "fa69691fc1b7dc4390a5e2d685a19a7f8f813203f91e301e6420cadc1110441b"}
 
 # Achieved shader clock of the long MFMA kernels: GRBM_GUI_ACTIVE / 8 XCDs / traced kernel
 # duration, from rocprofv3 --kernel-trace --stats --pmc GRBM_GUI_ACTIVE ... over

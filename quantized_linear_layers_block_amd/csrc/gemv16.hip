@@ -223,8 +223,8 @@ __device__ __forceinline__ G16Chunk g16_transpose(const G16Chunk& cr) {
 // past K.
 // Row of unit u: u / per_row through a float reciprocal taken once, not an integer division
 // per unit (about 45 instructions each, ahead of the first code load).  Exact: u < 2^11 and
-// per_row = 32 chunks <= 2^9, so (u + 1/2) / per_row lies at least 2^-10 from an integer,
-// far beyond the error of the rounded reciprocal and product (below 2^-16 here).
+// per_row = 32 x (chunks per split) <= 2^9, so (u + 1/2) / per_row lies at least 2^-10 from
+// an integer, far beyond the error of the rounded reciprocal and product (below 2^-16 here).
 __device__ __forceinline__ float g16_row_inv(int per_row) { return 1.0f / (float)per_row; }
 __device__ __forceinline__ int g16_row_of(int u, float inv) { return (int)(((float)u + 0.5f) * inv); }
 
