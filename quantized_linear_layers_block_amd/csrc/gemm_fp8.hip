@@ -234,11 +234,20 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
 // take about as long as the MFMAs, drop by a third.  Operand stages, swizzle and copies
 // are those of gemm_fp8_kernel (each wave copies 64 rows of each operand); the copies of
 // the next block go out during fragments 0-3 and the block barrier sits before fragment 7.
+// SW4 (K a multiple of 512 and 4-byte aligned scale arrays): the E8M0 bytes of four
+// consecutive K blocks of a row form one aligned word, copied global -> LDS with the
+// operand copies once per four blocks (each wave 64 activation rows, wave 0 also the
+// tile's two weight blocks) into a two-slot ring after the operand stages; each lane then
+// reads its nine scale bytes from LDS.  Nine single-byte global loads per lane per block
+// cost about 15% of the kernel's time (measured by leaving them out): the compiler,
+// which counts them but not the assembly copies, waited on them at the top of every
+// block.  The bytes, and hence the results, are the same either way.
 constexpr int kP2Threads = 256;
 constexpr int kP2StagePerWave = 128 * kStagePitch;  // 128 rows of 128 bf16 columns per wave
 constexpr size_t kP2Lds = 4 * kP2StagePerWave;      // >= the two operand stages (128 KB)
+static_assert(kP2Lds >= 4 * kTile * kRowBytes + 2 * 1280, "the scale ring follows the two operand stages");
 
-template <int OUT_F32>
+template <int OUT_F32, bool SW4>
 __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
   constexpr int kStage = 2 * kTile * kRowBytes;
@@ -285,6 +294,25 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
   const bool nblk_ok = nblk * 128 < a.n;
   const uint8_t* sxb = (const uint8_t*)a.sx + m0 * kblocks;
   const uint8_t* swb = (const uint8_t*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
+  // SW4 scale ring: slot (group & 1) holds the words of the tile's 256 activation rows
+  // (bytes 0..1023) and of its weight blocks n0/128 + 0..63 (clamped; 1024..1279)
+  constexpr int kScRing = 2 * kStage, kScSlot = 1280;
+  const int arow = 64 * wave + lane;
+  const uint32_t oxw = (uint32_t)((arow < m_last ? arow : m_last) * kblocks);
+  const int64_t nb_last = (a.n - 1) / 128 - n0 / 128;
+  const uint32_t oww = (uint32_t)((lane < nb_last ? lane : nb_last) * kblocks);
+  const uint8_t* swt = (const uint8_t*)a.sw + (n0 / 128) * kblocks;
+  auto dma_sc = [&](int64_t grp) {  // the words of blocks 4 grp .. 4 grp + 3
+    const uint32_t lb = lds_addr(smem + kScRing) + (uint32_t)(grp & 1) * kScSlot;
+    lds_copy4(sxb + 4 * grp, oxw, lb + wave * 256);
+    if (wave == 0) lds_copy4(swt + 4 * grp, oww, lb + 1024);
+  };
+  auto read_sc = [&](int64_t kbk, int& sa_, int (&sb_)[8]) {  // block kbk's bytes, from its group's slot
+    const uint8_t* sl = smem + kScRing + (int)((kbk >> 2) & 1) * kScSlot + (int)(kbk & 3);
+    sa_ = sl[1024 + 4 * wn];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sb_[j] = sl[4 * (128 * wm + 16 * j + r)];
+  };
 
   f32x4 acc[8][8];
 #pragma unroll
@@ -294,11 +322,17 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
 
 #pragma unroll
   for (int q = 0; q < 16; ++q) dma(0, 0, q);
-  int sa = swb[0], sb[8];
+  int sa = 0, sb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (SW4) {
+    dma_sc(0);
+  } else {
+    sa = swb[0];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sb[j] = sxb[osx[j]];
+    for (int j = 0; j < 8; ++j) sb[j] = sxb[osx[j]];
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (SW4) read_sc(0, sa, sb);
   i32x8 bf[8], af, afn;
 #pragma unroll
   for (int j = 0; j < 8; ++j) bf[j] = frag_fp8(smem + kTile * kRowBytes, 128 * wm + 16 * j + r, g);
@@ -306,10 +340,17 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
   for (int64_t kb = 0; kb < kblocks; ++kb) {
     const int buf = (int)(kb & 1);
     const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;  // the last block re-copies itself into the idle buffer
-    const int san = swb[kn];
-    int sbn[8];
+    // the next block's scales: bytes, or (SW4) the copy of the next group's words when the
+    // next block starts one (landed by the block barrier's vmcnt(0) below; its slot was
+    // last read two groups ago)
+    int san = 0, sbn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (SW4) {
+      if (kn != kb && (kn & 3) == 0) dma_sc(kn >> 2);
+    } else {
+      san = swb[kn];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sbn[j] = sxb[osx[j] + kn];
+      for (int j = 0; j < 8; ++j) sbn[j] = sxb[osx[j] + kn];
+    }
     const uint8_t* As = smem + buf * kStage;
     const uint8_t* An = smem + (buf ^ 1) * kStage;
 #pragma unroll
@@ -329,9 +370,13 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
       }
       af = afn;
     }
-    sa = san;
+    if (SW4) {
+      read_sc(kn, sa, sb);  // after the block barrier: every copy of this block has landed
+    } else {
+      sa = san;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sb[j] = sbn[j];
+      for (int j = 0; j < 8; ++j) sb[j] = sbn[j];
+    }
   }
 
   // Epilogue: lane holds m = m0 + 128 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
@@ -402,13 +447,17 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t
     if (e != hipSuccess) return e;                                                                        \
     gemm_fp8_kernel<OF><<<grid, kGThreads, lds, s>>>(a);                                                   \
   }
-#define QL_FP8_P2_LAUNCH(OF)                                                                              \
+#define QL_FP8_P2_LAUNCH_W(OF, W)                                                                         \
   {                                                                                                       \
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_pow2_kernel<OF>,                             \
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_pow2_kernel<OF, W>,                          \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kP2Lds);          \
     if (e != hipSuccess) return e;                                                                        \
-    gemm_fp8_pow2_kernel<OF><<<grid, kP2Threads, kP2Lds, s>>>(a);                                          \
+    gemm_fp8_pow2_kernel<OF, W><<<grid, kP2Threads, kP2Lds, s>>>(a);                                       \
   }
+  // scale words of four blocks: every row's bytes start on a 4-byte boundary
+  const bool sw4 = (k / 128) % 4 == 0 && ((uintptr_t)sx & 3) == 0 && ((uintptr_t)sw & 3) == 0;
+#define QL_FP8_P2_LAUNCH(OF) \
+  if (sw4) QL_FP8_P2_LAUNCH_W(OF, true) else QL_FP8_P2_LAUNCH_W(OF, false)
   if (out_f32) {
     if (pow2) QL_FP8_P2_LAUNCH(1) else QL_FP8_LAUNCH(1)
   } else {
@@ -416,6 +465,7 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t
   }
 #undef QL_FP8_LAUNCH
 #undef QL_FP8_P2_LAUNCH
+#undef QL_FP8_P2_LAUNCH_W
   return hipGetLastError();
 }
 
