@@ -33,7 +33,11 @@ constexpr int kTile = 256;     // rows of n and of m per workgroup
 constexpr int kRowBytes = 128; // one K block of fp8 per LDS row
 constexpr int kStagePitch = 272;                 // output staging: bytes per 128-column bf16 row
 constexpr int kStagePerWave = 64 * kStagePitch;  // 64 rows per wave
-constexpr size_t kFp8Lds = 8 * kStagePerWave;    // >= the two operand stages (128 KB)
+// float32-scale kernel with SW4: a two-slot ring of scale units after the two operand stages
+// (per slot 256 activation rows x 16 bytes, then 64 x 16 bytes of weight-block units)
+constexpr int kF32ScSlot = 256 * 16 + 64 * 16;
+constexpr size_t kFp8Lds = 8 * kStagePerWave > 4 * kTile * kRowBytes + 2 * kF32ScSlot
+                               ? 8 * kStagePerWave : 4 * kTile * kRowBytes + 2 * kF32ScSlot;
 
 struct Fp8GemmArgs {
   const uint8_t* xq;
@@ -56,7 +60,7 @@ __device__ __forceinline__ i32x8 frag_fp8(const uint8_t* tile, int row, int g) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int OUT_F32>
+template <int OUT_F32, bool SW4>
 __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];  // [2][A 256x128 | B 256x128]
   constexpr int kStage = 2 * kTile * kRowBytes;
@@ -118,15 +122,43 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
   const float* sxbase = (const float*)a.sx + m0 * kblocks;
   const float* swp = (const float*)a.sw + (nblk_ok ? nblk : 0) * kblocks;
   const float swmask = nblk_ok ? 1.0f : 0.0f;
+  // SW4 (K a multiple of 512, 16-byte aligned scale arrays): the float scales of four
+  // consecutive blocks of a row form one aligned 16-byte unit, copied global -> LDS with
+  // the operand copies once per four blocks (waves 0-3: 64 activation rows each, wave 4:
+  // the tile's weight blocks n0/128 + lane, clamped) and read from LDS: five 4-byte global
+  // loads per lane per block otherwise made the compiler wait at the top of every block.
+  constexpr int kScRing = 4 * kTile * kRowBytes;
+  const int arow = 64 * (wave & 3) + lane;
+  const uint32_t oxu = (uint32_t)((arow < m_last ? arow : m_last) * kblocks * 4);
+  const int64_t nb_last = (a.n - 1) / 128 - n0 / 128;
+  const uint32_t owu = (uint32_t)((lane < nb_last ? lane : nb_last) * kblocks * 4);
+  const uint8_t* sxt = (const uint8_t*)sxbase;
+  const uint8_t* swt = (const uint8_t*)((const float*)a.sw + (n0 / 128) * kblocks);
+  auto dma_sc = [&](int64_t grp) {  // the units of blocks 4 grp .. 4 grp + 3
+    const uint32_t lb = lds_addr(smem + kScRing) + (uint32_t)(grp & 1) * kF32ScSlot;
+    if (wave < 4) lds_copy16(sxt + 16 * grp, oxu, lb + wave * 1024);
+    else if (wave == 4) lds_copy16(swt + 16 * grp, owu, lb + 4096);
+  };
+  auto read_sc = [&](int64_t kbk, float (&sx_)[4], float& sw_) {  // block kbk's scales
+    const uint8_t* sl = smem + kScRing + (int)((kbk >> 2) & 1) * kF32ScSlot + 4 * (int)(kbk & 3);
+    sw_ = *(const float*)(sl + 4096 + 16 * wn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sx_[j] = *(const float*)(sl + 16 * (64 * wm + 16 * j + r));
+  };
 
-  float sxn[4];
+  float sxn[4] = {0, 0, 0, 0}, swn = 0.0f;
 #pragma unroll
   for (int q = 0; q < 8; ++q) dma(0, 0, q);
+  if (SW4) {
+    dma_sc(0);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j]];
-  float swn = swp[0];
+    for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j]];
+    swn = swp[0];
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (SW4) read_sc(0, sxn, swn);
 
   // Software pipeline.  The MFMAs of a K block run fragment by fragment (8 A fragments x
   // 4 B fragments); each MFMA is issued right after the four FMAs that fold the product
@@ -155,9 +187,15 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
       sc_prev[j] = sc[j];
       sc[j] = sxn[j] * swn * swmask;
     }
+    if (SW4) {
+      // the next group's units when the next block starts one (landed by the block
+      // barrier's vmcnt(0) below; its slot was last read two groups ago)
+      if (kn != kb && (kn & 3) == 0) dma_sc(kn >> 2);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j] + kn];
-    swn = swp[kn];
+      for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j] + kn];
+      swn = swp[kn];
+    }
     const uint8_t* As = smem + buf * kStage;
     const uint8_t* An = smem + (buf ^ 1) * kStage;
 #pragma unroll
@@ -184,6 +222,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
       }
       af = afn;
     }
+    if (SW4) read_sc(kn, sxn, swn);  // after the block barrier: this block's copies have landed
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
@@ -440,13 +479,17 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t
   const size_t lds = kFp8Lds;
   static_assert(kFp8Lds >= 4 * kTile * kRowBytes, "staging must cover the operand buffers");
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-#define QL_FP8_LAUNCH(OF)                                                                                 \
+#define QL_FP8_LAUNCH_W(OF, W)                                                                            \
   {                                                                                                       \
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<OF>,                                   \
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<OF, W>,                                \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);             \
     if (e != hipSuccess) return e;                                                                        \
-    gemm_fp8_kernel<OF><<<grid, kGThreads, lds, s>>>(a);                                                   \
+    gemm_fp8_kernel<OF, W><<<grid, kGThreads, lds, s>>>(a);                                                \
   }
+  // float32 scale units of four blocks: every row's scales start on a 16-byte boundary
+  const bool f4 = (k / 128) % 4 == 0 && ((uintptr_t)sx & 15) == 0 && ((uintptr_t)sw & 15) == 0;
+#define QL_FP8_LAUNCH(OF) \
+  if (f4) QL_FP8_LAUNCH_W(OF, true) else QL_FP8_LAUNCH_W(OF, false)
 #define QL_FP8_P2_LAUNCH_W(OF, W)                                                                         \
   {                                                                                                       \
     hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_pow2_kernel<OF, W>,                          \
@@ -466,6 +509,7 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const void* sx, int64_t m, int64_t
 #undef QL_FP8_LAUNCH
 #undef QL_FP8_P2_LAUNCH
 #undef QL_FP8_P2_LAUNCH_W
+#undef QL_FP8_LAUNCH_W
   return hipGetLastError();
 }
 
