@@ -188,9 +188,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
       sc[j] = sxn[j] * swn * swmask;
     }
     if (SW4) {
-      // the next group's units when the next block starts one (landed by the block
-      // barrier's vmcnt(0) below; its slot was last read two groups ago)
-      if (kn != kb && (kn & 3) == 0) dma_sc(kn >> 2);
+      // kn's group landed at least one block barrier ago: each group's copy goes out two
+      // blocks before its first block (its slot was last read a whole group earlier)
+      if (((kb + 2) & 3) == 0 && kb + 2 < kblocks) dma_sc((kb + 2) >> 2);
+      read_sc(kn, sxn, swn);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sxn[j] = sxbase[osx[j] + kn];
@@ -222,7 +223,6 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(Fp8GemmArgs a) {
       }
       af = afn;
     }
-    if (SW4) read_sc(kn, sxn, swn);  // after the block barrier: this block's copies have landed
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[7][j] += sc[j] * p[j];
@@ -379,12 +379,13 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
   for (int64_t kb = 0; kb < kblocks; ++kb) {
     const int buf = (int)(kb & 1);
     const int64_t kn = kb + 1 < kblocks ? kb + 1 : kb;  // the last block re-copies itself into the idle buffer
-    // the next block's scales: bytes, or (SW4) the copy of the next group's words when the
-    // next block starts one (landed by the block barrier's vmcnt(0) below; its slot was
-    // last read two groups ago)
+    // the next block's scales: bytes, or (SW4) from the ring, where kn's group landed at
+    // least one block barrier ago: each group's copy goes out two blocks before its first
+    // block (its slot was last read a whole group earlier)
     int san = 0, sbn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (SW4) {
-      if (kn != kb && (kn & 3) == 0) dma_sc(kn >> 2);
+      if (((kb + 2) & 3) == 0 && kb + 2 < kblocks) dma_sc((kb + 2) >> 2);
+      read_sc(kn, san, sbn);
     } else {
       san = swb[kn];
 #pragma unroll
@@ -409,13 +410,9 @@ __global__ __launch_bounds__(kP2Threads) void gemm_fp8_pow2_kernel(Fp8GemmArgs a
       }
       af = afn;
     }
-    if (SW4) {
-      read_sc(kn, sa, sb);  // after the block barrier: every copy of this block has landed
-    } else {
-      sa = san;
+    sa = san;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sb[j] = sbn[j];
-    }
+    for (int j = 0; j < 8; ++j) sb[j] = sbn[j];
   }
 
   // Epilogue: lane holds m = m0 + 128 wm + 16 j + r, n = n0 + 128 wn + 16 i + 4 g + (0..3).
