@@ -60,12 +60,12 @@ COUNTER_CLOCKS = {
     "a5": {"GHz": 1.91, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
            "sources_sha256": "7c9dd1a1bad5c896ebded9fa7b6eea82e39db1c2065c0d76365d5a2288e6b317"},
-    "a6": {"GHz": 2.02, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+    "a6": {"GHz": 1.94, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
-    "a6p": {"GHz": 2.09, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "57a62bdd01b81995478db2d4f75be14d708ffa3717116c71a7e1515a099e76bf"},
+    "a6p": {"GHz": 2.06, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-            "sources_sha256": "9143a72b2c0aff87f6a3a3a5a62bdf2e31969e699c6077b2e1afac5dd2eea073"},
+            "sources_sha256": "57a62bdd01b81995478db2d4f75be14d708ffa3717116c71a7e1515a099e76bf"},
     # the backward's dX kernel (gemm_nvfp4_dx_kernel)
     "bwd": {"GHz": 2.07, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp",
