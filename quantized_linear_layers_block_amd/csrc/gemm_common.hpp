@@ -99,46 +99,59 @@ __device__ __forceinline__ void store4(void* y, int out_f32, int64_t n_total, in
 // clamped to m_lim); lane (r, g) supplies ranks q0 + 8 g .. + 7 of row r.  Per 32-rank chunk every fragment is loaded once and
 // all NI x NJ MFMAs follow.  With rank % 8 == 0 a lane's 8 ranks are one aligned
 // 16-byte load (lora_b is 16-byte aligned) and are either all in range or all out.
+// The MFMA operands of ranks q0 .. q0 + 32: rows of B (A operand) and of t (B operand).
+template <int NI, int NJ>
+__device__ __forceinline__ void lora_frags(const uint16_t* __restrict__ lora_b, const uint16_t* __restrict__ t,
+                                           int32_t rank, int64_t n_lim, int64_t m_lim, int64_t nbase,
+                                           int64_t mbase, int r, int g, int64_t ts, int q0, i32x4 (&af)[NI],
+                                           i32x4 (&bfr)[NJ]) {
+  const bool vec = (rank & 7) == 0;
+  const int q = q0 + 8 * g;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t nr0 = nbase + 16 * i + r;
+    const int64_t nr = nr0 < n_lim ? nr0 : n_lim - 1;
+    if (vec) {
+      af[i] = *(const i32x4*)(lora_b + nr * rank + (q < rank ? q : 0));
+      if (q >= rank) af[i] = i32x4{0, 0, 0, 0};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t b0 = q + e < rank ? lora_b[nr * rank + q + e] : 0u;
+        const uint32_t b1 = q + e + 1 < rank ? lora_b[nr * rank + q + e + 1] : 0u;
+        w[e / 2] = b0 | (b1 << 16);
+      }
+      af[i] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t mr0 = mbase + 16 * j + r;
+    const int64_t mr = mr0 < m_lim ? mr0 : m_lim - 1;
+    bfr[j] = *(const i32x4*)(t + mr * ts + q);
+  }
+}
+template <int NI, int NJ>
+__device__ __forceinline__ void lora_mfma(const i32x4 (&af)[NI], const i32x4 (&bfr)[NJ], f32x4 (&acc)[NI][NJ]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                          __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+}
+// acc += (t B^T) for ranks q_from .. rank_pad, 32 at a time.
 template <int NI, int NJ>
 __device__ __forceinline__ void lora_wave(const uint16_t* __restrict__ lora_b, const uint16_t* __restrict__ t,
                                           int32_t rank, int32_t rank_pad, int64_t n_lim, int64_t m_lim,
                                           int64_t nbase, int64_t mbase, int r, int g,
-                                          f32x4 (&acc)[NI][NJ], int64_t t_stride = 0) {
-  const bool vec = (rank & 7) == 0;
+                                          f32x4 (&acc)[NI][NJ], int64_t t_stride = 0, int q_from = 0) {
   const int64_t ts = t_stride > 0 ? t_stride : rank_pad;
-  for (int q0 = 0; q0 < rank_pad; q0 += 32) {
-    const int q = q0 + 8 * g;
+  for (int q0 = q_from; q0 < rank_pad; q0 += 32) {
     i32x4 af[NI], bfr[NJ];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int64_t nr0 = nbase + 16 * i + r;
-      const int64_t nr = nr0 < n_lim ? nr0 : n_lim - 1;
-      if (vec) {
-        af[i] = *(const i32x4*)(lora_b + nr * rank + (q < rank ? q : 0));
-        if (q >= rank) af[i] = i32x4{0, 0, 0, 0};
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const uint32_t b0 = q + e < rank ? lora_b[nr * rank + q + e] : 0u;
-          const uint32_t b1 = q + e + 1 < rank ? lora_b[nr * rank + q + e + 1] : 0u;
-          w[e / 2] = b0 | (b1 << 16);
-        }
-        af[i] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t mr0 = mbase + 16 * j + r;
-      const int64_t mr = mr0 < m_lim ? mr0 : m_lim - 1;
-      bfr[j] = *(const i32x4*)(t + mr * ts + q);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                            __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+    lora_frags<NI, NJ>(lora_b, t, rank, n_lim, m_lim, nbase, mbase, r, g, ts, q0, af, bfr);
+    lora_mfma<NI, NJ>(af, bfr, acc);
   }
 }
 

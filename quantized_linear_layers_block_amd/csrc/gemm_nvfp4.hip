@@ -849,6 +849,13 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue: lane holds n = n0 + 64 wn + 16 i + 4 g + (0..3), m = m0 + 128 wm + 16 j + r.
+  // The first 32 ranks' LoRA operands are loaded together with S and the row factors, so
+  // that the epilogue waits for one memory round trip instead of two.
+  const bool lora = a.rank_pad > 0 && work.split == 0;
+  const uint16_t* const tl = a.t + (int64_t)sg * a.rank;
+  const int64_t tstride = a.t_stride > 0 ? a.t_stride : a.rank_pad;
+  i32x4 laf[4], lbf[8];
+  if (lora) lora_frags<4, 8>(lora_b, tl, a.rank, N, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g, tstride, 0, laf, lbf);
   const float S = *a.seg.tensor_scale[sg];
   float fac[8];
 #pragma unroll
@@ -860,9 +867,10 @@ __global__ __launch_bounds__(kQThreads) void gemm_nvfp4_f16_kernel(Nvfp4F16Args 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] *= fac[j];
-  if (a.rank_pad > 0 && work.split == 0)
-    lora_wave<4, 8>(lora_b, a.t + (int64_t)sg * a.rank, a.rank, a.rank_pad, N, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g,
-                    acc, a.t_stride);
+  if (lora) {
+    lora_mfma<4, 8>(laf, lbf, acc);
+    lora_wave<4, 8>(lora_b, tl, a.rank, a.rank_pad, N, a.m, n0 + 64 * wn, m0 + 128 * wm, r, g, acc, a.t_stride, 32);
+  }
   if (work.slot >= 0) {
     // split tile: scaled float32 partial (LoRA in split 0), summed by nv_tail_reduce_kernel
     float* pt = a.part + work.slot * (kQTile * kQTile);
