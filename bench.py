@@ -57,20 +57,20 @@ DECODE_TRAFFIC = {"bytes_per_launch": 28527321, "fetch_bytes": 26905038, "write_
 # (mean over both shapes of the row).  Reported only while the kernel sources are the ones
 # measured (hash), like the traffic above.
 COUNTER_CLOCKS = {
-    "a5": {"GHz": 1.91, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "a5": {"GHz": 1.89, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "7c9dd1a1bad5c896ebded9fa7b6eea82e39db1c2065c0d76365d5a2288e6b317"},
-    "a6": {"GHz": 1.94, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "4f91ca3ffbac43e401135fe5afc379b3d5481b0dc739703d70538066208c78c7"},
+    "a6": {"GHz": 1.87, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                     "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-           "sources_sha256": "57a62bdd01b81995478db2d4f75be14d708ffa3717116c71a7e1515a099e76bf"},
-    "a6p": {"GHz": 2.06, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
+           "sources_sha256": "7d7093a559e7c8d53fd8cfd8ced21ffa98a0df9569564751c213c877b815042d"},
+    "a6p": {"GHz": 2.02, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_fp8.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp"],
-            "sources_sha256": "57a62bdd01b81995478db2d4f75be14d708ffa3717116c71a7e1515a099e76bf"},
+            "sources_sha256": "7d7093a559e7c8d53fd8cfd8ced21ffa98a0df9569564751c213c877b815042d"},
     # the backward's dX kernel (gemm_nvfp4_dx_kernel)
-    "bwd": {"GHz": 2.07, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
+    "bwd": {"GHz": 2.06, "sources": ["quantized_linear_layers_block_amd/csrc/gemm_nvfp4.hip",
                                      "quantized_linear_layers_block_amd/csrc/gemm_common.hpp",
                                      "quantized_linear_layers_block_amd/csrc/backward.hip"],
-            "sources_sha256": "4efa679b6d5f5fad83c2c52f6f5a0c2c68d456a447aa272018efbb53dc636ed3"},
+            "sources_sha256": "a01c78ed2889fee906b754419a59ce95bc02bacad258eb425d6d4c92f4fce7ae"},
 }
 
 
