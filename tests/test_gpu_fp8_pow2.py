@@ -97,7 +97,10 @@ def _layer_case(w, x, a=None, b=None, s=0.0, rows_m=None, rows_n=None, prequant=
     assert err <= TOL, f"max rel err {err}"
 
 
-@pytest.mark.parametrize("m,n,k,r", [(8, 256, 256, 0), (300, 384, 1024, 0), (1, 128, 128, 0), (257, 512, 640, 40)])
+# K a multiple of 512 takes the block scales through an LDS ring four blocks at a time:
+# 2048 rotates the ring (ragged M, LoRA), 512 is a single group; the others load them per block.
+@pytest.mark.parametrize("m,n,k,r", [(8, 256, 256, 0), (300, 384, 1024, 0), (1, 128, 128, 0), (257, 512, 640, 40),
+                                     (257, 512, 2048, 40), (64, 256, 512, 8)])
 def test_pow2_layer_small(m, n, k, r):
     g = np.random.default_rng(m + n + k + 7)
     w = synth.normal_bf16((n, k), 0.02, g)
